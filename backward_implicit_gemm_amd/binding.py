@@ -1,0 +1,203 @@
+"""Python binding of libgc (include/gc.h): argument marshalling only.
+
+Every function here turns torch tensors into device pointers, a descriptor
+and the current HIP stream, and calls the C entry point of the same name;
+all computation happens in the HIP kernels behind it.  There is no fallback:
+if ``libgc.so`` is missing or a call fails, an exception is raised.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgc.so")
+
+GC_OK, GC_ERR_INVALID_ARG, GC_ERR_UNSUPPORTED, GC_ERR_WORKSPACE, GC_ERR_HIP = range(5)
+GC_F32, GC_BF16 = 0, 1
+GC_OP_FWD, GC_OP_BWD_DATA, GC_OP_BWD_WEIGHT = 0, 1, 2
+
+EXPORTED = (
+    "gc_conv_out_dims", "gc_conv_workspace_bytes", "gc_conv_fwd", "gc_conv_bwd_data",
+    "gc_conv_bwd_weight", "gc_status_string", "gc_fastdiv_selfcheck", "gc_version",
+)
+
+
+class GcError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)}")
+
+
+class gc_conv_desc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("B", "IC", "H", "W", "OC", "KH", "KW", "stride")]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libgc.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libgc.so not found at {LIB_PATH}; run __graft_entry__.build() "
+                           "(python -m backward_implicit_gemm_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, sz, i, dp = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(gc_conv_desc)
+    L.gc_conv_out_dims.argtypes = [dp, ctypes.POINTER(i), ctypes.POINTER(i)]
+    L.gc_conv_out_dims.restype = i
+    L.gc_conv_workspace_bytes.argtypes = [i, dp, i]
+    L.gc_conv_workspace_bytes.restype = sz
+    L.gc_conv_fwd.argtypes = [vp, vp, vp, vp, sz, dp, i, i, vp]
+    L.gc_conv_fwd.restype = i
+    L.gc_conv_bwd_data.argtypes = [vp, vp, vp, vp, vp, sz, dp, i, i, vp]
+    L.gc_conv_bwd_data.restype = i
+    L.gc_conv_bwd_weight.argtypes = [vp, vp, vp, vp, vp, sz, dp, i, i, vp]
+    L.gc_conv_bwd_weight.restype = i
+    L.gc_status_string.argtypes = [i]
+    L.gc_status_string.restype = ctypes.c_char_p
+    L.gc_fastdiv_selfcheck.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
+    L.gc_fastdiv_selfcheck.restype = ctypes.c_int64
+    L.gc_version.argtypes = []
+    L.gc_version.restype = i
+    _lib = L
+    return L
+
+
+def status_string(status):
+    return lib().gc_status_string(int(status)).decode()
+
+
+def make_desc(B, IC, H, W, OC, KH, KW, stride):
+    return gc_conv_desc(int(B), int(IC), int(H), int(W), int(OC), int(KH), int(KW), int(stride))
+
+
+def desc_from(x_shape, w_shape, stride):
+    B, IC, H, W = (int(v) for v in x_shape)
+    OC, IC2, KH, KW = (int(v) for v in w_shape)
+    if IC2 != IC:
+        raise ValueError(f"x has {IC} channels but w expects {IC2}")
+    return make_desc(B, IC, H, W, OC, KH, KW, stride)
+
+
+def gc_conv_out_dims(desc):
+    oh, ow = ctypes.c_int(0), ctypes.c_int(0)
+    st = lib().gc_conv_out_dims(ctypes.byref(desc), ctypes.byref(oh), ctypes.byref(ow))
+    if st != GC_OK:
+        raise GcError("gc_conv_out_dims", st)
+    return oh.value, ow.value
+
+
+def gc_conv_workspace_bytes(op, desc, dtype):
+    return int(lib().gc_conv_workspace_bytes(int(op), ctypes.byref(desc), int(dtype)))
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return GC_F32
+    if t.dtype == torch.bfloat16:
+        return GC_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
+
+
+def _dev(t, name, dtype):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if _dtype_code(t) != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, the call uses another")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+
+
+def _check(fn, st):
+    if st != GC_OK:
+        raise GcError(fn, st)
+
+
+def workspace_for(op, desc, dtype, device="cuda"):
+    """A device buffer of the size gc_conv_workspace_bytes asks for (or None)."""
+    n = gc_conv_workspace_bytes(op, desc, dtype)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def gc_conv_fwd(x, w, y, relu, stride, workspace=None, stream=None):
+    """y = relu?(conv(x, w)) via the C entry point gc_conv_fwd."""
+    dt = _dtype_code(x)
+    desc = desc_from(x.shape, w.shape, stride)
+    wp, wn = _ws(workspace)
+    st = lib().gc_conv_fwd(_dev(x, "x", dt), _dev(w, "w", dt), _dev(y, "y", dt), wp, wn,
+                           ctypes.byref(desc), int(relu), dt, _stream(stream))
+    _check("gc_conv_fwd", st)
+    return y
+
+
+def gc_conv_bwd_data(dy, w, y_mask, dx, relu, stride, workspace=None, stream=None):
+    """dx from dy (masked by y_mask > 0 when relu) via gc_conv_bwd_data."""
+    dt = _dtype_code(dy)
+    desc = desc_from(dx.shape, w.shape, stride)
+    wp, wn = _ws(workspace)
+    st = lib().gc_conv_bwd_data(_dev(dy, "dy", dt), _dev(w, "w", dt), _dev(y_mask, "y_mask", dt),
+                                _dev(dx, "dx", dt), wp, wn, ctypes.byref(desc), int(relu), dt,
+                                _stream(stream))
+    _check("gc_conv_bwd_data", st)
+    return dx
+
+
+def gc_conv_bwd_weight(x, dy, y_mask, dw, relu, stride, workspace, stream=None):
+    """dw from x and dy (masked by y_mask > 0 when relu) via gc_conv_bwd_weight."""
+    dt = _dtype_code(x)
+    desc = desc_from(x.shape, dw.shape, stride)
+    wp, wn = _ws(workspace)
+    st = lib().gc_conv_bwd_weight(_dev(x, "x", dt), _dev(dy, "dy", dt), _dev(y_mask, "y_mask", dt),
+                                  _dev(dw, "dw", dt), wp, wn, ctypes.byref(desc), int(relu), dt,
+                                  _stream(stream))
+    _check("gc_conv_bwd_weight", st)
+    return dw
+
+
+class Conv:
+    """One convolution layer's three passes with their workspaces allocated
+    once (torch allocates; the library only receives pointers)."""
+
+    def __init__(self, x_shape, w_shape, stride, relu, dtype, device="cuda"):
+        self.stride, self.relu = int(stride), int(relu)
+        self.dt = {torch.float32: GC_F32, torch.bfloat16: GC_BF16}[dtype]
+        self.dtype = dtype
+        self.desc = desc_from(x_shape, w_shape, stride)
+        self.x_shape, self.w_shape = tuple(x_shape), tuple(w_shape)
+        OH, OW = gc_conv_out_dims(self.desc)
+        self.y_shape = (x_shape[0], w_shape[0], OH, OW)
+        self.ws = {op: workspace_for(op, self.desc, self.dt, device)
+                   for op in (GC_OP_FWD, GC_OP_BWD_DATA, GC_OP_BWD_WEIGHT)}
+
+    def fwd(self, x, w, y, stream=None):
+        return gc_conv_fwd(x, w, y, self.relu, self.stride, self.ws[GC_OP_FWD], stream)
+
+    def bwd_data(self, dy, w, y, dx, stream=None):
+        return gc_conv_bwd_data(dy, w, y if self.relu else None, dx, self.relu, self.stride,
+                                self.ws[GC_OP_BWD_DATA], stream)
+
+    def bwd_weight(self, x, dy, y, dw, stream=None):
+        return gc_conv_bwd_weight(x, dy, y if self.relu else None, dw, self.relu, self.stride,
+                                  self.ws[GC_OP_BWD_WEIGHT], stream)

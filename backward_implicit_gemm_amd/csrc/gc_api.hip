@@ -1,0 +1,170 @@
+// gc_api.hip -- the C ABI declared in include/gc.h: argument validation, the
+// output-size closed form, workspace sizing and kernel selection.  All
+// validation happens before the first HIP call, so the error paths are
+// testable on a machine without a GPU.
+#include <limits.h>
+
+#include "../../include/gc.h"
+#include "gc_kernels.h"
+
+using namespace gc;
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool valid_dtype(int dtype) { return dtype == GC_F32 || dtype == GC_BF16; }
+
+// Checks the descriptor and fills the geometry.  OH = (H-KH)/S + 1 and
+// OW = (W-KW)/S + 1 with integer division (no padding; the floor drops the
+// input rows/columns no window reaches).
+int check_desc(const gc_conv_desc *d, Geom *g)
+{
+    if (!d) return GC_ERR_INVALID_ARG;
+    if (d->B < 1 || d->IC < 1 || d->H < 1 || d->W < 1 || d->OC < 1 || d->KH < 1 ||
+        d->KW < 1 || d->stride < 1)
+        return GC_ERR_INVALID_ARG;
+    if (d->H < d->KH || d->W < d->KW) return GC_ERR_INVALID_ARG;
+    const long long OH = (d->H - d->KH) / d->stride + 1;
+    const long long OW = (d->W - d->KW) / d->stride + 1;
+    const long long nx = (long long)d->B * d->IC * d->H * d->W;
+    const long long ny = (long long)d->B * d->OC * OH * OW;
+    const long long nw = (long long)d->OC * d->IC * d->KH * d->KW;
+    if (nx > INT_MAX || ny > INT_MAX || nw > INT_MAX) return GC_ERR_INVALID_ARG;
+    if (g) *g = make_geom(d->B, d->IC, d->H, d->W, d->OC, d->KH, d->KW, d->stride);
+    return GC_OK;
+}
+
+bool aligned(const void *p, int dtype)
+{
+    const uintptr_t a = dtype == GC_F32 ? 4 : 2;
+    return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? GC_OK : GC_ERR_HIP; }
+
+size_t wgrad_ws_bytes(const Geom &g)
+{
+    const int splits = wgrad_generic_splits(g);
+    return size_t(splits) * g.OC * g.K * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gc_version(void) { return kVersion; }
+
+const char *gc_status_string(int status)
+{
+    switch (status) {
+    case GC_OK: return "GC_OK";
+    case GC_ERR_INVALID_ARG: return "GC_ERR_INVALID_ARG: invalid descriptor, flag, dtype or pointer";
+    case GC_ERR_UNSUPPORTED: return "GC_ERR_UNSUPPORTED: shape not supported by the kernels";
+    case GC_ERR_WORKSPACE: return "GC_ERR_WORKSPACE: workspace missing or too small";
+    case GC_ERR_HIP: return "GC_ERR_HIP: kernel launch failed";
+    default: return "unknown gc status";
+    }
+}
+
+int gc_conv_out_dims(const gc_conv_desc *d, int *OH, int *OW)
+{
+    Geom g;
+    const int st = check_desc(d, &g);
+    if (st != GC_OK) return st;
+    if (OH) *OH = g.OH;
+    if (OW) *OW = g.OW;
+    return GC_OK;
+}
+
+size_t gc_conv_workspace_bytes(int op, const gc_conv_desc *d, int dtype)
+{
+    Geom g;
+    if (check_desc(d, &g) != GC_OK || !valid_dtype(dtype)) return 0;
+    switch (op) {
+    case GC_OP_FWD: return 0;
+    case GC_OP_BWD_DATA: return 0;
+    case GC_OP_BWD_WEIGHT: return wgrad_ws_bytes(g);
+    default: return 0;
+    }
+}
+
+int gc_conv_fwd(const void *x, const void *w, void *y, void *workspace, size_t ws_bytes,
+                const gc_conv_desc *d, int relu, int dtype, void *stream)
+{
+    (void)workspace; (void)ws_bytes;
+    Geom g;
+    int st = check_desc(d, &g);
+    if (st != GC_OK) return st;
+    if (!valid_dtype(dtype) || (relu != 0 && relu != 1)) return GC_ERR_INVALID_ARG;
+    if (!x || !w || !y) return GC_ERR_INVALID_ARG;
+    if (!aligned(x, dtype) || !aligned(w, dtype) || !aligned(y, dtype)) return GC_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == GC_F32) return hip_status(launch_fwd_generic<float>(g, x, w, y, relu, s));
+    return hip_status(launch_fwd_generic<bf16_t>(g, x, w, y, relu, s));
+}
+
+int gc_conv_bwd_data(const void *dy, const void *w, const void *y_mask, void *dx,
+                     void *workspace, size_t ws_bytes, const gc_conv_desc *d, int relu,
+                     int dtype, void *stream)
+{
+    (void)workspace; (void)ws_bytes;
+    Geom g;
+    int st = check_desc(d, &g);
+    if (st != GC_OK) return st;
+    if (!valid_dtype(dtype) || (relu != 0 && relu != 1)) return GC_ERR_INVALID_ARG;
+    if (!dy || !w || !dx) return GC_ERR_INVALID_ARG;
+    if ((relu == 1) != (y_mask != nullptr)) return GC_ERR_INVALID_ARG;
+    if (!aligned(dy, dtype) || !aligned(w, dtype) || !aligned(dx, dtype) ||
+        (y_mask && !aligned(y_mask, dtype)))
+        return GC_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == GC_F32)
+        return hip_status(launch_dgrad_generic<float>(g, dy, w, y_mask, dx, relu, s));
+    return hip_status(launch_dgrad_generic<bf16_t>(g, dy, w, y_mask, dx, relu, s));
+}
+
+int gc_conv_bwd_weight(const void *x, const void *dy, const void *y_mask, void *dw,
+                       void *workspace, size_t ws_bytes, const gc_conv_desc *d, int relu,
+                       int dtype, void *stream)
+{
+    Geom g;
+    int st = check_desc(d, &g);
+    if (st != GC_OK) return st;
+    if (!valid_dtype(dtype) || (relu != 0 && relu != 1)) return GC_ERR_INVALID_ARG;
+    if (!x || !dy || !dw) return GC_ERR_INVALID_ARG;
+    if ((relu == 1) != (y_mask != nullptr)) return GC_ERR_INVALID_ARG;
+    if (!aligned(x, dtype) || !aligned(dy, dtype) || !aligned(dw, dtype) ||
+        (y_mask && !aligned(y_mask, dtype)))
+        return GC_ERR_INVALID_ARG;
+    const size_t need = wgrad_ws_bytes(g);
+    if (need && (!workspace || ws_bytes < need)) return GC_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 16) return GC_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int splits = wgrad_generic_splits(g);
+    float *part = static_cast<float *>(workspace);
+    hipError_t e;
+    if (dtype == GC_F32) {
+        e = launch_wgrad_generic<float>(g, x, dy, y_mask, part, splits, relu, s);
+        if (e == hipSuccess) e = launch_wgrad_reduce<float>(part, dw, splits, g.OC * g.K, s);
+    } else {
+        e = launch_wgrad_generic<bf16_t>(g, x, dy, y_mask, part, splits, relu, s);
+        if (e == hipSuccess) e = launch_wgrad_reduce<bf16_t>(part, dw, splits, g.OC * g.K, s);
+    }
+    return hip_status(e);
+}
+
+int64_t gc_fastdiv_selfcheck(uint32_t divisor, uint32_t n_end)
+{
+    if (divisor < 1 || n_end > 0x80000000u) return -1;
+    const FastDiv f = make_fastdiv(divisor);
+    int64_t bad = 0;
+    for (uint32_t n = 0; n < n_end; ++n) {
+        uint32_t q, r;
+        fdivmod(n, f, q, r);
+        if (q != n / divisor || r != n % divisor) ++bad;
+    }
+    return bad;
+}
+
+}  // extern "C"

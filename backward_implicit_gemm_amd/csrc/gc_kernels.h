@@ -1,0 +1,25 @@
+// gc_kernels.h -- launchers of the gfx950 kernels, called by the C ABI layer.
+#pragma once
+
+#include "gc_common.h"
+
+namespace gc {
+
+// Shape-generic implicit GEMM (igemm_generic.hip).
+template <typename T>
+hipError_t launch_fwd_generic(const Geom &g, const void *x, const void *w, void *y, int relu,
+                              hipStream_t s);
+template <typename T>
+hipError_t launch_dgrad_generic(const Geom &g, const void *dy, const void *w, const void *ym,
+                                void *dx, int relu, hipStream_t s);
+template <typename T>
+hipError_t launch_wgrad_generic(const Geom &g, const void *x, const void *dy, const void *ym,
+                                float *part, int splits, int relu, hipStream_t s);
+int wgrad_generic_splits(const Geom &g);
+
+// Fixed-order sum of split partials, then the store in the output type
+// (wgrad_reduce.hip).
+template <typename T>
+hipError_t launch_wgrad_reduce(const float *part, void *dw, int splits, int n, hipStream_t s);
+
+}  // namespace gc

@@ -1,0 +1,123 @@
+/*
+ * gc.h -- C ABI of libgc: 2-D convolution forward, d_input and wgrad as
+ * im2col-free implicit GEMMs on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one benchmarked in "Speedups to gemm_conv_forward and
+ * gemm_conv_backward kernels" (PufferLib pull request #522): a forward conv
+ * with an optional fused ReLU (the relu=1/relu=0 flag of its layer-1 and
+ * layer-2 benchmark lines), and a backward pass that produces the weight
+ * gradient ("wgrad") and the input gradient ("d_input"), in fp32 or bf16
+ * (its precision=fp32 / precision=bf16 runs).  Stride S, no padding, dilation
+ * 1, one group, no bias.  Output size: OH = (H-KH)/S + 1, OW = (W-KW)/S + 1
+ * (integer division; the page's layer 1 maps 11x15, K=5, S=3 to 3x4).
+ *
+ *   y [b,oc,oh,ow] = f( sum_{ic,kh,kw} x[b,ic,oh*S+kh,ow*S+kw] * w[oc,ic,kh,kw] )
+ *   dz             = relu ? dy * (y > 0) : dy          (derivative 0 at 0)
+ *   dx [b,ic,ih,iw] = sum over (oc,oh,ow,kh,kw) with oh*S+kh = ih and
+ *                     ow*S+kw = iw of dz[b,oc,oh,ow] * w[oc,ic,kh,kw]
+ *   dw [oc,ic,kh,kw] = sum_{b,oh,ow} dz[b,oc,oh,ow] * x[b,ic,oh*S+kh,ow*S+kw]
+ *
+ * Layouts: x, dx NCHW [B][IC][H][W]; w, dw OIHW [OC][IC][KH][KW]; y, dy NCHW
+ * [B][OC][OH][OW]; all dense and contiguous.  Storage type GC_F32 (IEEE fp32)
+ * or GC_BF16 (bfloat16, 16-bit words); every tensor of a call has that type.
+ * Products are accumulated in fp32; bf16 outputs are rounded to nearest even.
+ *
+ * Conventions common to every entry point:
+ *   - Pointers are device pointers (HBM), owned by the caller, at least
+ *     4-byte aligned for fp32 and 2-byte aligned for bf16.  The library
+ *     never allocates, frees or synchronises; it enqueues kernels on
+ *     `stream` (a hipStream_t; NULL means the default stream) and returns.
+ *   - Outputs are overwritten, never accumulated into; every element is
+ *     written, including exact zeros (input pixels no window covers).
+ *   - Scratch memory, where an operation needs it, is passed in as
+ *     `workspace` of `ws_bytes` bytes (device memory, 256-byte aligned);
+ *     gc_conv_workspace_bytes() gives the size.  NULL/0 is fine when that
+ *     size is 0.  Calls that overlap in time must not share a workspace.
+ *   - Errors: an invalid descriptor, flag, dtype or a NULL pointer returns
+ *     GC_ERR_INVALID_ARG before any HIP call; a workspace that is too small
+ *     returns GC_ERR_WORKSPACE; shapes the kernels cannot tile return
+ *     GC_ERR_UNSUPPORTED; a failed launch returns GC_ERR_HIP.  Nothing is
+ *     enqueued when an error is returned before the launch.
+ *   - Every element count (B*IC*H*W, B*OC*OH*OW, OC*IC*KH*KW) must be below
+ *     2^31; larger tensors are rejected with GC_ERR_INVALID_ARG.
+ *   - Entry points are reentrant and keep no state between calls.
+ */
+#ifndef GC_H
+#define GC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GC_OK = 0,
+    GC_ERR_INVALID_ARG = 1,
+    GC_ERR_UNSUPPORTED = 2,
+    GC_ERR_WORKSPACE = 3,
+    GC_ERR_HIP = 4
+} gc_status;
+
+typedef enum { GC_F32 = 0, GC_BF16 = 1 } gc_dtype;
+
+typedef enum { GC_OP_FWD = 0, GC_OP_BWD_DATA = 1, GC_OP_BWD_WEIGHT = 2 } gc_op;
+
+/* Problem size.  No padding, dilation 1, one group. */
+typedef struct {
+    int B, IC, H, W;   /* input  [B][IC][H][W] */
+    int OC, KH, KW;    /* weight [OC][IC][KH][KW] */
+    int stride;        /* S >= 1, the same along h and w */
+} gc_conv_desc;
+
+/* Output extent (pure host arithmetic).  Returns GC_OK and sets *OH, *OW, or
+ * GC_ERR_INVALID_ARG for a descriptor with any dimension < 1, H < KH, W < KW,
+ * stride < 1, or an element count of 2^31 or more. */
+int gc_conv_out_dims(const gc_conv_desc *d, int *OH, int *OW);
+
+/* Bytes of workspace that operation `op` needs for this problem and dtype
+ * (0 if none).  Returns 0 as well for an invalid descriptor. */
+size_t gc_conv_workspace_bytes(int op, const gc_conv_desc *d, int dtype);
+
+/* Forward pass: y = f(conv(x, w)), f = ReLU when relu == 1, identity when
+ * relu == 0.  x [B][IC][H][W], w [OC][IC][KH][KW] in, y [B][OC][OH][OW] out. */
+int gc_conv_fwd(const void *x, const void *w, void *y,
+                void *workspace, size_t ws_bytes,
+                const gc_conv_desc *d, int relu, int dtype, void *stream);
+
+/* d_input: dx from dy and w.  With relu == 1, dy is masked by (y_mask > 0),
+ * y_mask being the forward output y; y_mask must be NULL when relu == 0.
+ * dy [B][OC][OH][OW], w [OC][IC][KH][KW], y_mask like dy; dx [B][IC][H][W]
+ * out (gather form, no atomics: each dx element is written once). */
+int gc_conv_bwd_data(const void *dy, const void *w, const void *y_mask, void *dx,
+                     void *workspace, size_t ws_bytes,
+                     const gc_conv_desc *d, int relu, int dtype, void *stream);
+
+/* wgrad: dw from x and dy (masked by y_mask > 0 when relu == 1; y_mask NULL
+ * when relu == 0).  The sum over B*OH*OW is split across workgroups into fp32
+ * partials in `workspace` and finished by a fixed-order reduction, so the
+ * result is bit-identical from run to run. */
+int gc_conv_bwd_weight(const void *x, const void *dy, const void *y_mask, void *dw,
+                       void *workspace, size_t ws_bytes,
+                       const gc_conv_desc *d, int relu, int dtype, void *stream);
+
+/* Human-readable name of a status code. */
+const char *gc_status_string(int status);
+
+/* Index-mapper self-check (pure host): builds the magic-number divider for
+ * `divisor` exactly as the kernels use it (Granlund & Montgomery, "Division
+ * by invariant integers using multiplication", 1994), applies it to every
+ * n in [0, n_end) with the same arithmetic the device performs, and returns
+ * the number of quotients or remainders that differ from n / divisor and
+ * n % divisor.  Requires 1 <= divisor and n_end <= 2^31; returns -1 otherwise. */
+int64_t gc_fastdiv_selfcheck(uint32_t divisor, uint32_t n_end);
+
+/* Library version, as major*10000 + minor*100 + patch. */
+int gc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GC_H */

@@ -1,0 +1,151 @@
+"""Host-side checks of libgc's C ABI (no GPU needed).
+
+The library must load and export every function include/gc.h declares; the
+pure-host entry points (output size, workspace size, status strings, the
+index-mapper self-check) must be right; and every invalid call must be
+rejected before the first HIP call, which is why these run without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from backward_implicit_gemm_amd import binding as gb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gc.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(gc_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("gc_conv_fwd", "gc_conv_bwd_data", "gc_conv_bwd_weight"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = gb.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert set(declared_functions()) == set(gb.EXPORTED)
+
+
+def test_out_dims_page1_layers():
+    assert gb.gc_conv_out_dims(gb.make_desc(1024, 59, 11, 15, 128, 5, 5, 3)) == (3, 4)
+    assert gb.gc_conv_out_dims(gb.make_desc(1024, 128, 3, 4, 128, 3, 3, 1)) == (1, 2)
+    assert gb.gc_conv_out_dims(gb.make_desc(1, 1, 7, 9, 1, 2, 3, 2)) == (3, 4)
+
+
+@pytest.mark.parametrize("bad", [
+    (0, 1, 3, 3, 1, 3, 3, 1), (1, 0, 3, 3, 1, 3, 3, 1), (1, 1, 2, 3, 1, 3, 3, 1),
+    (1, 1, 3, 2, 1, 3, 3, 1), (1, 1, 3, 3, 0, 3, 3, 1), (1, 1, 3, 3, 1, 3, 3, 0),
+    (1, 1, 3, 3, 1, 0, 3, 1), (-1, 1, 3, 3, 1, 3, 3, 1),
+    (1 << 16, 1 << 10, 64, 64, 1, 1, 1, 1),      # B*IC*H*W >= 2^31
+    (1 << 20, 1, 1, 1, 4096, 1, 1, 1),          # B*OC*OH*OW >= 2^31
+])
+def test_invalid_descriptors_rejected(bad):
+    d = gb.make_desc(*bad)
+    oh, ow = ctypes.c_int(), ctypes.c_int()
+    assert gb.lib().gc_conv_out_dims(ctypes.byref(d), ctypes.byref(oh), ctypes.byref(ow)) == gb.GC_ERR_INVALID_ARG
+    assert gb.gc_conv_workspace_bytes(gb.GC_OP_BWD_WEIGHT, d, gb.GC_F32) == 0
+
+
+def test_null_descriptor_rejected():
+    L = gb.lib()
+    assert L.gc_conv_out_dims(None, None, None) == gb.GC_ERR_INVALID_ARG
+    assert L.gc_conv_fwd(None, None, None, None, 0, None, 0, 0, None) == gb.GC_ERR_INVALID_ARG
+
+
+FAKE = ctypes.c_void_p(0x10000)    # never dereferenced: every call below fails validation
+
+
+def _call(fn, *ptrs, desc, relu, dtype, ws=None, ws_bytes=0):
+    L = gb.lib()
+    return getattr(L, fn)(*ptrs, ws, ws_bytes, ctypes.byref(desc), relu, dtype, None)
+
+
+L1 = gb.make_desc(1024, 59, 11, 15, 128, 5, 5, 3)
+
+
+def test_fwd_argument_errors():
+    assert _call("gc_conv_fwd", None, FAKE, FAKE, desc=L1, relu=1, dtype=0) == gb.GC_ERR_INVALID_ARG
+    assert _call("gc_conv_fwd", FAKE, FAKE, None, desc=L1, relu=1, dtype=0) == gb.GC_ERR_INVALID_ARG
+    assert _call("gc_conv_fwd", FAKE, FAKE, FAKE, desc=L1, relu=2, dtype=0) == gb.GC_ERR_INVALID_ARG
+    assert _call("gc_conv_fwd", FAKE, FAKE, FAKE, desc=L1, relu=0, dtype=7) == gb.GC_ERR_INVALID_ARG
+    odd = ctypes.c_void_p(0x10002)
+    assert _call("gc_conv_fwd", odd, FAKE, FAKE, desc=L1, relu=0, dtype=gb.GC_F32) == gb.GC_ERR_INVALID_ARG
+    odd = ctypes.c_void_p(0x10001)
+    assert _call("gc_conv_fwd", odd, FAKE, FAKE, desc=L1, relu=0, dtype=gb.GC_BF16) == gb.GC_ERR_INVALID_ARG
+    bad = gb.make_desc(1, 1, 2, 2, 1, 3, 3, 1)
+    assert _call("gc_conv_fwd", FAKE, FAKE, FAKE, desc=bad, relu=0, dtype=0) == gb.GC_ERR_INVALID_ARG
+
+
+def test_backward_mask_must_match_relu():
+    # relu=1 needs y_mask; relu=0 forbids it
+    assert _call("gc_conv_bwd_data", FAKE, FAKE, None, FAKE, desc=L1, relu=1, dtype=0) == gb.GC_ERR_INVALID_ARG
+    assert _call("gc_conv_bwd_data", FAKE, FAKE, FAKE, FAKE, desc=L1, relu=0, dtype=0) == gb.GC_ERR_INVALID_ARG
+    assert _call("gc_conv_bwd_weight", FAKE, FAKE, None, FAKE, desc=L1, relu=1, dtype=0) == gb.GC_ERR_INVALID_ARG
+    assert _call("gc_conv_bwd_weight", FAKE, FAKE, FAKE, FAKE, desc=L1, relu=0, dtype=0) == gb.GC_ERR_INVALID_ARG
+
+
+def test_wgrad_workspace_errors():
+    need = gb.gc_conv_workspace_bytes(gb.GC_OP_BWD_WEIGHT, L1, gb.GC_BF16)
+    assert need > 0
+    assert _call("gc_conv_bwd_weight", FAKE, FAKE, FAKE, FAKE, desc=L1, relu=1, dtype=gb.GC_BF16,
+                 ws=None, ws_bytes=0) == gb.GC_ERR_WORKSPACE
+    assert _call("gc_conv_bwd_weight", FAKE, FAKE, FAKE, FAKE, desc=L1, relu=1, dtype=gb.GC_BF16,
+                 ws=FAKE, ws_bytes=need - 1) == gb.GC_ERR_WORKSPACE
+
+
+def test_workspace_sizes_are_sane():
+    for d in (L1, gb.make_desc(1024, 128, 3, 4, 128, 3, 3, 1), gb.make_desc(3, 2, 5, 5, 3, 2, 2, 1)):
+        for dt in (gb.GC_F32, gb.GC_BF16):
+            n = gb.gc_conv_workspace_bytes(gb.GC_OP_BWD_WEIGHT, d, dt)
+            K = d.IC * d.KH * d.KW
+            assert n % (d.OC * K * 4) == 0 and n >= d.OC * K * 4
+            assert n <= 64 * d.OC * K * 4
+    assert gb.gc_conv_workspace_bytes(99, L1, 0) == 0
+
+
+def test_status_strings():
+    for s in range(5):
+        assert gb.status_string(s).startswith("GC_")
+    assert "unknown" in gb.status_string(42)
+
+
+# Divisors the kernels split by at the page's layer shapes and the chain:
+# P = OH*OW, OW, KK = KH*KW, KW, HW = H*W, W, S.
+LAYER_DIVISORS = [12, 4, 25, 5, 165, 15, 3, 2, 9, 1]
+
+
+@pytest.mark.parametrize("d", LAYER_DIVISORS)
+def test_fastdiv_exhaustive_over_used_ranges(d):
+    # largest numerator: B*H*W at B=32768 on the 11x15 input (5.4M), doubled
+    assert gb.lib().gc_fastdiv_selfcheck(d, 11_000_000) == 0
+
+
+@pytest.mark.parametrize("d", [1, 3, 7, 1475, 1152, 9735, 65537, 2**31 - 1, 2**30 + 3])
+def test_fastdiv_random_divisors_prefix(d):
+    assert gb.lib().gc_fastdiv_selfcheck(d, 4_000_000) == 0
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("d", [3, 165])
+def test_fastdiv_full_31bit_range(d):
+    assert gb.lib().gc_fastdiv_selfcheck(d, 2**31) == 0
+
+
+def test_fastdiv_rejects_bad_args():
+    assert gb.lib().gc_fastdiv_selfcheck(0, 10) == -1
+    assert gb.lib().gc_fastdiv_selfcheck(3, 2**31 + 1) == -1
+
+
+def test_version():
+    assert gb.lib().gc_version() >= 100

@@ -1,0 +1,207 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Covers the policy-network layer shapes of "Speedups to gemm_conv_forward and
+gemm_conv_backward kernels" (PufferLib pull request #522) at their full
+batch of 1024 in fp32 and bf16, the two-layer chain at B=16384 on sampled
+outputs, an odd-shape sweep whose tiles end mid-tile, integer-valued inputs
+that must match bit for bit, and run-to-run determinism of wgrad.
+"""
+import numpy as np
+import pytest
+import torch
+
+from backward_implicit_gemm_amd import binding as gb
+from backward_implicit_gemm_amd import inputs
+from oracle import oracle as orc
+
+from parity import TOL, Layer, check_layer, draw, f64, gpu_layer, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    gb.lib()
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads (B=1024), every output element against the oracle
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3], ids=[w.name for w in inputs.WORKLOADS[:4]])
+def test_workload_full_parity(idx):
+    wl = inputs.WORKLOADS[idx]
+    L = wl.layers[0]
+    layer = Layer.of(L)
+    x, w, dy = inputs.layer_inputs(L, wl.seeds, wl.dtype)
+    errs, (y, dx, dw), (y_ref, _, _) = check_layer(layer, wl.dtype, x=x, w=w, dy=dy)
+    print(f"{wl.name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    if layer.relu:
+        flips = int(np.sum((f64(y) > 0) != (y_ref > 0)))
+        print(f"{wl.name}: ReLU mask disagreements with the oracle's y: {flips}", flush=True)
+    if layer.W == 15 and layer.KW == 5 and layer.stride == 3:
+        # layer-1 input column 14 is covered by no window
+        assert torch.all(dx[..., 14] == 0)
+
+
+# ---------------------------------------------------------------------------
+# Two-layer chain at B=16384, stage-wise on sampled outputs
+# ---------------------------------------------------------------------------
+
+def _sample(shape, n, seed):
+    r = np.random.default_rng(seed)
+    return np.stack([r.integers(0, s, n) for s in shape], axis=1)
+
+
+def test_chain_b16384_sampled():
+    wl = inputs.WORKLOADS[4]
+    l1, l2 = (Layer.of(L) for L in wl.layers)
+    t = inputs.workload_inputs(wl)
+    dev = "cuda"
+    td = torch.bfloat16
+    c1 = gb.Conv(l1.x_shape, l1.w_shape, l1.stride, l1.relu, td, dev)
+    c2 = gb.Conv(l2.x_shape, l2.w_shape, l2.stride, l2.relu, td, dev)
+    x, w1, w2, dy2 = (t[k].to(dev) for k in ("x", "w1", "w2", "dy"))
+    y1 = torch.empty(l1.y_shape, dtype=td, device=dev)
+    y2 = torch.empty(l2.y_shape, dtype=td, device=dev)
+    dy1 = torch.empty_like(y1)
+    dw2 = torch.empty_like(w2)
+    dx1 = torch.empty_like(x)
+    dw1 = torch.empty_like(w1)
+    c1.fwd(x, w1, y1)
+    c2.fwd(y1, w2, y2)
+    c2.bwd_data(dy2, w2, None, dy1)
+    c2.bwd_weight(y1, dy2, None, dw2)
+    c1.bwd_data(dy1, w1, y1, dx1)
+    c1.bwd_weight(x, dy1, y1, dw1)
+    torch.cuda.synchronize()
+
+    n = 400
+    X, W1, W2, DY2 = f64(t["x"]), f64(t["w1"]), f64(t["w2"]), f64(t["dy"])
+    Y1, DY1 = f64(y1), f64(dy1)
+    checks = []
+    c = _sample(l1.y_shape, n, 1)
+    checks.append(("y1", f64(y1)[tuple(c.T)], orc.conv_fwd_at(X, W1, c, l1.stride, 1)))
+    c = _sample(l2.y_shape, n, 2)
+    checks.append(("y2", f64(y2)[tuple(c.T)], orc.conv_fwd_at(Y1, W2, c, l2.stride, 0)))
+    c = _sample(l2.x_shape, n, 3)
+    checks.append(("dy1", DY1[tuple(c.T)],
+                   orc.conv_bwd_data_at(DY2, W2, None, l2.x_shape, c, l2.stride, 0)))
+    c = _sample(l2.w_shape, n, 4)
+    checks.append(("dw2", f64(dw2)[tuple(c.T)],
+                   orc.conv_bwd_weight_at(Y1, DY2, None, l2.w_shape, c, l2.stride, 0)))
+    c = _sample(l1.x_shape, n, 5)
+    checks.append(("dx1", f64(dx1)[tuple(c.T)],
+                   orc.conv_bwd_data_at(DY1, W1, Y1, l1.x_shape, c, l1.stride, 1)))
+    c = _sample(l1.w_shape, n, 6)
+    checks.append(("dw1", f64(dw1)[tuple(c.T)],
+                   orc.conv_bwd_weight_at(X, DY1, Y1, l1.w_shape, c, l1.stride, 1)))
+    for name, got, ref in checks:
+        e = rel_err(got, ref)
+        print(f"chain {name}: sampled max|diff|/max|ref| = {e:.2e}", flush=True)
+        assert e <= TOL["bf16"], (name, e)
+    assert torch.all(dx1[..., 14] == 0)
+    assert torch.isfinite(dx1.float()).all() and torch.isfinite(dw1.float()).all()
+
+
+# ---------------------------------------------------------------------------
+# Odd shapes: ragged batches, channel counts around tile edges, H != W,
+# KH != KW, strides 1-4, full-window and pointwise kernels
+# ---------------------------------------------------------------------------
+
+ODD = [
+    # B, IC, H, W, OC, KH, KW, S
+    (1, 1, 1, 1, 1, 1, 1, 1),
+    (1, 1, 5, 5, 1, 3, 3, 1),
+    (3, 3, 7, 8, 4, 3, 3, 2),
+    (17, 59, 11, 15, 128, 5, 5, 3),
+    (17, 128, 3, 4, 128, 3, 3, 1),
+    (3, 64, 9, 6, 65, 2, 4, 1),
+    (2, 65, 10, 10, 33, 3, 2, 4),
+    (5, 7, 6, 6, 130, 6, 6, 1),
+    (4, 16, 12, 20, 24, 1, 1, 1),
+    (2, 3, 32, 32, 8, 5, 5, 2),
+    (2, 200, 3, 3, 7, 3, 3, 1),
+    (33, 1, 11, 15, 3, 5, 5, 3),
+]
+
+
+@pytest.mark.parametrize("shape", ODD, ids=["x".join(map(str, s)) for s in ODD])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("relu", [0, 1])
+def test_odd_shapes(shape, dtype, relu):
+    layer = Layer(*shape, relu)
+    errs, _, _ = check_layer(layer, dtype, seeds=(sum(shape), 7, 8 + relu))
+    print(f"{shape} {dtype} relu={relu}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()),
+          flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Integer-valued inputs: every partial sum is an exact small integer, so the
+# result cannot depend on summation order and must match exactly.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(64, 59, 11, 15, 128, 5, 5, 3), (64, 128, 3, 4, 128, 3, 3, 1)])
+def test_integer_inputs_exact(shape, dtype):
+    layer = Layer(*shape, relu=1)
+    x = inputs.integers(layer.x_shape, 21, dtype=dtype)
+    w = inputs.integers(layer.w_shape, 22, dtype=dtype)
+    dy = inputs.integers(layer.y_shape, 23, dtype=dtype)
+    _, y, dx, dw = gpu_layer(layer, x, w, dy, dtype)
+    ym = f64(y)
+    y_ref = orc.conv_fwd(f64(x), f64(w), layer.stride, 1)
+    dx_ref = orc.conv_bwd_data(f64(dy), f64(w), ym, layer.x_shape, layer.stride, 1)
+    dw_ref = orc.conv_bwd_weight(f64(x), f64(dy), ym, layer.w_shape, layer.stride, 1)
+    td = inputs.torch_dtype(dtype)
+    rne = lambda a: torch.from_numpy(a).to(torch.float32).to(td).to(torch.float64).numpy()
+    for name, got, ref in (("y", y, y_ref), ("dx", dx, dx_ref), ("dw", dw, dw_ref)):
+        assert np.all(np.abs(ref) < 2 ** 24)
+        assert np.array_equal(f64(got), rne(ref)), name
+
+
+# ---------------------------------------------------------------------------
+# wgrad is bit-reproducible (fixed-order split-K reduction, no atomics)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_wgrad_deterministic(dtype):
+    L = inputs.LAYER1
+    layer = Layer.of(L)
+    x, w, dy = inputs.layer_inputs(L, (11, 12, 13), dtype)
+    conv, y, dx, dw = gpu_layer(layer, x, w, dy, dtype)
+    xd, dyd = x.cuda(), dy.cuda()
+    for _ in range(3):
+        dw2 = torch.empty_like(dw)
+        conv.bwd_weight(xd, dyd, y, dw2)
+        dx2 = torch.empty_like(dx)
+        conv.bwd_data(dyd, w.cuda(), y, dx2)
+        torch.cuda.synchronize()
+        assert torch.equal(dw2.view(torch.int16) if dtype == "bf16" else dw2.view(torch.int32),
+                           dw.view(torch.int16) if dtype == "bf16" else dw.view(torch.int32))
+        assert torch.equal(dx2, dx)
+
+
+def test_outputs_fully_overwritten():
+    # Outputs start as NaN in gpu_layer; every element must have been written.
+    layer = Layer(5, 59, 11, 15, 128, 5, 5, 3, 1)
+    x, w, dy = draw(layer, (1, 2, 3), "bf16")
+    _, y, dx, dw = gpu_layer(layer, x, w, dy, "bf16")
+    for t in (y, dx, dw):
+        assert torch.isfinite(t.float()).all()
+
+
+def test_bf16_rounding_is_nearest_even():
+    # 1x1 conv with w = 1 copies x through the fp32 accumulator; pick fp32
+    # values that sit exactly on bf16 ties is impossible from bf16 inputs, so
+    # use w = 1 + 2^-8 on bf16 x: products land between bf16 neighbours and
+    # the stored result must equal torch's round-to-nearest-even of the fp32
+    # product.
+    B, C = 4, 1
+    x = inputs.normal((B, C, 8, 8), 5, "bf16")
+    w = torch.full((1, 1, 1, 1), 1.0 + 2 ** -7, dtype=torch.bfloat16)
+    layer = Layer(B, C, 8, 8, 1, 1, 1, 1, 0)
+    dy = torch.zeros(layer.y_shape, dtype=torch.bfloat16)
+    _, y, _, _ = gpu_layer(layer, x, w, dy, "bf16")
+    want = (x.float() * w.float()).to(torch.bfloat16)
+    assert torch.equal(y.cpu(), want)
