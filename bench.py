@@ -1,0 +1,281 @@
+"""Benchmark: convolution forward + d_input + wgrad through libgc's C ABI.
+
+One step is one pass of the whole path over one batch -- forward (with the
+fused ReLU where the layer has one), d_input and wgrad -- on synthetic seeded
+inputs already resident in HBM.  The default workload is the policy
+network's layer 1 in fp32 at B=1024 (59->128 channels, 11x15 input, 5x5
+kernel, stride 3, ReLU), as benchmarked in "Speedups to gemm_conv_forward and
+gemm_conv_backward kernels" (PufferLib pull request #522), which times
+forward and backward separately over 50 warmup and 200 timed iterations.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
+
+Prints one JSON line per workload: throughput in TFLOP/s of algorithmic work
+(2*B*OC*OH*OW*IC*KH*KW per pass, three passes per step), per-pass times from
+HIP events recorded on the launch stream around every call of the timed
+region, a roofline entry for the dominant kernel, and the CPU oracle timed
+on this host on a bounded sample (default workload only).
+"""
+import argparse
+import hashlib
+import glob
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "conv fwd+bwd µs/iter and TFLOP/s at B=1024 (layer1/layer2, fp32/bf16)"
+DEFAULT_WORKLOAD = "layer1_fp32_relu_b1024"
+
+# MI355X published peaks.
+PEAK = {"mfma_f32": 157.3, "mfma_bf16": 2500.0, "hbm_gbs": 8000.0}
+
+# Page 1's fast kernels (gemm_fast), unnamed NVIDIA GPU, microseconds per
+# iteration for forward and for backward (wgrad + d_input): context only.
+PAGE1_US = {
+    "layer1_fp32_relu_b1024": (192.4102, 541.7361),
+    "layer2_fp32_b1024": (56.8698, 100.2875),
+    "layer1_bf16_relu_b1024": (106.4277, 403.5356),
+    "layer2_bf16_b1024": (18.4427, 49.1440),
+}
+
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--all", action="store_true", help="every workload, one line each")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle leg")
+    return ap.parse_args()
+
+
+def layer_flops(L):
+    return 2.0 * L.B * L.OC * L.OH * L.OW * L.IC * L.KH * L.KW
+
+
+def layer_bytes(L, esize):
+    """Algorithmic bytes: each tensor read once, each output written once."""
+    nx = L.B * L.IC * L.H * L.W
+    nw = L.OC * L.IC * L.KH * L.KW
+    ny = L.B * L.OC * L.OH * L.OW
+    fwd = (nx + nw + ny) * esize
+    dgrad = (ny + (ny if L.relu else 0) + nw + nx) * esize
+    wgrad = (nx + ny + (ny if L.relu else 0) + nw) * esize
+    return {"fwd": fwd, "dgrad": dgrad, "wgrad": wgrad}
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "backward_implicit_gemm_amd", "csrc", "*"))):
+        h.update(os.path.basename(p).encode())
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, op):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources; else None."""
+    try:
+        t = json.load(open(PROFILE_TRAFFIC))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_digest") != source_digest():
+        return None
+    e = t.get("entries", {}).get(f"{workload}/{op}")
+    return None if e is None else e.get("bytes_per_launch")
+
+
+def run_gpu(wl, steps, warmup):
+    import torch
+
+    from backward_implicit_gemm_amd import binding as gb
+    from backward_implicit_gemm_amd import inputs
+
+    dev = torch.device("cuda:0")
+    td = inputs.torch_dtype(wl.dtype)
+    t = inputs.workload_inputs(wl)
+    layers = wl.layers
+    convs = [gb.Conv(L.x_shape, L.w_shape, L.stride, L.relu, td, dev) for L in layers]
+    if len(layers) == 1:
+        xs = [t["x"].to(dev)]
+        ws = [t["w"].to(dev)]
+    else:
+        xs = [t["x"].to(dev), None]
+        ws = [t["w1"].to(dev), t["w2"].to(dev)]
+    ys = [torch.empty(L.y_shape, dtype=td, device=dev) for L in layers]
+    if len(layers) == 2:
+        xs[1] = ys[0]
+    dys = [None] * len(layers)
+    dys[-1] = t["dy"].to(dev)
+    for i in range(len(layers) - 1):
+        dys[i] = torch.empty(layers[i].y_shape, dtype=td, device=dev)
+    dxs = [torch.empty(L.x_shape, dtype=td, device=dev) if i == 0 else dys[i - 1]
+           for i, L in enumerate(layers)]
+    dws = [torch.empty(L.w_shape, dtype=td, device=dev) for L in layers]
+    stream = torch.cuda.current_stream()
+
+    # calls of one step, in order: forward through the layers, then backward
+    calls = []
+    for i, c in enumerate(convs):
+        calls.append((f"fwd{i + 1}", lambda c=c, i=i: c.fwd(xs[i], ws[i], ys[i])))
+    for i in reversed(range(len(convs))):
+        c = convs[i]
+        calls.append((f"dgrad{i + 1}", lambda c=c, i=i: c.bwd_data(dys[i], ws[i], ys[i], dxs[i])))
+        calls.append((f"wgrad{i + 1}", lambda c=c, i=i: c.bwd_weight(xs[i], dys[i], ys[i], dws[i])))
+
+    for _ in range(warmup):
+        for _, f in calls:
+            f()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(steps):
+        ev[s][0].record(stream)
+        for j, (_, f) in enumerate(calls):
+            f()
+            ev[s][j + 1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    per_call = {}
+    for j, (name, _) in enumerate(calls):
+        per_call[name] = statistics.mean(ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(steps)) * 1e3
+    return total_ms / steps, per_call
+
+
+def cpu_baseline(wl, budget_s):
+    """The oracle (fp64, OpenMP) on a bounded sample of the workload's batch."""
+    import numpy as np
+
+    from backward_implicit_gemm_amd import inputs
+    from oracle import oracle as orc
+
+    L = wl.layers[0]
+    x, w, dy = inputs.layer_inputs(L, wl.seeds, wl.dtype)
+    f64 = lambda a: a.to(dtype=__import__("torch").float64).numpy()
+    X, Wt, DY = f64(x), f64(w), f64(dy)
+
+    def step(nb):
+        xs, dys = X[:nb], DY[:nb]
+        t0 = time.perf_counter()
+        y = orc.conv_fwd(xs, Wt, L.stride, L.relu)
+        orc.conv_bwd_data(dys, Wt, y if L.relu else None, xs.shape, L.stride, L.relu)
+        orc.conv_bwd_weight(xs, dys, y if L.relu else None, Wt.shape, L.stride, L.relu)
+        return time.perf_counter() - t0
+
+    # size the sample from a small probe so the leg takes about budget_s
+    probe_b = min(L.B, 16)
+    tp = step(probe_b)
+    nb = int(min(L.B, max(probe_b, probe_b * (budget_s / 3.0) / max(tp, 1e-6))))
+    times = [step(nb) for _ in range(3)]
+    t = statistics.median(times)
+    flops = 3 * layer_flops(L.with_batch(nb))
+    return {
+        "value": flops / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": orc.thread_count(),
+        "kind": "oracle",
+        "sample": f"{nb} of {L.B} images of {wl.name}, fwd+dgrad+wgrad in fp64, median of 3",
+        "ms_per_step_sample": t * 1e3,
+    }
+
+
+def report(wl, ms_step, per_call, steps, warmup, cpu):
+    L0 = wl.layers[0]
+    esize = 4 if wl.dtype == "f32" else 2
+    flops_step = sum(3 * layer_flops(L) for L in wl.layers)
+    # per-call algorithmic work
+    work = {}
+    for i, L in enumerate(wl.layers):
+        b = layer_bytes(L, esize)
+        for op in ("fwd", "dgrad", "wgrad"):
+            work[f"{op}{i + 1}"] = (layer_flops(L), b[op])
+    dom = max(per_call, key=per_call.get)
+    fl, by = work[dom]
+    us = per_call[dom]
+    if wl.dtype == "f32":
+        bound, peak, unit, achieved = "mfma", PEAK["mfma_f32"], "TFLOP/s", fl / (us * 1e-6) / 1e12
+    else:
+        # bf16 at these shapes sits left of the MFMA ridge: HBM-bound
+        bound, peak, unit, achieved = "hbm", PEAK["hbm_gbs"], "GB/s", by / (us * 1e-6) / 1e9
+    roof = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": measured_traffic(wl.name, dom),
+            "kernel_call": dom, "us_per_launch": round(us, 3)}
+    value = flops_step / (ms_step * 1e-3) / 1e12
+    fwd_us = sum(v for k, v in per_call.items() if k.startswith("fwd"))
+    bwd_us = sum(v for k, v in per_call.items() if not k.startswith("fwd"))
+    vs = None
+    if wl.name in PAGE1_US:
+        page_us = sum(PAGE1_US[wl.name])
+        vs = round(page_us / (ms_step * 1e3), 3)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": vs,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "global_batch": L0.B,
+            "layers": [f"{L.IC}->{L.OC} {L.H}x{L.W} k{L.KH}x{L.KW} s{L.stride}"
+                       + (" relu" if L.relu else "") for L in wl.layers],
+            "parallelism": "none (one GPU)",
+        },
+        "us_per_iter": {"fwd": round(fwd_us, 3), "bwd": round(bwd_us, 3),
+                        **{k: round(v, 3) for k, v in per_call.items()}},
+        "tflops": {"fwd": round(sum(layer_flops(L) for L in wl.layers) / (fwd_us * 1e-6) / 1e12, 3),
+                   "bwd": round(sum(2 * layer_flops(L) for L in wl.layers) / (bwd_us * 1e-6) / 1e12, 3)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    if vs is not None:
+        line["baseline_note"] = ("page 1 gemm_fast fwd+bwd on an unnamed NVIDIA GPU: "
+                                 f"{PAGE1_US[wl.name][0]} + {PAGE1_US[wl.name][1]} us; context only")
+    return line
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported "
+              "(this library has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+    from backward_implicit_gemm_amd import inputs
+
+    names = [w.name for w in inputs.WORKLOADS]
+    todo = names if a.all else [a.workload]
+    for name in todo:
+        if name not in names:
+            print(f"unknown workload {name}; choose from {names}", file=sys.stderr)
+            sys.exit(2)
+        wl = inputs.WORKLOADS[names.index(name)]
+        ms, per_call = run_gpu(wl, a.steps, a.warmup)
+        cpu = None
+        if not a.no_cpu and name == DEFAULT_WORKLOAD:
+            cpu = cpu_baseline(wl, a.cpu_seconds)
+        print(json.dumps(report(wl, ms, per_call, a.steps, a.warmup, cpu)), flush=True)
+
+
+if __name__ == "__main__":
+    main()
