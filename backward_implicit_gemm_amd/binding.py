@@ -20,7 +20,9 @@ GC_OP_FWD, GC_OP_BWD_DATA, GC_OP_BWD_WEIGHT = 0, 1, 2
 EXPORTED = (
     "gc_conv_out_dims", "gc_conv_workspace_bytes", "gc_conv_fwd", "gc_conv_bwd_data",
     "gc_conv_bwd_weight", "gc_status_string", "gc_fastdiv_selfcheck", "gc_version",
+    "gc_set_kernel_policy",
 )
+GC_POLICY_AUTO, GC_POLICY_GENERIC = 0, 1
 
 
 class GcError(RuntimeError):
@@ -62,8 +64,19 @@ def lib():
     L.gc_fastdiv_selfcheck.restype = ctypes.c_int64
     L.gc_version.argtypes = []
     L.gc_version.restype = i
+    L.gc_set_kernel_policy.argtypes = [i]
+    L.gc_set_kernel_policy.restype = i
     _lib = L
     return L
+
+
+def gc_set_kernel_policy(policy):
+    """Process-wide kernel selection (GC_POLICY_AUTO or GC_POLICY_GENERIC);
+    returns the previous policy."""
+    prev = lib().gc_set_kernel_policy(int(policy))
+    if prev < 0:
+        raise ValueError(f"unknown kernel policy {policy}")
+    return prev
 
 
 def status_string(status):

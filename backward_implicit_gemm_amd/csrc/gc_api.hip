@@ -4,8 +4,11 @@
 // testable on a machine without a GPU.
 #include <limits.h>
 
+#include <atomic>
+
 #include "../../include/gc.h"
 #include "gc_kernels.h"
+#include "ig_common.h"
 
 using namespace gc;
 
@@ -43,10 +46,27 @@ bool aligned(const void *p, int dtype)
 
 int hip_status(hipError_t e) { return e == hipSuccess ? GC_OK : GC_ERR_HIP; }
 
-size_t wgrad_ws_bytes(const Geom &g)
+std::atomic<int> g_policy{GC_POLICY_AUTO};
+
+bool use_ig() { return g_policy.load(std::memory_order_relaxed) == GC_POLICY_AUTO; }
+
+// Number of fp32 partial tiles wgrad writes for this problem, and the plan
+// of the image-group kernel when it runs.
+int wgrad_splits(const Geom &g, int dtype, WgradIgPlan *ig, bool *use)
 {
-    const int splits = wgrad_generic_splits(g);
-    return size_t(splits) * g.OC * g.K * sizeof(float);
+    WgradIgPlan p;
+    if (dtype == GC_F32 && use_ig() && plan_wgrad_ig_f32(g, p)) {
+        if (ig) *ig = p;
+        if (use) *use = true;
+        return p.splits;
+    }
+    if (use) *use = false;
+    return wgrad_generic_splits(g);
+}
+
+size_t wgrad_ws_bytes(const Geom &g, int dtype)
+{
+    return size_t(wgrad_splits(g, dtype, nullptr, nullptr)) * g.OC * g.K * sizeof(float);
 }
 
 }  // namespace
@@ -84,7 +104,7 @@ size_t gc_conv_workspace_bytes(int op, const gc_conv_desc *d, int dtype)
     switch (op) {
     case GC_OP_FWD: return 0;
     case GC_OP_BWD_DATA: return 0;
-    case GC_OP_BWD_WEIGHT: return wgrad_ws_bytes(g);
+    case GC_OP_BWD_WEIGHT: return wgrad_ws_bytes(g, dtype);
     default: return 0;
     }
 }
@@ -100,7 +120,12 @@ int gc_conv_fwd(const void *x, const void *w, void *y, void *workspace, size_t w
     if (!x || !w || !y) return GC_ERR_INVALID_ARG;
     if (!aligned(x, dtype) || !aligned(w, dtype) || !aligned(y, dtype)) return GC_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (dtype == GC_F32) return hip_status(launch_fwd_generic<float>(g, x, w, y, relu, s));
+    if (dtype == GC_F32) {
+        FwdIgPlan p;
+        if (use_ig() && plan_fwd_ig_f32(g, p))
+            return hip_status(launch_fwd_ig_f32(g, p, x, w, y, relu, s));
+        return hip_status(launch_fwd_generic<float>(g, x, w, y, relu, s));
+    }
     return hip_status(launch_fwd_generic<bf16_t>(g, x, w, y, relu, s));
 }
 
@@ -119,8 +144,12 @@ int gc_conv_bwd_data(const void *dy, const void *w, const void *y_mask, void *dx
         (y_mask && !aligned(y_mask, dtype)))
         return GC_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (dtype == GC_F32)
+    if (dtype == GC_F32) {
+        DgradIgPlan p;
+        if (use_ig() && plan_dgrad_ig_f32(g, p))
+            return hip_status(launch_dgrad_ig_f32(g, p, dy, w, y_mask, dx, relu, s));
         return hip_status(launch_dgrad_generic<float>(g, dy, w, y_mask, dx, relu, s));
+    }
     return hip_status(launch_dgrad_generic<bf16_t>(g, dy, w, y_mask, dx, relu, s));
 }
 
@@ -137,21 +166,32 @@ int gc_conv_bwd_weight(const void *x, const void *dy, const void *y_mask, void *
     if (!aligned(x, dtype) || !aligned(dy, dtype) || !aligned(dw, dtype) ||
         (y_mask && !aligned(y_mask, dtype)))
         return GC_ERR_INVALID_ARG;
-    const size_t need = wgrad_ws_bytes(g);
+    WgradIgPlan ig;
+    bool use_ig_path = false;
+    const int splits = wgrad_splits(g, dtype, &ig, &use_ig_path);
+    const size_t need = size_t(splits) * g.OC * g.K * sizeof(float);
     if (need && (!workspace || ws_bytes < need)) return GC_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % 16) return GC_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const int splits = wgrad_generic_splits(g);
     float *part = static_cast<float *>(workspace);
     hipError_t e;
     if (dtype == GC_F32) {
-        e = launch_wgrad_generic<float>(g, x, dy, y_mask, part, splits, relu, s);
+        if (use_ig_path)
+            e = launch_wgrad_ig_f32(g, ig, x, dy, y_mask, part, relu, s);
+        else
+            e = launch_wgrad_generic<float>(g, x, dy, y_mask, part, splits, relu, s);
         if (e == hipSuccess) e = launch_wgrad_reduce<float>(part, dw, splits, g.OC * g.K, s);
     } else {
         e = launch_wgrad_generic<bf16_t>(g, x, dy, y_mask, part, splits, relu, s);
         if (e == hipSuccess) e = launch_wgrad_reduce<bf16_t>(part, dw, splits, g.OC * g.K, s);
     }
     return hip_status(e);
+}
+
+int gc_set_kernel_policy(int policy)
+{
+    if (policy != GC_POLICY_AUTO && policy != GC_POLICY_GENERIC) return -1;
+    return g_policy.exchange(policy);
 }
 
 int64_t gc_fastdiv_selfcheck(uint32_t divisor, uint32_t n_end)

@@ -17,6 +17,21 @@ hipError_t launch_wgrad_generic(const Geom &g, const void *x, const void *dy, co
                                 float *part, int splits, int relu, hipStream_t s);
 int wgrad_generic_splits(const Geom &g);
 
+// Image-group kernels, fp32 storage (fwd_ig_f32.hip, dgrad_ig_f32.hip,
+// wgrad_ig_f32.hip).  plan_* returns false when a shape does not fit them.
+struct FwdIgPlan;
+struct DgradIgPlan;
+struct WgradIgPlan;
+bool plan_fwd_ig_f32(const Geom &g, FwdIgPlan &p);
+hipError_t launch_fwd_ig_f32(const Geom &g, const FwdIgPlan &p, const void *x, const void *w,
+                             void *y, int relu, hipStream_t s);
+bool plan_dgrad_ig_f32(const Geom &g, DgradIgPlan &p);
+hipError_t launch_dgrad_ig_f32(const Geom &g, const DgradIgPlan &p, const void *dy, const void *w,
+                               const void *ym, void *dx, int relu, hipStream_t s);
+bool plan_wgrad_ig_f32(const Geom &g, WgradIgPlan &p);
+hipError_t launch_wgrad_ig_f32(const Geom &g, const WgradIgPlan &p, const void *x, const void *dy,
+                               const void *ym, float *part, int relu, hipStream_t s);
+
 // Fixed-order sum of split partials, then the store in the output type
 // (wgrad_reduce.hip).
 template <typename T>

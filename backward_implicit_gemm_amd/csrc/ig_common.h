@@ -1,0 +1,102 @@
+// ig_common.h -- pieces shared by the image-group kernels: vector global
+// loads at any element alignment, and the per-call tiling plans.
+//
+// An image-group kernel gives each workgroup whole images (or a split of the
+// reduction for wgrad) so that the small spatial extent of the policy-network
+// layers (OH*OW = 12 or 2 outputs per image) never leaves a tile mostly empty,
+// and stages contiguous NCHW slabs instead of gathering element by element.
+#pragma once
+
+#include <algorithm>
+
+#include "gc_common.h"
+
+namespace gc {
+
+// 16-byte load from a 4-byte-aligned global address.  The compiler emits a
+// single global_load_dwordx4 for this copy (the HSA runtime runs gfx9 parts in
+// unaligned-access mode); callers keep all four elements inside the tensor.
+__device__ __forceinline__ float4 ldg4_any(const float *p)
+{
+    float4 v;
+    __builtin_memcpy(&v, p, sizeof(v));
+    return v;
+}
+
+constexpr int IG_NT = 256;   // threads per workgroup (4 waves)
+
+// Direct global -> LDS copy of one 4-byte word per lane (gfx950
+// global_load_lds_dword): lane i writes LDS address lds_wave_base + 4*i,
+// where lds_wave_base must be the same for the whole wave.  No VGPR holds
+// the data, so staging the next chunk costs no registers while the MFMAs of
+// the current one run.  Completion is tracked by vmcnt: wait_vm() before the
+// barrier that publishes the buffer.
+__device__ __forceinline__ void g2lds_dword(const void *src, void *lds_wave_base)
+{
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void *)src,
+        (__attribute__((address_space(3))) void *)lds_wave_base, 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(0): every global load (including LDS-direct ones) of this
+// wave has landed.
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// ---------------------------------------------------------------- forward --
+struct FwdIgPlan {
+    int NW;       // waves per workgroup (they split the output channels)
+    int G;        // images per workgroup
+    int MB;       // 16-row M blocks (G*P <= 16*MB)
+    int NB;       // 16-column N blocks per wave (tile width NW*16*NB)
+    int CC;       // input channels per chunk
+    int KCH;      // CC*KK, multiple of 4 (one fp32 MFMA step)
+    int KS;       // MFMA k steps per chunk (4*KS >= KCH; slots past KCH read zeros)
+    int KCHP;     // LDS row stride of the weight chunk
+    int XCS;      // LDS floats per image in the x chunk (CC*HW rounded up to 4)
+    int nchunks;  // ceil(IC/CC)
+    int XV, WV;   // float4 staging loads per thread (x, w)
+    size_t lds;   // dynamic LDS bytes
+};
+
+// ---------------------------------------------------------------- d_input --
+struct DgradIgPlan {
+    int NW;       // waves per workgroup (they split the dcol columns)
+    int G;        // images per workgroup
+    int MB;       // 16-row M blocks over G*P rows
+    int CC;       // input channels per chunk
+    int NCH;      // CC*KK dcol columns per chunk
+    int NBT;      // 16-column blocks per chunk (ceil(NCH/16))
+    int NBW;      // blocks per wave (ceil(NBT/4))
+    int OCS;      // output channels per weight sub-chunk (multiple of 4)
+    int nsub;     // ceil(OC/OCS)
+    int OCP;      // OC rounded up to OCS multiple
+    int DZP;      // LDS row stride of dz rows
+    int WCP;      // LDS row stride of the weight sub-chunk
+    int DCP;      // LDS row stride of dcol
+    int TH, TW;   // max taps per input row / column: ceil(KH/S), ceil(KW/S)
+    int nchunks;  // ceil(IC/CC)
+    int cgroups;  // channel groups along grid.y
+    int cpg;      // chunks per channel group
+    int WV;       // float4 staging loads per thread for a weight sub-chunk
+    size_t lds;
+};
+
+// ---------------------------------------------------------------- wgrad ----
+struct WgradIgPlan {
+    int NW;       // waves per workgroup: 4 split OC, NW/4 split the k tile
+    int G;        // images per stage
+    int R4;       // stage rows G*P rounded up to 4 (one fp32 MFMA step)
+    int RP;       // LDS row stride of the transposed dz stage
+    int MBW;      // 16-row oc blocks per wave (OC <= 64*MBW)
+    int NBK;      // 16-column k blocks per tile (NBK/(NW/4) per wave)
+    int BNK;      // 16*NBK
+    int nkt;      // k tiles
+    int NCHS;     // max channels a k tile spans
+    int XSS;      // LDS floats per image of the x stage (NCHS*HW rounded up to 4)
+    int GS;       // images per split
+    int splits;
+    int DV, XV;   // staging loads per thread (dz scalars, x float4)
+    size_t lds;
+};
+
+}  // namespace gc

@@ -113,6 +113,16 @@ const char *gc_status_string(int status);
  * n % divisor.  Requires 1 <= divisor and n_end <= 2^31; returns -1 otherwise. */
 int64_t gc_fastdiv_selfcheck(uint32_t divisor, uint32_t n_end);
 
+/* Kernel selection policy, process-wide.  GC_POLICY_AUTO (the default) runs
+ * the image-group kernels wherever a shape fits them and the shape-generic
+ * kernels elsewhere; GC_POLICY_GENERIC runs the shape-generic kernels for
+ * every shape (used to test both families on the same problems).  Returns
+ * the previous policy, or -1 for an unknown value (nothing changes).  Calls
+ * already enqueued are not affected; set it only while no other thread is
+ * issuing calls. */
+enum { GC_POLICY_AUTO = 0, GC_POLICY_GENERIC = 1 };
+int gc_set_kernel_policy(int policy);
+
 /* Library version, as major*10000 + minor*100 + patch. */
 int gc_version(void);
 

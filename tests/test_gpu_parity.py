@@ -28,14 +28,26 @@ def setup_module():
 # Full-size workloads (B=1024), every output element against the oracle
 # ---------------------------------------------------------------------------
 
+@pytest.fixture
+def kernel_policy(request):
+    prev = gb.gc_set_kernel_policy(request.param)
+    yield request.param
+    gb.gc_set_kernel_policy(prev)
+
+
+POLICIES = [gb.GC_POLICY_AUTO, gb.GC_POLICY_GENERIC]
+
+
+@pytest.mark.parametrize("kernel_policy", POLICIES, ids=["auto", "generic"], indirect=True)
 @pytest.mark.parametrize("idx", [0, 1, 2, 3], ids=[w.name for w in inputs.WORKLOADS[:4]])
-def test_workload_full_parity(idx):
+def test_workload_full_parity(idx, kernel_policy):
     wl = inputs.WORKLOADS[idx]
     L = wl.layers[0]
     layer = Layer.of(L)
     x, w, dy = inputs.layer_inputs(L, wl.seeds, wl.dtype)
     errs, (y, dx, dw), (y_ref, _, _) = check_layer(layer, wl.dtype, x=x, w=w, dy=dy)
-    print(f"{wl.name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    print(f"{wl.name} policy={kernel_policy}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()),
+          flush=True)
     if layer.relu:
         flips = int(np.sum((f64(y) > 0) != (y_ref > 0)))
         print(f"{wl.name}: ReLU mask disagreements with the oracle's y: {flips}", flush=True)
@@ -123,13 +135,17 @@ ODD = [
     (2, 3, 32, 32, 8, 5, 5, 2),
     (2, 200, 3, 3, 7, 3, 3, 1),
     (33, 1, 11, 15, 3, 5, 5, 3),
+    (9, 59, 11, 15, 128, 5, 5, 3),      # last image group ragged (9 = 2*4 + 1)
+    (37, 128, 3, 4, 96, 3, 3, 1),       # OC not a multiple of 64
+    (6, 13, 9, 7, 20, 3, 2, 2),         # P = 12 from a rectangular kernel
 ]
 
 
+@pytest.mark.parametrize("kernel_policy", POLICIES, ids=["auto", "generic"], indirect=True)
 @pytest.mark.parametrize("shape", ODD, ids=["x".join(map(str, s)) for s in ODD])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("relu", [0, 1])
-def test_odd_shapes(shape, dtype, relu):
+def test_odd_shapes(shape, dtype, relu, kernel_policy):
     layer = Layer(*shape, relu)
     errs, _, _ = check_layer(layer, dtype, seeds=(sum(shape), 7, 8 + relu))
     print(f"{shape} {dtype} relu={relu}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()),
@@ -141,9 +157,10 @@ def test_odd_shapes(shape, dtype, relu):
 # result cannot depend on summation order and must match exactly.
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("kernel_policy", POLICIES, ids=["auto", "generic"], indirect=True)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", [(64, 59, 11, 15, 128, 5, 5, 3), (64, 128, 3, 4, 128, 3, 3, 1)])
-def test_integer_inputs_exact(shape, dtype):
+def test_integer_inputs_exact(shape, dtype, kernel_policy):
     layer = Layer(*shape, relu=1)
     x = inputs.integers(layer.x_shape, 21, dtype=dtype)
     w = inputs.integers(layer.w_shape, 22, dtype=dtype)
