@@ -1,4 +1,6 @@
-// dgrad_ig_f32.hip -- d_input, fp32 storage, image-group tiling, gather form.
+// dgrad_ig_f32.hip -- d_input on fp32 MFMA, image-group tiling, gather form.
+// Storage may be fp32 or bf16: bf16 operands are widened exactly to fp32 as
+// they are staged into LDS, and the result is rounded to bf16 once, on store.
 //
 // For a group of G whole images the workgroup first forms, chunk by chunk of
 // CC input channels, the column gradient
@@ -23,10 +25,11 @@
 namespace gc {
 namespace {
 
+template <typename T>
 struct DgradIgArgs {
     Geom g;
-    const float *dy, *w, *ym;
-    float *dx;
+    const T *dy, *w, *ym;
+    T *dx;
     int relu;
     DgradIgPlan p;
     FastDiv fd_ocp;    // OC*P: dz elements per image
@@ -34,8 +37,8 @@ struct DgradIgArgs {
     FastDiv fd_nq;     // ceil(NCH/4): float4 slots per weight row
 };
 
-template <int NW, int MB, int NBW, int KSD, int TAPS, int WV>
-__global__ void __launch_bounds__(64 * NW) dgrad_ig_f32(DgradIgArgs a)
+template <typename T, int NW, int MB, int NBW, int KSD, int TAPS, int WV>
+__global__ void __launch_bounds__(64 * NW) dgrad_ig_f32(DgradIgArgs<T> a)
 {
     extern __shared__ __attribute__((aligned(16))) float lds[];
     const Geom &g = a.g;
@@ -106,8 +109,8 @@ __global__ void __launch_bounds__(64 * NW) dgrad_ig_f32(DgradIgArgs a)
             uint32_t img, rem, oc, pp;
             fdivmod(e, a.fd_ocp, img, rem);
             fdivmod(rem, g.fd_P, oc, pp);
-            float v = a.dy[base + e];
-            if (a.relu && !(a.ym[base + e] > 0.f)) v = 0.f;
+            float v = to_f32(a.dy[base + e]);
+            if (a.relu && !(to_f32(a.ym[base + e]) > 0.f)) v = 0.f;
             dz[(int(img) * g.P + int(pp)) * p.DZP + int(oc)] = v;
         }
     }
@@ -130,19 +133,19 @@ __global__ void __launch_bounds__(64 * NW) dgrad_ig_f32(DgradIgArgs a)
         const int ch = ch_begin + st / p.nsub, sub = st % p.nsub;
         const int c0 = ch * p.CC, oc0 = sub * OCS;
         const int valid_k = min(p.CC, g.IC - c0) * g.KK;
-        const float *base = a.w + size_t(oc0) * g.K + size_t(c0) * g.KK;
+        const T *base = a.w + size_t(oc0) * g.K + size_t(c0) * g.KK;
 #pragma unroll
         for (int j = 0; j < WV; ++j) {
             float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
             const int kl = s_kl[j];
             if (s_row[j] >= 0 && oc0 + s_row[j] < g.OC) {
-                const float *src = base + s_goff[j];
+                const T *src = base + s_goff[j];
                 if (kl + 3 < valid_k) {
-                    v = ldg4_any(src);
+                    v = ld4_f32(src);
                 } else {
-                    if (kl + 0 < valid_k) v.x = src[0];
-                    if (kl + 1 < valid_k) v.y = src[1];
-                    if (kl + 2 < valid_k) v.z = src[2];
+                    if (kl + 0 < valid_k) v.x = to_f32(src[0]);
+                    if (kl + 1 < valid_k) v.y = to_f32(src[1]);
+                    if (kl + 2 < valid_k) v.z = to_f32(src[2]);
                 }
             }
             rw[j] = v;
@@ -220,7 +223,8 @@ __global__ void __launch_bounds__(64 * NW) dgrad_ig_f32(DgradIgArgs a)
 #pragma unroll
                     for (int j = 0; j < TAPS; ++j)
                         if (j < ntap) sum += dc[toff[j]];
-                    a.dx[(size_t(b0) + img) * g.IC * g.HW + size_t(c0 + int(icl)) * g.HW + q] = sum;
+                    a.dx[(size_t(b0) + img) * g.IC * g.HW + size_t(c0 + int(icl)) * g.HW + q] =
+                        from_f32<T>(sum);
                 }
             }
         }
@@ -228,14 +232,16 @@ __global__ void __launch_bounds__(64 * NW) dgrad_ig_f32(DgradIgArgs a)
     }
 }
 
+template <typename T>
 struct DgradVariant {
     int NW, MB, NBW, KSD, TAPS, WV;
-    void (*fn)(DgradIgArgs);
+    void (*fn)(DgradIgArgs<T>);
 };
 
 #define DG_V(NW, MB, NBW, KSD, TAPS, WV) \
-    {NW, MB, NBW, KSD, TAPS, WV, dgrad_ig_f32<NW, MB, NBW, KSD, TAPS, WV>}
-const DgradVariant kDgradVariants[] = {
+    {NW, MB, NBW, KSD, TAPS, WV, dgrad_ig_f32<T, NW, MB, NBW, KSD, TAPS, WV>}
+template <typename T>
+const DgradVariant<T> kDgradVariants[] = {
     DG_V(8, 3, 1, 16, 4, 4),    // layer 1: 4 images x 12 rows, 5 channels x 25 taps, 2x2 taps/pixel
     DG_V(4, 4, 1, 16, 9, 4),    // layer 2: 32 images x 2 rows, 7 channels x 9 taps, 3x3 taps/pixel
     DG_V(4, 1, 1, 16, 9, 4), DG_V(4, 2, 1, 16, 9, 4), DG_V(4, 3, 1, 16, 9, 4),
@@ -251,10 +257,11 @@ const DgradVariant kDgradVariants[] = {
 
 int rup(int v, int m) { return (v + m - 1) / m * m; }
 
-const DgradVariant *pick_dgrad(int NW, int MB, int NBW, int taps, int wv)
+template <typename T>
+const DgradVariant<T> *pick_dgrad(int NW, int MB, int NBW, int taps, int wv)
 {
-    const DgradVariant *best = nullptr;
-    for (const auto &v : kDgradVariants)
+    const DgradVariant<T> *best = nullptr;
+    for (const auto &v : kDgradVariants<T>)
         if (v.NW == NW && v.MB == MB && v.NBW == NBW && taps <= v.TAPS && wv <= v.WV &&
             (!best || v.TAPS < best->TAPS || (v.TAPS == best->TAPS && v.WV < best->WV)))
             best = &v;
@@ -304,7 +311,7 @@ bool plan_dgrad_ig_f32(const Geom &g, DgradIgPlan &p)
             q.lds = sizeof(float) * (size_t(16 * MB) * q.DZP + 2 * size_t(OCS) * q.WCP +
                                      size_t(16 * MB) * q.DCP);
             if (q.lds > budget) continue;
-            if (!pick_dgrad(NW, MB, q.NBW, TH * TW, q.WV)) continue;
+            if (!pick_dgrad<float>(NW, MB, q.NBW, TH * TW, q.WV)) continue;
             // MFMA slots used: dcol columns over the columns the waves compute
             const double eff = double(q.NCH) / (q.NBW * NW * 16);
             if (eff > best + 1e-9) {
@@ -319,19 +326,24 @@ bool plan_dgrad_ig_f32(const Geom &g, DgradIgPlan &p)
     return found;
 }
 
-hipError_t launch_dgrad_ig_f32(const Geom &g, const DgradIgPlan &p, const void *dy, const void *w,
-                               const void *ym, void *dx, int relu, hipStream_t s)
+template <typename T>
+hipError_t launch_dgrad_ig(const Geom &g, const DgradIgPlan &p, const void *dy, const void *w,
+                           const void *ym, void *dx, int relu, hipStream_t s)
 {
-    const DgradVariant *v = pick_dgrad(p.NW, p.MB, p.NBW, p.TH * p.TW, p.WV);
+    const DgradVariant<T> *v = pick_dgrad<T>(p.NW, p.MB, p.NBW, p.TH * p.TW, p.WV);
     if (!v || 4 * v->KSD != p.OCS || g.HW > 64 * p.NW) return hipErrorInvalidValue;
-    DgradIgArgs a{g, (const float *)dy, (const float *)w, (const float *)ym, (float *)dx, relu, p,
-                  make_fastdiv(g.OC * g.P), make_fastdiv(p.CC), make_fastdiv((p.NCH + 3) / 4)};
+    DgradIgArgs<T> a{g, (const T *)dy, (const T *)w, (const T *)ym, (T *)dx, relu, p,
+                     make_fastdiv(g.OC * g.P), make_fastdiv(p.CC), make_fastdiv((p.NCH + 3) / 4)};
     dim3 grid((g.B + p.G - 1) / p.G, p.cgroups);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(v->fn),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(p.lds));
+    hipError_t e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(v->fn, grid, dim3(64 * p.NW), p.lds, s, a);
     return hipGetLastError();
 }
+
+template hipError_t launch_dgrad_ig<float>(const Geom &, const DgradIgPlan &, const void *,
+                                           const void *, const void *, void *, int, hipStream_t);
+template hipError_t launch_dgrad_ig<bf16_t>(const Geom &, const DgradIgPlan &, const void *,
+                                            const void *, const void *, void *, int, hipStream_t);
 
 }  // namespace gc

@@ -309,8 +309,7 @@ hipError_t launch_fwd_ig_f32(const Geom &g, const FwdIgPlan &p, const void *x, c
     FwdIgArgs a{g, (const float *)x, (const float *)w, (float *)y, relu, p,
                 make_fastdiv(p.XCS / 4), make_fastdiv(p.KCH / 4)};
     dim3 grid((g.B + p.G - 1) / p.G, (g.OC + 16 * p.NW - 1) / (16 * p.NW));
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(v->fn),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(p.lds));
+    hipError_t e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(v->fn, grid, dim3(64 * p.NW), p.lds, s, a);
     return hipGetLastError();

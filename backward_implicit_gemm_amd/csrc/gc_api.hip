@@ -5,6 +5,7 @@
 #include <limits.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/gc.h"
 #include "gc_kernels.h"
@@ -50,12 +51,65 @@ std::atomic<int> g_policy{GC_POLICY_AUTO};
 
 bool use_ig() { return g_policy.load(std::memory_order_relaxed) == GC_POLICY_AUTO; }
 
+// Plans depend only on the geometry, and some take a search (the bf16
+// forward's LDS pitch) that costs far more host time than a launch, so each
+// planner's answers are kept per geometry.  Thread-safe; a full table
+// overwrites its entries round-robin.
+template <typename P>
+bool cached_plan(const Geom &g, bool (*planner)(const Geom &, P &), P &out)
+{
+    struct Entry {
+        int key[8];
+        bool ok;
+        P plan;
+    };
+    constexpr int kSlots = 64;
+    static std::mutex m;
+    static Entry table[kSlots];
+    static int used = 0, next = 0;
+    const int key[8] = {g.B, g.IC, g.H, g.W, g.OC, g.KH, g.KW, g.S};
+    {
+        std::lock_guard<std::mutex> lk(m);
+        for (int i = 0; i < used; ++i)
+            if (std::equal(key, key + 8, table[i].key)) {
+                if (table[i].ok) out = table[i].plan;
+                return table[i].ok;
+            }
+    }
+    P p{};
+    const bool ok = planner(g, p);
+    std::lock_guard<std::mutex> lk(m);
+    Entry &e = table[used < kSlots ? used++ : (next++ % kSlots)];
+    std::copy(key, key + 8, e.key);
+    e.ok = ok;
+    e.plan = p;
+    if (ok) out = p;
+    return ok;
+}
+
+bool fwd_f32_plan(const Geom &g, FwdIgPlan &p)
+{
+    return use_ig() && cached_plan(g, plan_fwd_ig_f32, p);
+}
+bool fwd_bf16_plan(const Geom &g, FwdBfPlan &p)
+{
+    return use_ig() && cached_plan(g, plan_fwd_ig_bf16, p);
+}
+bool dgrad_plan(const Geom &g, DgradIgPlan &p)
+{
+    return use_ig() && cached_plan(g, plan_dgrad_ig_f32, p);
+}
+bool wgrad_plan(const Geom &g, WgradIgPlan &p)
+{
+    return use_ig() && cached_plan(g, plan_wgrad_ig_f32, p);
+}
+
 // Number of fp32 partial tiles wgrad writes for this problem, and the plan
 // of the image-group kernel when it runs.
 int wgrad_splits(const Geom &g, int dtype, WgradIgPlan *ig, bool *use)
 {
     WgradIgPlan p;
-    if (dtype == GC_F32 && use_ig() && plan_wgrad_ig_f32(g, p)) {
+    if (wgrad_plan(g, p)) {
         if (ig) *ig = p;
         if (use) *use = true;
         return p.splits;
@@ -102,7 +156,11 @@ size_t gc_conv_workspace_bytes(int op, const gc_conv_desc *d, int dtype)
     Geom g;
     if (check_desc(d, &g) != GC_OK || !valid_dtype(dtype)) return 0;
     switch (op) {
-    case GC_OP_FWD: return 0;
+    case GC_OP_FWD: {
+        FwdBfPlan p;
+        if (dtype == GC_BF16 && fwd_bf16_plan(g, p)) return p.ws_bytes;
+        return 0;
+    }
     case GC_OP_BWD_DATA: return 0;
     case GC_OP_BWD_WEIGHT: return wgrad_ws_bytes(g, dtype);
     default: return 0;
@@ -112,7 +170,6 @@ size_t gc_conv_workspace_bytes(int op, const gc_conv_desc *d, int dtype)
 int gc_conv_fwd(const void *x, const void *w, void *y, void *workspace, size_t ws_bytes,
                 const gc_conv_desc *d, int relu, int dtype, void *stream)
 {
-    (void)workspace; (void)ws_bytes;
     Geom g;
     int st = check_desc(d, &g);
     if (st != GC_OK) return st;
@@ -122,9 +179,15 @@ int gc_conv_fwd(const void *x, const void *w, void *y, void *workspace, size_t w
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == GC_F32) {
         FwdIgPlan p;
-        if (use_ig() && plan_fwd_ig_f32(g, p))
+        if (fwd_f32_plan(g, p))
             return hip_status(launch_fwd_ig_f32(g, p, x, w, y, relu, s));
         return hip_status(launch_fwd_generic<float>(g, x, w, y, relu, s));
+    }
+    FwdBfPlan p;
+    if (fwd_bf16_plan(g, p)) {
+        if (!workspace || ws_bytes < p.ws_bytes) return GC_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(workspace) % 16) return GC_ERR_WORKSPACE;
+        return hip_status(launch_fwd_ig_bf16(g, p, x, w, y, workspace, relu, s));
     }
     return hip_status(launch_fwd_generic<bf16_t>(g, x, w, y, relu, s));
 }
@@ -144,13 +207,13 @@ int gc_conv_bwd_data(const void *dy, const void *w, const void *y_mask, void *dx
         (y_mask && !aligned(y_mask, dtype)))
         return GC_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (dtype == GC_F32) {
-        DgradIgPlan p;
-        if (use_ig() && plan_dgrad_ig_f32(g, p))
-            return hip_status(launch_dgrad_ig_f32(g, p, dy, w, y_mask, dx, relu, s));
-        return hip_status(launch_dgrad_generic<float>(g, dy, w, y_mask, dx, relu, s));
-    }
-    return hip_status(launch_dgrad_generic<bf16_t>(g, dy, w, y_mask, dx, relu, s));
+    DgradIgPlan p;
+    const bool ig = dgrad_plan(g, p);
+    if (dtype == GC_F32)
+        return hip_status(ig ? launch_dgrad_ig<float>(g, p, dy, w, y_mask, dx, relu, s)
+                             : launch_dgrad_generic<float>(g, dy, w, y_mask, dx, relu, s));
+    return hip_status(ig ? launch_dgrad_ig<bf16_t>(g, p, dy, w, y_mask, dx, relu, s)
+                         : launch_dgrad_generic<bf16_t>(g, dy, w, y_mask, dx, relu, s));
 }
 
 int gc_conv_bwd_weight(const void *x, const void *dy, const void *y_mask, void *dw,
@@ -177,12 +240,15 @@ int gc_conv_bwd_weight(const void *x, const void *dy, const void *y_mask, void *
     hipError_t e;
     if (dtype == GC_F32) {
         if (use_ig_path)
-            e = launch_wgrad_ig_f32(g, ig, x, dy, y_mask, part, relu, s);
+            e = launch_wgrad_ig<float>(g, ig, x, dy, y_mask, part, relu, s);
         else
             e = launch_wgrad_generic<float>(g, x, dy, y_mask, part, splits, relu, s);
         if (e == hipSuccess) e = launch_wgrad_reduce<float>(part, dw, splits, g.OC * g.K, s);
     } else {
-        e = launch_wgrad_generic<bf16_t>(g, x, dy, y_mask, part, splits, relu, s);
+        if (use_ig_path)
+            e = launch_wgrad_ig<bf16_t>(g, ig, x, dy, y_mask, part, relu, s);
+        else
+            e = launch_wgrad_generic<bf16_t>(g, x, dy, y_mask, part, splits, relu, s);
         if (e == hipSuccess) e = launch_wgrad_reduce<bf16_t>(part, dw, splits, g.OC * g.K, s);
     }
     return hip_status(e);

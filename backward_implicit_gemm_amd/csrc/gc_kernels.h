@@ -25,12 +25,22 @@ struct WgradIgPlan;
 bool plan_fwd_ig_f32(const Geom &g, FwdIgPlan &p);
 hipError_t launch_fwd_ig_f32(const Geom &g, const FwdIgPlan &p, const void *x, const void *w,
                              void *y, int relu, hipStream_t s);
+// d_input and wgrad run on fp32 MFMA for both storage types (T = float or
+// bf16_t; bf16 is widened exactly while staging).
 bool plan_dgrad_ig_f32(const Geom &g, DgradIgPlan &p);
-hipError_t launch_dgrad_ig_f32(const Geom &g, const DgradIgPlan &p, const void *dy, const void *w,
-                               const void *ym, void *dx, int relu, hipStream_t s);
+template <typename T>
+hipError_t launch_dgrad_ig(const Geom &g, const DgradIgPlan &p, const void *dy, const void *w,
+                           const void *ym, void *dx, int relu, hipStream_t s);
 bool plan_wgrad_ig_f32(const Geom &g, WgradIgPlan &p);
-hipError_t launch_wgrad_ig_f32(const Geom &g, const WgradIgPlan &p, const void *x, const void *dy,
-                               const void *ym, float *part, int relu, hipStream_t s);
+template <typename T>
+hipError_t launch_wgrad_ig(const Geom &g, const WgradIgPlan &p, const void *x, const void *dy,
+                           const void *ym, float *part, int relu, hipStream_t s);
+
+// Image-group kernels, bf16 storage.
+struct FwdBfPlan;
+bool plan_fwd_ig_bf16(const Geom &g, FwdBfPlan &p);
+hipError_t launch_fwd_ig_bf16(const Geom &g, const FwdBfPlan &p, const void *x, const void *w,
+                              void *y, void *ws, int relu, hipStream_t s);
 
 // Fixed-order sum of split partials, then the store in the output type
 // (wgrad_reduce.hip).

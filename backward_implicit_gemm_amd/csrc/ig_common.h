@@ -8,10 +8,48 @@
 #pragma once
 
 #include <algorithm>
+#include <mutex>
+#include <utility>
+#include <vector>
 
 #include "gc_common.h"
 
 namespace gc {
+
+// Raises a kernel's dynamic-LDS limit to the full 160 KiB once per (device,
+// kernel); every later launch of it, with any LDS size up to that, needs no
+// further attribute call.
+inline hipError_t allow_max_lds(const void *fn)
+{
+    static std::mutex m;
+    static std::vector<std::pair<int, const void *>> done;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(m);
+    for (const auto &d : done)
+        if (d.first == dev && d.second == fn) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e == hipSuccess) done.emplace_back(dev, fn);
+    return e;
+}
+
+// Four consecutive elements as fp32 from an element-aligned global address:
+// one 16-byte load for fp32 storage, one 8-byte load widened exactly for
+// bf16 storage.
+__device__ __forceinline__ float4 ld4_f32(const float *p)
+{
+    float4 v;
+    __builtin_memcpy(&v, p, sizeof(v));
+    return v;
+}
+__device__ __forceinline__ float4 ld4_f32(const bf16_t *p)
+{
+    uint2 u;
+    __builtin_memcpy(&u, p, sizeof(u));
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+}
 
 // 16-byte load from a 4-byte-aligned global address.  The compiler emits a
 // single global_load_dwordx4 for this copy (the HSA runtime runs gfx9 parts in
@@ -56,6 +94,20 @@ struct FwdIgPlan {
     int nchunks;  // ceil(IC/CC)
     int XV, WV;   // float4 staging loads per thread (x, w)
     size_t lds;   // dynamic LDS bytes
+};
+
+// -------------------------------------------------------- forward, bf16 ----
+struct FwdBfPlan {
+    int NW;       // waves per workgroup, 16 output channels each
+    int G;        // images per workgroup
+    int MB;       // 16-row M blocks
+    int TS;       // tap steps: ceil(KH*KW/4)
+    int WP;       // LDS pixel slots per image row (>= W, padded against bank conflicts)
+    int IS;       // LDS pixel slots per image (>= H*WP)
+    int nblk;     // 8-pixel blocks per image
+    int NCG;      // channel groups of 8
+    size_t lds;
+    size_t ws_bytes;   // packed weights
 };
 
 // ---------------------------------------------------------------- d_input --

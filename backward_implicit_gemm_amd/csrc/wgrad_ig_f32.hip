@@ -1,4 +1,6 @@
-// wgrad_ig_f32.hip -- weight gradient, fp32 storage, split-K over images.
+// wgrad_ig_f32.hip -- weight gradient on fp32 MFMA, split-K over images.
+// Storage may be fp32 or bf16 (bf16 operands are widened exactly to fp32 as
+// they are staged); the partials and their fixed-order sum are fp32.
 //
 // dW[oc][k] = sum_r dz[r][oc] * A[r][k] with r = (b,oh,ow), k = (ic,kh,kw):
 // a GEMM with M = OC, N = IC*KH*KW and a reduction of B*OH*OW that is far
@@ -21,17 +23,18 @@
 namespace gc {
 namespace {
 
+template <typename T>
 struct WgradIgArgs {
     Geom g;
-    const float *x, *dy, *ym;
+    const T *x, *dy, *ym;
     float *part;
     int relu;
     WgradIgPlan p;
     FastDiv fd_ocp;    // OC*P: dz elements per image
 };
 
-template <int NW, int MBW, int NBKW, int RS, int DV, int XV>
-__global__ void __launch_bounds__(64 * NW) wgrad_ig_f32(WgradIgArgs a)
+template <typename T, int NW, int MBW, int NBKW, int RS, int DV, int XV>
+__global__ void __launch_bounds__(64 * NW) wgrad_ig_f32(WgradIgArgs<T> a)
 {
     extern __shared__ __attribute__((aligned(16))) float lds[];
     const Geom &g = a.g;
@@ -114,24 +117,24 @@ __global__ void __launch_bounds__(64 * NW) wgrad_ig_f32(WgradIgArgs a)
             const int e = tid + j * NT;
             float v = 0.f;
             if (e < nd) {
-                v = a.dy[dbase + e];
-                if (a.relu && !(a.ym[dbase + e] > 0.f)) v = 0.f;
+                v = to_f32(a.dy[dbase + e]);
+                if (a.relu && !(to_f32(a.ym[dbase + e]) > 0.f)) v = 0.f;
             }
             rd[j] = v;
         }
-        const float *xbase = a.x + size_t(b) * g.IC * g.HW;
+        const T *xbase = a.x + size_t(b) * g.IC * g.HW;
 #pragma unroll
         for (int j = 0; j < XV; ++j) {
             float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
             const int e = s_e[j];
             if (s_img[j] >= 0 && s_img[j] < gimg) {
-                const float *src = xbase + s_goff[j];
+                const T *src = xbase + s_goff[j];
                 if (e + 3 < valid_x) {
-                    v = ldg4_any(src);
+                    v = ld4_f32(src);
                 } else {
-                    if (e + 0 < valid_x) v.x = src[0];
-                    if (e + 1 < valid_x) v.y = src[1];
-                    if (e + 2 < valid_x) v.z = src[2];
+                    if (e + 0 < valid_x) v.x = to_f32(src[0]);
+                    if (e + 1 < valid_x) v.y = to_f32(src[1]);
+                    if (e + 2 < valid_x) v.z = to_f32(src[2]);
                 }
             }
             rx[j] = v;
@@ -207,14 +210,16 @@ __global__ void __launch_bounds__(64 * NW) wgrad_ig_f32(WgradIgArgs a)
         }
 }
 
+template <typename T>
 struct WgradVariant {
     int NW, MBW, NBKW, RS, DV, XV;
-    void (*fn)(WgradIgArgs);
+    void (*fn)(WgradIgArgs<T>);
 };
 
 #define WG_V(NW, MBW, NBKW, RS, DV, XV) \
-    {NW, MBW, NBKW, RS, DV, XV, wgrad_ig_f32<NW, MBW, NBKW, RS, DV, XV>}
-const WgradVariant kWgradVariants[] = {
+    {NW, MBW, NBKW, RS, DV, XV, wgrad_ig_f32<T, NW, MBW, NBKW, RS, DV, XV>}
+template <typename T>
+const WgradVariant<T> kWgradVariants[] = {
     WG_V(8, 2, 6, 12, 12, 4),   // layers 1 and 2: 128 oc x 192 k, stages of 48 rows
     WG_V(8, 1, 6, 12, 12, 4), WG_V(8, 2, 2, 12, 12, 4), WG_V(8, 1, 2, 12, 12, 4),
 };
@@ -222,9 +227,10 @@ const WgradVariant kWgradVariants[] = {
 
 int rup4(int v) { return (v + 3) / 4 * 4; }
 
-const WgradVariant *pick_wgrad(int NW, int MBW, int NBK, int rs, int dv, int xv)
+template <typename T>
+const WgradVariant<T> *pick_wgrad(int NW, int MBW, int NBK, int rs, int dv, int xv)
 {
-    for (const auto &v : kWgradVariants)
+    for (const auto &v : kWgradVariants<T>)
         if (v.NW == NW && v.MBW == MBW && v.NBKW * (NW / 4) == NBK && v.RS == rs && dv <= v.DV &&
             xv <= v.XV)
             return &v;
@@ -262,7 +268,7 @@ bool plan_wgrad_ig_f32(const Geom &g, WgradIgPlan &p)
             q.splits = (g.B + q.GS - 1) / q.GS;
             q.lds = sizeof(float) * (2 * size_t(MBW * 64) * q.RP + 2 * size_t(q.G) * q.XSS);
             if (q.lds > budget) continue;
-            if (!pick_wgrad(q.NW, MBW, NBK, RS, q.DV, q.XV)) continue;
+            if (!pick_wgrad<float>(q.NW, MBW, NBK, RS, q.DV, q.XV)) continue;
             p = q;
             return true;
         }
@@ -270,19 +276,24 @@ bool plan_wgrad_ig_f32(const Geom &g, WgradIgPlan &p)
     return false;
 }
 
-hipError_t launch_wgrad_ig_f32(const Geom &g, const WgradIgPlan &p, const void *x, const void *dy,
-                               const void *ym, float *part, int relu, hipStream_t s)
+template <typename T>
+hipError_t launch_wgrad_ig(const Geom &g, const WgradIgPlan &p, const void *x, const void *dy,
+                           const void *ym, float *part, int relu, hipStream_t s)
 {
-    const WgradVariant *v = pick_wgrad(p.NW, p.MBW, p.NBK, p.R4 / 4, p.DV, p.XV);
+    const WgradVariant<T> *v = pick_wgrad<T>(p.NW, p.MBW, p.NBK, p.R4 / 4, p.DV, p.XV);
     if (!v || 4 * v->RS != p.R4 || p.G * g.P > p.R4) return hipErrorInvalidValue;
-    WgradIgArgs a{g, (const float *)x, (const float *)dy, (const float *)ym, part, relu, p,
-                  make_fastdiv(g.OC * g.P)};
+    WgradIgArgs<T> a{g, (const T *)x, (const T *)dy, (const T *)ym, part, relu, p,
+                     make_fastdiv(g.OC * g.P)};
     dim3 grid(p.nkt, p.splits);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(v->fn),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(p.lds));
+    hipError_t e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(v->fn, grid, dim3(64 * p.NW), p.lds, s, a);
     return hipGetLastError();
 }
+
+template hipError_t launch_wgrad_ig<float>(const Geom &, const WgradIgPlan &, const void *,
+                                           const void *, const void *, float *, int, hipStream_t);
+template hipError_t launch_wgrad_ig<bf16_t>(const Geom &, const WgradIgPlan &, const void *,
+                                            const void *, const void *, float *, int, hipStream_t);
 
 }  // namespace gc

@@ -11,10 +11,12 @@ forward and backward separately over 50 warmup and 200 timed iterations.
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
 
 Prints one JSON line per workload: throughput in TFLOP/s of algorithmic work
-(2*B*OC*OH*OW*IC*KH*KW per pass, three passes per step), per-pass times from
-HIP events recorded on the launch stream around every call of the timed
-region, a roofline entry for the dominant kernel, and the CPU oracle timed
-on this host on a bounded sample (default workload only).
+(2*B*OC*OH*OW*IC*KH*KW per pass, three passes per step) over K steps, each
+step replayed as one HIP graph between HIP events on the launch stream; the
+same K steps issued eagerly (host work included); per-call GPU times from
+graphs of back-to-back copies of each call; a roofline entry for the
+dominant call; and the CPU oracle timed on this host on a bounded sample
+(default workload only).
 """
 import argparse
 import hashlib
@@ -123,7 +125,6 @@ def run_gpu(wl, steps, warmup):
     dxs = [torch.empty(L.x_shape, dtype=td, device=dev) if i == 0 else dys[i - 1]
            for i, L in enumerate(layers)]
     dws = [torch.empty(L.w_shape, dtype=td, device=dev) for L in layers]
-    stream = torch.cuda.current_stream()
 
     # calls of one step, in order: forward through the layers, then backward
     calls = []
@@ -134,28 +135,65 @@ def run_gpu(wl, steps, warmup):
         calls.append((f"dgrad{i + 1}", lambda c=c, i=i: c.bwd_data(dys[i], ws[i], ys[i], dxs[i])))
         calls.append((f"wgrad{i + 1}", lambda c=c, i=i: c.bwd_weight(xs[i], dys[i], ys[i], dws[i])))
 
-    for _ in range(warmup):
+    def step():
         for _, f in calls:
             f()
+
+    # Eager warmup: plans, LDS attributes and the library's lazy set-up are
+    # settled before capture, so the graphs hold kernel launches only.
+    for _ in range(max(warmup, 1)):
+        step()
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
+    # One step as a HIP graph: replaying it issues the step's kernels without
+    # the per-call host work (argument checks, ctypes marshalling), which at
+    # these sizes is comparable to the kernels themselves.
+    step_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(step_graph):
+        step()
+    for _ in range(warmup):
+        step_graph.replay()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     start.record(stream)
-    for s in range(steps):
-        ev[s][0].record(stream)
-        for j, (_, f) in enumerate(calls):
-            f()
-            ev[s][j + 1].record(stream)
+    for _ in range(steps):
+        step_graph.replay()
     end.record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
+    ms_step = start.elapsed_time(end) / steps
+
+    # The same steps issued eagerly through the C ABI, host work included.
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_eager = start.elapsed_time(end) / steps
+
+    # Per call: a graph of REPS back-to-back copies of the call, replayed and
+    # timed with HIP events on the launch stream, so each figure is the
+    # call's GPU time (its kernels plus the gaps between graph nodes).
+    reps = 10
+    replays = max(2, min(20, steps // reps))
     per_call = {}
-    for j, (name, _) in enumerate(calls):
-        per_call[name] = statistics.mean(ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(steps)) * 1e3
-    return total_ms / steps, per_call
+    for name, f in calls:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                f()
+        g.replay()
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(replays):
+            g.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        per_call[name] = start.elapsed_time(end) / (replays * reps) * 1e3
+        del g
+    return ms_step, ms_eager, per_call
 
 
 def cpu_baseline(wl, budget_s):
@@ -195,7 +233,15 @@ def cpu_baseline(wl, budget_s):
     }
 
 
-def report(wl, ms_step, per_call, steps, warmup, cpu):
+# Kernels behind each call, as named in rocprofv3 summaries.
+CALL_KERNELS = {
+    "fwd": {"f32": ["fwd_ig_f32"], "bf16": ["pack_w_fwd_bf16", "fwd_ig_bf16"]},
+    "dgrad": {"f32": ["dgrad_ig_f32"], "bf16": ["dgrad_ig_f32<bf16>"]},
+    "wgrad": {"f32": ["wgrad_ig_f32", "wgrad_reduce"], "bf16": ["wgrad_ig_f32<bf16>", "wgrad_reduce"]},
+}
+
+
+def report(wl, ms_step, ms_eager, per_call, steps, warmup, cpu):
     L0 = wl.layers[0]
     esize = 4 if wl.dtype == "f32" else 2
     flops_step = sum(3 * layer_flops(L) for L in wl.layers)
@@ -215,7 +261,8 @@ def report(wl, ms_step, per_call, steps, warmup, cpu):
         bound, peak, unit, achieved = "hbm", PEAK["hbm_gbs"], "GB/s", by / (us * 1e-6) / 1e9
     roof = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": measured_traffic(wl.name, dom),
-            "kernel_call": dom, "us_per_launch": round(us, 3)}
+            "kernel_call": dom, "kernels": CALL_KERNELS[dom.rstrip("0123456789")][wl.dtype],
+            "us_per_launch": round(us, 3)}
     value = flops_step / (ms_step * 1e-3) / 1e12
     fwd_us = sum(v for k, v in per_call.items() if k.startswith("fwd"))
     bwd_us = sum(v for k, v in per_call.items() if not k.startswith("fwd"))
@@ -231,6 +278,7 @@ def report(wl, ms_step, per_call, steps, warmup, cpu):
         "steps": steps,
         "warmup": warmup,
         "ms_per_step": round(ms_step, 5),
+        "ms_per_step_eager": round(ms_eager, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": vs,
@@ -270,11 +318,11 @@ def main():
             print(f"unknown workload {name}; choose from {names}", file=sys.stderr)
             sys.exit(2)
         wl = inputs.WORKLOADS[names.index(name)]
-        ms, per_call = run_gpu(wl, a.steps, a.warmup)
+        ms, ms_eager, per_call = run_gpu(wl, a.steps, a.warmup)
         cpu = None
         if not a.no_cpu and name == DEFAULT_WORKLOAD:
             cpu = cpu_baseline(wl, a.cpu_seconds)
-        print(json.dumps(report(wl, ms, per_call, a.steps, a.warmup, cpu)), flush=True)
+        print(json.dumps(report(wl, ms, ms_eager, per_call, a.steps, a.warmup, cpu)), flush=True)
 
 
 if __name__ == "__main__":
