@@ -95,6 +95,10 @@ bool fwd_bf16_plan(const Geom &g, FwdBfPlan &p)
 {
     return use_ig() && cached_plan(g, plan_fwd_ig_bf16, p);
 }
+bool dgrad_bf16_plan(const Geom &g, DgradBfPlan &p)
+{
+    return use_ig() && cached_plan(g, plan_dgrad_ig_bf16, p);
+}
 bool dgrad_plan(const Geom &g, DgradIgPlan &p)
 {
     return use_ig() && cached_plan(g, plan_dgrad_ig_f32, p);
@@ -161,7 +165,11 @@ size_t gc_conv_workspace_bytes(int op, const gc_conv_desc *d, int dtype)
         if (dtype == GC_BF16 && fwd_bf16_plan(g, p)) return p.ws_bytes;
         return 0;
     }
-    case GC_OP_BWD_DATA: return 0;
+    case GC_OP_BWD_DATA: {
+        DgradBfPlan p;
+        if (dtype == GC_BF16 && dgrad_bf16_plan(g, p)) return p.ws_bytes;
+        return 0;
+    }
     case GC_OP_BWD_WEIGHT: return wgrad_ws_bytes(g, dtype);
     default: return 0;
     }
@@ -196,7 +204,6 @@ int gc_conv_bwd_data(const void *dy, const void *w, const void *y_mask, void *dx
                      void *workspace, size_t ws_bytes, const gc_conv_desc *d, int relu,
                      int dtype, void *stream)
 {
-    (void)workspace; (void)ws_bytes;
     Geom g;
     int st = check_desc(d, &g);
     if (st != GC_OK) return st;
@@ -207,6 +214,14 @@ int gc_conv_bwd_data(const void *dy, const void *w, const void *y_mask, void *dx
         (y_mask && !aligned(y_mask, dtype)))
         return GC_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == GC_BF16) {
+        DgradBfPlan bp;
+        if (dgrad_bf16_plan(g, bp)) {
+            if (!workspace || ws_bytes < bp.ws_bytes) return GC_ERR_WORKSPACE;
+            if (reinterpret_cast<uintptr_t>(workspace) % 16) return GC_ERR_WORKSPACE;
+            return hip_status(launch_dgrad_ig_bf16(g, bp, dy, w, y_mask, dx, workspace, relu, s));
+        }
+    }
     DgradIgPlan p;
     const bool ig = dgrad_plan(g, p);
     if (dtype == GC_F32)

@@ -22,6 +22,7 @@ int wgrad_generic_splits(const Geom &g);
 struct FwdIgPlan;
 struct DgradIgPlan;
 struct WgradIgPlan;
+struct DgradBfPlan;
 bool plan_fwd_ig_f32(const Geom &g, FwdIgPlan &p);
 hipError_t launch_fwd_ig_f32(const Geom &g, const FwdIgPlan &p, const void *x, const void *w,
                              void *y, int relu, hipStream_t s);
@@ -41,6 +42,9 @@ struct FwdBfPlan;
 bool plan_fwd_ig_bf16(const Geom &g, FwdBfPlan &p);
 hipError_t launch_fwd_ig_bf16(const Geom &g, const FwdBfPlan &p, const void *x, const void *w,
                               void *y, void *ws, int relu, hipStream_t s);
+bool plan_dgrad_ig_bf16(const Geom &g, DgradBfPlan &p);
+hipError_t launch_dgrad_ig_bf16(const Geom &g, const DgradBfPlan &p, const void *dy, const void *w,
+                                const void *ym, void *dx, void *ws, int relu, hipStream_t s);
 
 // Fixed-order sum of split partials, then the store in the output type
 // (wgrad_reduce.hip).

@@ -111,6 +111,25 @@ struct FwdBfPlan {
 };
 
 // ---------------------------------------------------------------- d_input --
+// bf16 d_input on bf16 MFMA (dgrad_ig_bf16.hip).
+struct DgradBfPlan {
+    int NW;       // waves per workgroup (they split each chunk's column blocks)
+    int G;        // images per workgroup, a multiple of 4
+    int MB;       // 16-row blocks over the G*P rows m = p*G + img
+    int KS;       // 32-channel steps over OC (zero-padded)
+    int TAPS;     // register slots for the taps of one input pixel
+    int CC;       // input channels per chunk
+    int NBC;      // 16-column blocks per chunk, ceil(CC*KH*KW / 16)
+    int nchunks;  // ceil(IC / CC)
+    int cgroups;  // workgroups along the chunks
+    int cpg;      // chunks per workgroup
+    int RP;       // dcol column pitch in floats (MB*16 + 4)
+    int OCP;      // dz row pitch in bf16 elements (32*KS + 8)
+    int dz_bytes; // LDS bytes of the dz tile
+    size_t lds;       // dz tile + double-buffered dcol
+    size_t ws_bytes;  // packed weights
+};
+
 struct DgradIgPlan {
     int NW;       // waves per workgroup (they split the dcol columns)
     int G;        // images per workgroup
