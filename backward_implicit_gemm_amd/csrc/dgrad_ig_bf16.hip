@@ -12,14 +12,17 @@
 // blocks.  The weights are pre-packed (a small kernel before the main one)
 // into the exact B-fragment order -- [chunk][column block][32-oc step][lane]
 // x 8 oc -- so a wave's B operand for one step is one contiguous 1 KB load,
-// issued one block ahead of its use.  The fp32 dcol tile goes to LDS, column
+// requested one chunk ahead of its use.  The fp32 dcol tile goes to LDS, column
 // by column, and the chunk's input gradient is gathered from it:
 //     dx[b][ic][ih][iw] = sum over the taps with oh*S+kh = ih, ow*S+kw = iw
 //                         of dcol[(oh,ow,b)][(ic,kh,kw)]
 // Because the image index is innermost in m, one 16-byte LDS read returns a
 // tap for four images at once.  The sum is in fp32 in a fixed tap order and
-// rounded to bf16 once.  dcol is double-buffered, so one barrier per chunk
-// separates the MFMA writes from the gather reads.
+// rounded to bf16 once into an LDS tile of the chunk's dx, which leaves in
+// 16-byte stores after the next barrier.  dcol and the dx tile are
+// double-buffered, so one barrier per chunk separates every LDS producer from
+// its consumers.  Index arithmetic is
+// 32-bit (the C ABI caps every tensor below 2^31 elements).
 #include "gc_kernels.h"
 #include "ig_common.h"
 
@@ -73,7 +76,21 @@ struct DgradBfArgs {
 
 __device__ __forceinline__ float bf_to_f(u16 v) { return __uint_as_float(uint32_t(v) << 16); }
 
-template <int NW, int MB, int KS, int TAPS>
+// 16 bytes from a 2-byte-aligned global address (one global_load_dwordx4).
+__device__ __forceinline__ uint4 ldg16_any(const u16 *p)
+{
+    uint4 v;
+    __builtin_memcpy(&v, p, sizeof(v));
+    return v;
+}
+
+__device__ __forceinline__ u16 half_of(const uint4 &v, int i)
+{
+    const uint32_t w = i < 2 ? v.x : i < 4 ? v.y : i < 6 ? v.z : v.w;
+    return u16((i & 1) ? (w >> 16) : (w & 0xFFFFu));
+}
+
+template <int NW, int MB, int KS, int TAPS, int NBW, int GP>
 __global__ void __launch_bounds__(64 * NW) dgrad_ig_bf16(DgradBfArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint4 lds4[];
@@ -90,52 +107,142 @@ __global__ void __launch_bounds__(64 * NW) dgrad_ig_bf16(DgradBfArgs a)
     u16 *dz = reinterpret_cast<u16 *>(lds4);                                   // [MB*16][OCP]
     float *dcol = reinterpret_cast<float *>(reinterpret_cast<char *>(lds4) + p.dz_bytes);
     const int dcol_buf = p.NBC * 16 * p.RP;                                    // [2][NBC*16][RP]
+    u16 *otile = reinterpret_cast<u16 *>(dcol + 2 * dcol_buf);                // [2][G][ORUN]
+    const int obuf = G * p.ORUN;
+    const int zrow = MB * 16;        // rows zrow .. zrow+G-1 of every dcol column stay zero
 
-    // Padding rows (images past the batch, rows past G*P) and channels past
-    // OC must read as zero.
+    // Zero the dz tile (padding rows and channels past OC must read as 0)
+    // and the zero rows of dcol, which stand in for absent taps.
     for (int i = tid; i < p.dz_bytes / 16; i += NT) lds4[i] = make_uint4(0, 0, 0, 0);
+    {
+        const int per_col = G / 4, n = 2 * p.NBC * 16 * per_col;
+        for (int i = tid; i < n; i += NT) {
+            const int col = i / per_col, k = i - col * per_col;
+            *reinterpret_cast<f32x4 *>(dcol + col * p.RP + zrow + 4 * k) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
 
-    // Gather role: this thread owns input pixel q of the (channel, image
-    // quad) planes r0, r0 + rpi, ...  Pixel (ih, iw) takes the taps
-    // oh*S + kh = ih, ow*S + kw = iw; their dcol offsets are fixed.
+    // The weight fragments of this wave's first chunk are requested now; each
+    // later chunk's are requested one chunk ahead of their use.
+    auto nbc_of = [&](int c) {
+        const int cc = min(p.CC, g.IC - c * p.CC);
+        return (cc * g.KK + 15) >> 4;
+    };
+    uint4 bcur[NBW][KS], bnext[NBW][KS];
+    auto load_b = [&](int c, uint4 (&dst)[NBW][KS]) {
+        const int nbc = nbc_of(c);
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+            const int nbl = min(wave + j * NW, nbc - 1);      // clamped: always a valid block
+            const uint4 *src = a.wp + (uint32_t(c * p.NBC + nbl) * KS * 64 + lane);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) dst[j][ks] = src[ks * 64];
+        }
+    };
+    if (c_begin < c_end) load_b(c_begin, bcur);
+
+    // dz: the group's gimg*OC*P contiguous elements of dy (and y), 8 per
+    // 16-byte load, all of a thread's loads in flight together; element
+    // e = (img, oc, p) goes to LDS row m = p*G + img, column oc.  With a ReLU
+    // the element is kept where y > 0: for bf16 bits, 0 < bits <= 0x7F80
+    // (positive, finite or +inf; NaN and -0 excluded).
+    __syncthreads();            // zero fill complete
+    {
+        const int n = gimg * g.OC * g.P;
+        const int n8 = n >> 3;
+        const uint32_t base = uint32_t(b0) * g.OC * g.P;
+        const int step = G * p.OCP;
+        // writes elements e0 .. e0+cnt-1 held in v/m (8 lanes of 16 bits)
+        auto put8 = [&](int e0, const uint4 &v, const uint4 &m, int cnt) {
+            uint32_t img, rem, oc, pp;
+            fdivmod(uint32_t(e0), a.fd_ocp, img, rem);
+            fdivmod(rem, g.fd_P, oc, pp);
+            int dst = (int(pp) * G + int(img)) * p.OCP + int(oc);
+            int ip = int(pp), ioc = int(oc);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (i >= cnt) break;
+                u16 x = half_of(v, i);
+                if (a.relu && uint32_t(half_of(m, i)) - 1u >= 0x7F80u) x = 0;
+                dz[dst] = x;
+                // advance (img, oc, p) by one element in NCHW order
+                ++ip;
+                dst += step;
+                if (ip == g.P) {
+                    ip = 0;
+                    ++ioc;
+                    dst += 1 - g.P * step;
+                    if (ioc == g.OC) {
+                        ioc = 0;
+                        dst += 1 * p.OCP - g.OC;   // next image: row + 1, column 0
+                    }
+                }
+            }
+        };
+        constexpr int U = 4;
+        uint4 dv[U], mv[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int u = tid + k * NT;
+            dv[k] = mv[k] = make_uint4(0, 0, 0, 0);
+            if (u < n8) {
+                dv[k] = ldg16_any(a.dy + base + 8 * u);
+                if (a.relu) mv[k] = ldg16_any(a.ym + base + 8 * u);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int u = tid + k * NT;
+            if (u < n8) put8(8 * u, dv[k], mv[k], 8);
+        }
+        for (int u = tid + U * NT; u < n8; u += NT) {
+            const uint4 v = ldg16_any(a.dy + base + 8 * u);
+            const uint4 m = a.relu ? ldg16_any(a.ym + base + 8 * u) : make_uint4(0, 0, 0, 0);
+            put8(8 * u, v, m, 8);
+        }
+        if (tid == 0 && 8 * n8 < n) {
+            // the last n % 8 elements
+            u16 tv[8] = {0, 0, 0, 0, 0, 0, 0, 0}, tm[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            for (int e = 8 * n8; e < n; ++e) {
+                tv[e - 8 * n8] = a.dy[base + e];
+                tm[e - 8 * n8] = a.relu ? a.ym[base + e] : u16(0);
+            }
+            uint4 v, m;
+            v.x = tv[0] | (uint32_t(tv[1]) << 16); v.y = tv[2] | (uint32_t(tv[3]) << 16);
+            v.z = tv[4] | (uint32_t(tv[5]) << 16); v.w = tv[6] | (uint32_t(tv[7]) << 16);
+            m.x = tm[0] | (uint32_t(tm[1]) << 16); m.y = tm[2] | (uint32_t(tm[3]) << 16);
+            m.z = tm[4] | (uint32_t(tm[5]) << 16); m.w = tm[6] | (uint32_t(tm[7]) << 16);
+            put8(8 * n8, v, m, n - 8 * n8);
+        }
+    }
+
+    // Gather role: this thread owns input pixel q of the (image quad,
+    // channel) planes r0, r0 + rpi, ...  Pixel (ih, iw) takes the taps
+    // oh*S + kh = ih, ow*S + kw = iw, i.e. oh in [oh_lo, oh_hi] and ow in
+    // [ow_lo, ow_hi]; their dcol offsets are fixed.  Unused tap slots point
+    // at the zero rows, so every thread issues the same TAPS reads and adds.
     const int rpi = NT / g.HW;
     const bool gthr = tid < rpi * g.HW;
     const int q = gthr ? tid % g.HW : 0;
     const int r0 = gthr ? tid / g.HW : 0;
     int toff[TAPS];
-    int ntap = 0;
     {
-        const int ih = q / g.W, iw = q % g.W;
+        uint32_t ih, iw;
+        fdivmod(uint32_t(q), g.fd_W, ih, iw);
+        auto lo = [&](int i, int k) { return i - k + 1 <= 0 ? 0 : int(fdiv(uint32_t(i - k + g.S), g.fd_S)); };
+        const int oh_lo = lo(int(ih), g.KH), oh_hi = min(g.OH - 1, int(fdiv(ih, g.fd_S)));
+        const int ow_lo = lo(int(iw), g.KW), ow_hi = min(g.OW - 1, int(fdiv(iw, g.fd_S)));
 #pragma unroll
-        for (int j = 0; j < TAPS; ++j) toff[j] = 0;
-        for (int oh = 0; oh < g.OH; ++oh) {
-            const int kh = ih - oh * g.S;
-            if (kh < 0 || kh >= g.KH) continue;
-            for (int ow = 0; ow < g.OW; ++ow) {
-                const int kw = iw - ow * g.S;
-                if (kw < 0 || kw >= g.KW) continue;
-                const int off = (kh * g.KW + kw) * p.RP + (oh * g.OW + ow) * G;
+        for (int j = 0; j < TAPS; ++j) toff[j] = zrow;
+        int j = 0;
+        for (int oh = oh_lo; oh <= oh_hi; ++oh)
+            for (int ow = ow_lo; ow <= ow_hi; ++ow, ++j) {
+                const int off = ((int(ih) - oh * g.S) * g.KW + int(iw) - ow * g.S) * p.RP +
+                                (oh * g.OW + ow) * G;
 #pragma unroll
-                for (int j = 0; j < TAPS; ++j)
-                    if (j == ntap) toff[j] = off;
-                ++ntap;
+                for (int t = 0; t < TAPS; ++t)
+                    if (t == j) toff[t] = off;
             }
-        }
-    }
-    __syncthreads();
-
-    // dz rows m = p*G + img, columns oc
-    {
-        const int n = gimg * g.OC * g.P;
-        const size_t base = size_t(b0) * g.OC * g.P;
-        for (int e = tid; e < n; e += NT) {
-            uint32_t img, rem, oc, pp;
-            fdivmod(e, a.fd_ocp, img, rem);
-            fdivmod(rem, g.fd_P, oc, pp);
-            u16 v = a.dy[base + e];
-            if (a.relu && !(bf_to_f(a.ym[base + e]) > 0.f)) v = 0;
-            dz[(int(pp) * G + int(img)) * p.OCP + int(oc)] = v;
-        }
     }
     __syncthreads();
 
@@ -149,37 +256,35 @@ __global__ void __launch_bounds__(64 * NW) dgrad_ig_bf16(DgradBfArgs a)
             af[mb][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(row + ks * 32));
     }
 
-    // This wave's column blocks: nbl = wave, wave + NW, ... of every chunk.
-    auto nbc_of = [&](int c) {
-        const int cc = min(p.CC, g.IC - c * p.CC);
-        return (cc * g.KK + 15) >> 4;
-    };
-    int nc = c_begin, nn = wave;               // next block to load
-    auto skip = [&]() {
-        while (nc < c_end && nn >= nbc_of(nc)) {
-            ++nc;
-            nn = wave;
+    // The chunk's dx tile, staged in LDS as [img][icl*HW + q], leaves in
+    // 16-byte stores: for each image the chunk's cc*HW elements are
+    // contiguous in dx.
+    auto store_tile = [&](int c, const u16 *tile) {
+        const int c0 = c * p.CC;
+        const int run = min(p.CC, g.IC - c0) * g.HW;
+        const int nu = (run + 7) >> 3;
+        for (int u = tid; u < gimg * nu; u += NT) {
+            const int img = u / nu, e0 = (u - img * nu) * 8;
+            u16 *dst = a.dx + ((uint32_t(b0 + img) * g.IC + uint32_t(c0)) * g.HW + e0);
+            const u16 *src = tile + img * p.ORUN + e0;
+            if (e0 + 8 <= run) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(src);
+                __builtin_memcpy(dst, &v, sizeof(v));
+            } else {
+                for (int i = 0; i < run - e0; ++i) dst[i] = src[i];
+            }
         }
     };
-    uint4 bnext[KS];
-    auto load_b = [&]() {
-        const uint4 *src = a.wp + (size_t(nc) * p.NBC + nn) * KS * 64 + lane;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) bnext[ks] = src[ks * 64];
-    };
-    skip();
-    if (nc < c_end) load_b();
 
     for (int c = c_begin; c < c_end; ++c) {
-        float *dbuf = dcol + ((c - c_begin) & 1) * dcol_buf;
+        const int cb = (c - c_begin) & 1;
+        float *dbuf = dcol + cb * dcol_buf;
         const int nbc = nbc_of(c);
-        for (int nbl = wave; nbl < nbc; nbl += NW) {
-            uint4 b[KS];
+        if (c + 1 < c_end) load_b(c + 1, bnext);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) b[ks] = bnext[ks];
-            nn += NW;
-            skip();
-            if (nc < c_end) load_b();
+        for (int j = 0; j < NBW; ++j) {
+            const int nbl = wave + j * NW;
+            if (nbl >= nbc) break;
             f32x4 acc[MB];
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -188,53 +293,92 @@ __global__ void __launch_bounds__(64 * NW) dgrad_ig_bf16(DgradBfArgs a)
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
                     acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        af[mb][ks], __builtin_bit_cast(bf16x8, b[ks]), acc[mb], 0, 0, 0);
+                        af[mb][ks], __builtin_bit_cast(bf16x8, bcur[j][ks]), acc[mb], 0, 0, 0);
             // lane holds rows mb*16 + 4*(lane/16) + v of column nbl*16 + lane%16
             float *dst = dbuf + (nbl * 16 + (lane & 15)) * p.RP + (lane >> 4) * 4;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) *reinterpret_cast<f32x4 *>(dst + mb * 16) = acc[mb];
         }
         __syncthreads();
-
-        // gather the chunk's input gradient, four images per LDS read
-        if (gthr) {
-            const int c0 = c * p.CC;
-            const int cc = min(p.CC, g.IC - c0);
-            const int nquad = (gimg + 3) >> 2;
-            for (int pl = r0; pl < cc * nquad; pl += rpi) {
-                const int quad = pl / cc, icl = pl - quad * cc;
-                const float *src = dbuf + icl * g.KK * p.RP + quad * 4;
-                f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+        // next chunk's fragments: the loads were issued a whole MFMA phase
+        // ago; retire them before this iteration's stores are issued
+        wait_vm();
 #pragma unroll
-                for (int j = 0; j < TAPS; ++j)
-                    if (j < ntap) s += *reinterpret_cast<const f32x4 *>(src + toff[j]);
-                const int img0 = quad * 4;
-                u16 *out = a.dx + (size_t(b0 + img0) * g.IC + c0 + icl) * g.HW + q;
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) bcur[j][ks] = bnext[j][ks];
+
+        // the previous chunk's dx tile (complete since the barrier)
+        if (c > c_begin) store_tile(c - 1, otile + (cb ^ 1) * obuf);
+
+        // gather the chunk's input gradient, four images per LDS read;
+        // plane pl = quad*cc + icl, this thread's planes r0 + k*rpi for
+        // k < GP, all LDS reads issued before the first sum
+        if (gthr) {
+            const int cc = min(p.CC, g.IC - c * p.CC);
+            const int nplanes = cc * ((gimg + 3) >> 2);
+            int quad[GP], icl[GP];
+            {
+                int qd = 0, ic = r0;
+                while (ic >= cc) { ic -= cc; ++qd; }
+#pragma unroll
+                for (int k = 0; k < GP; ++k) {
+                    quad[k] = qd;
+                    icl[k] = ic;
+                    ic += rpi;
+                    while (ic >= cc) { ic -= cc; ++qd; }
+                }
+            }
+            f32x4 v[GP][TAPS];
+#pragma unroll
+            for (int k = 0; k < GP; ++k) {
+                // planes past the chunk read plane 0 (valid LDS) and are not stored
+                const bool on = r0 + k * rpi < nplanes;
+                const float *src = dbuf + (on ? icl[k] * g.KK * p.RP + quad[k] * 4 : 0);
+#pragma unroll
+                for (int j = 0; j < TAPS; ++j) v[k][j] = *reinterpret_cast<const f32x4 *>(src + toff[j]);
+            }
+            u16 *ot = otile + cb * obuf;
+#pragma unroll
+            for (int k = 0; k < GP; ++k) {
+                if (r0 + k * rpi >= nplanes) break;
+                f32x4 sum = v[k][0];
+#pragma unroll
+                for (int j = 1; j < TAPS; ++j) sum += v[k][j];
+                const int img0 = quad[k] * 4;
+                u16 *o = ot + img0 * p.ORUN + icl[k] * g.HW + q;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (img0 + i < gimg) out[size_t(i) * g.IC * g.HW] = from_f32<bf16_t>(s[i]);
+                    if (img0 + i < gimg) o[i * p.ORUN] = from_f32<bf16_t>(sum[i]);
             }
         }
     }
+    __syncthreads();
+    if (c_end > c_begin) store_tile(c_end - 1, otile + ((c_end - 1 - c_begin) & 1) * obuf);
 }
 
 struct DgradBfVariant {
-    int NW, MB, KS, TAPS;
+    int NW, MB, KS, TAPS, NBW, GP;
     void (*fn)(DgradBfArgs);
 };
 
-#define DB_V(MB, KS, TAPS) {8, MB, KS, TAPS, dgrad_ig_bf16<8, MB, KS, TAPS>}
-#define DB_TAPS(MB, KS) DB_V(MB, KS, 2), DB_V(MB, KS, 4), DB_V(MB, KS, 9)
+// GP (gather passes per chunk) is 2 throughout: the planner keeps every
+// chunk's planes within two passes of the gather threads.
+#define DB_V(MB, KS, TAPS, NBW) {8, MB, KS, TAPS, NBW, 2, dgrad_ig_bf16<8, MB, KS, TAPS, NBW, 2>}
+#define DB_NBW(MB, KS, TAPS) DB_V(MB, KS, TAPS, 1), DB_V(MB, KS, TAPS, 2)
+#define DB_TAPS(MB, KS) DB_NBW(MB, KS, 2), DB_NBW(MB, KS, 4), DB_NBW(MB, KS, 9)
 #define DB_KS(MB) DB_TAPS(MB, 1), DB_TAPS(MB, 2), DB_TAPS(MB, 4)
 const DgradBfVariant kDgradBfVariants[] = {DB_KS(1), DB_KS(2), DB_KS(3), DB_KS(4)};
 #undef DB_KS
 #undef DB_TAPS
+#undef DB_NBW
 #undef DB_V
 
-const DgradBfVariant *pick_dgrad_bf(int NW, int MB, int KS, int TAPS)
+const DgradBfVariant *pick_dgrad_bf(int NW, int MB, int KS, int TAPS, int NBW, int GP)
 {
     for (const auto &v : kDgradBfVariants)
-        if (v.NW == NW && v.MB == MB && v.KS == KS && v.TAPS == TAPS) return &v;
+        if (v.NW == NW && v.MB == MB && v.KS == KS && v.TAPS == TAPS && v.NBW == NBW && v.GP == GP)
+            return &v;
     return nullptr;
 }
 
@@ -281,12 +425,19 @@ bool plan_dgrad_ig_bf16(const Geom &g, DgradBfPlan &p)
         if (MB > 4) break;
         if (G > 4 && G - 4 >= g.B) break;   // no larger group than the batch needs
         const int OCP = 32 * KS + 8;
-        const int RP = MB * 16 + 4;
+        // column pitch: MB*16 computed rows, G zero rows, and RP/4 odd so the
+        // 16-byte column writes of 16 lanes hit distinct bank groups
+        const int RP = MB * 16 + G + (((G / 4) & 1) ? 0 : 4);
         const size_t dz_bytes = size_t(MB) * 16 * OCP * 2;
         const int ngroups = (g.B + G - 1) / G;
         for (int CC = 1; CC <= g.IC; ++CC) {
             const int NBC = (CC * g.KK + 15) / 16;
-            const size_t lds = dz_bytes + 2 * size_t(NBC) * 16 * RP * 4;
+            const int NBW = (NBC + NW - 1) / NW;
+            if (NBW > 2) break;
+            const int GP = 2;
+            if (CC * (G / 4) > GP * rpi) break;
+            const int ORUN = (CC * g.HW + 7) & ~7;
+            const size_t lds = dz_bytes + 2 * size_t(NBC) * 16 * RP * 4 + 2 * size_t(G) * ORUN * 2;
             if (lds > 160 * 1024) break;
             const int nchunks = (g.IC + CC - 1) / CC;
             const int occ = lds <= 80 * 1024 ? 2 : 1;
@@ -303,11 +454,11 @@ bool plan_dgrad_ig_bf16(const Geom &g, DgradBfPlan &p)
             const double waves_of_wgs = std::ceil(double(ngroups) * cgroups / (256.0 * occ));
             const double t = waves_of_wgs * per_wg * (occ == 2 ? 1.4 : 1.0);
             if (t < best - 1e-9) {
-                if (!pick_dgrad_bf(NW, MB, KS, TAPS)) continue;
+                if (!pick_dgrad_bf(NW, MB, KS, TAPS, NBW, GP)) continue;
                 best = t;
-                p.NW = NW; p.G = G; p.MB = MB; p.KS = KS; p.TAPS = TAPS;
+                p.NW = NW; p.G = G; p.MB = MB; p.KS = KS; p.TAPS = TAPS; p.NBW = NBW; p.GP = GP;
                 p.CC = CC; p.NBC = NBC; p.nchunks = nchunks; p.cgroups = cgroups; p.cpg = cpg;
-                p.RP = RP; p.OCP = OCP; p.dz_bytes = int(dz_bytes);
+                p.RP = RP; p.OCP = OCP; p.dz_bytes = int(dz_bytes); p.ORUN = ORUN;
                 p.lds = lds;
                 p.ws_bytes = size_t(nchunks) * NBC * KS * 64 * 16;
                 found = true;
@@ -320,8 +471,10 @@ bool plan_dgrad_ig_bf16(const Geom &g, DgradBfPlan &p)
 hipError_t launch_dgrad_ig_bf16(const Geom &g, const DgradBfPlan &p, const void *dy, const void *w,
                                 const void *ym, void *dx, void *ws, int relu, hipStream_t s)
 {
-    const DgradBfVariant *v = pick_dgrad_bf(p.NW, p.MB, p.KS, p.TAPS);
-    if (!v || g.HW > 64 * p.NW || p.G % 4 || p.G * g.P > 16 * p.MB) return hipErrorInvalidValue;
+    const DgradBfVariant *v = pick_dgrad_bf(p.NW, p.MB, p.KS, p.TAPS, p.NBW, p.GP);
+    if (!v || g.HW > 64 * p.NW || p.G % 4 || p.G * g.P > 16 * p.MB || p.NBC > p.NW * p.NBW ||
+        p.RP < 16 * p.MB + p.G || p.CC * (p.G / 4) > p.GP * ((64 * p.NW) / g.HW))
+        return hipErrorInvalidValue;
     const int total = p.nchunks * p.NBC * p.KS * 64;
     if (size_t(total) * 16 > p.ws_bytes) return hipErrorInvalidValue;
     hipLaunchKernelGGL(pack_w_dgrad_bf16, dim3(std::min((total + 255) / 256, 2048)), dim3(256), 0, s,

@@ -66,7 +66,7 @@ struct Geom {
     int KK;   // KH*KW, taps per channel
     int HW;   // H*W, pixels per channel plane
     int K;    // IC*KK, reduction length of the forward GEMM
-    FastDiv fd_P, fd_OW, fd_KK, fd_KW, fd_HW, fd_W, fd_S;
+    FastDiv fd_P, fd_OW, fd_KK, fd_KW, fd_HW, fd_W, fd_S, fd_OC;
 };
 
 inline Geom make_geom(int B, int IC, int H, int W, int OC, int KH, int KW, int S)
@@ -86,6 +86,7 @@ inline Geom make_geom(int B, int IC, int H, int W, int OC, int KH, int KW, int S
     g.fd_HW = make_fastdiv(g.HW);
     g.fd_W = make_fastdiv(W);
     g.fd_S = make_fastdiv(S);
+    g.fd_OC = make_fastdiv(OC);
     return g;
 }
 

@@ -63,21 +63,10 @@ __device__ __forceinline__ float4 ldg4_any(const float *p)
 
 constexpr int IG_NT = 256;   // threads per workgroup (4 waves)
 
-// Direct global -> LDS copy of one 4-byte word per lane (gfx950
-// global_load_lds_dword): lane i writes LDS address lds_wave_base + 4*i,
-// where lds_wave_base must be the same for the whole wave.  No VGPR holds
-// the data, so staging the next chunk costs no registers while the MFMAs of
-// the current one run.  Completion is tracked by vmcnt: wait_vm() before the
-// barrier that publishes the buffer.
-__device__ __forceinline__ void g2lds_dword(const void *src, void *lds_wave_base)
-{
-    __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void *)src,
-        (__attribute__((address_space(3))) void *)lds_wave_base, 4, 0, 0);
-}
-
-// s_waitcnt vmcnt(0): every global load (including LDS-direct ones) of this
-// wave has landed.
+// s_waitcnt vmcnt(0): every vector memory operation this wave has issued has
+// completed.  Placed where only loads issued long ago are outstanding, it
+// retires them before later stores are issued, so a later use of the loaded
+// registers does not wait for those stores as well.
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ---------------------------------------------------------------- forward --
@@ -118,6 +107,8 @@ struct DgradBfPlan {
     int MB;       // 16-row blocks over the G*P rows m = p*G + img
     int KS;       // 32-channel steps over OC (zero-padded)
     int TAPS;     // register slots for the taps of one input pixel
+    int NBW;      // column blocks per wave per chunk, ceil(NBC / NW)
+    int GP;       // gather passes per chunk (planes CC*G/4 <= GP * gather threads per pixel)
     int CC;       // input channels per chunk
     int NBC;      // 16-column blocks per chunk, ceil(CC*KH*KW / 16)
     int nchunks;  // ceil(IC / CC)
@@ -126,7 +117,8 @@ struct DgradBfPlan {
     int RP;       // dcol column pitch in floats (MB*16 + 4)
     int OCP;      // dz row pitch in bf16 elements (32*KS + 8)
     int dz_bytes; // LDS bytes of the dz tile
-    size_t lds;       // dz tile + double-buffered dcol
+    int ORUN;     // dx tile row (one image's chunk, CC*H*W) rounded up to 8 elements
+    size_t lds;       // dz tile + double-buffered dcol + double-buffered dx tile
     size_t ws_bytes;  // packed weights
 };
 
