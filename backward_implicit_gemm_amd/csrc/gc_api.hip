@@ -99,6 +99,10 @@ bool dgrad_bf16_plan(const Geom &g, DgradBfPlan &p)
 {
     return use_ig() && cached_plan(g, plan_dgrad_ig_bf16, p);
 }
+bool wgrad_bf16_plan(const Geom &g, WgradBfPlan &p)
+{
+    return use_ig() && cached_plan(g, plan_wgrad_ig_bf16, p);
+}
 bool dgrad_plan(const Geom &g, DgradIgPlan &p)
 {
     return use_ig() && cached_plan(g, plan_dgrad_ig_f32, p);
@@ -124,6 +128,8 @@ int wgrad_splits(const Geom &g, int dtype, WgradIgPlan *ig, bool *use)
 
 size_t wgrad_ws_bytes(const Geom &g, int dtype)
 {
+    WgradBfPlan bp;
+    if (dtype == GC_BF16 && wgrad_bf16_plan(g, bp)) return bp.ws_bytes;
     return size_t(wgrad_splits(g, dtype, nullptr, nullptr)) * g.OC * g.K * sizeof(float);
 }
 
@@ -244,13 +250,21 @@ int gc_conv_bwd_weight(const void *x, const void *dy, const void *y_mask, void *
     if (!aligned(x, dtype) || !aligned(dy, dtype) || !aligned(dw, dtype) ||
         (y_mask && !aligned(y_mask, dtype)))
         return GC_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == GC_BF16) {
+        WgradBfPlan bp;
+        if (wgrad_bf16_plan(g, bp)) {
+            if (!workspace || ws_bytes < bp.ws_bytes) return GC_ERR_WORKSPACE;
+            if (reinterpret_cast<uintptr_t>(workspace) % 256) return GC_ERR_WORKSPACE;
+            return hip_status(launch_wgrad_ig_bf16(g, bp, x, dy, y_mask, dw, workspace, relu, s));
+        }
+    }
     WgradIgPlan ig;
     bool use_ig_path = false;
     const int splits = wgrad_splits(g, dtype, &ig, &use_ig_path);
     const size_t need = size_t(splits) * g.OC * g.K * sizeof(float);
     if (need && (!workspace || ws_bytes < need)) return GC_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % 16) return GC_ERR_WORKSPACE;
-    hipStream_t s = static_cast<hipStream_t>(stream);
     float *part = static_cast<float *>(workspace);
     hipError_t e;
     if (dtype == GC_F32) {

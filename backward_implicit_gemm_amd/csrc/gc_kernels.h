@@ -23,6 +23,7 @@ struct FwdIgPlan;
 struct DgradIgPlan;
 struct WgradIgPlan;
 struct DgradBfPlan;
+struct WgradBfPlan;
 bool plan_fwd_ig_f32(const Geom &g, FwdIgPlan &p);
 hipError_t launch_fwd_ig_f32(const Geom &g, const FwdIgPlan &p, const void *x, const void *w,
                              void *y, int relu, hipStream_t s);
@@ -43,6 +44,10 @@ bool plan_fwd_ig_bf16(const Geom &g, FwdBfPlan &p);
 hipError_t launch_fwd_ig_bf16(const Geom &g, const FwdBfPlan &p, const void *x, const void *w,
                               void *y, void *ws, int relu, hipStream_t s);
 bool plan_dgrad_ig_bf16(const Geom &g, DgradBfPlan &p);
+bool plan_wgrad_ig_bf16(const Geom &g, WgradBfPlan &p);
+// dz regrouping, the partial-tile kernel and the fixed-order reduction into dw
+hipError_t launch_wgrad_ig_bf16(const Geom &g, const WgradBfPlan &p, const void *x, const void *dy,
+                                const void *ym, void *dw, void *ws, int relu, hipStream_t s);
 hipError_t launch_dgrad_ig_bf16(const Geom &g, const DgradBfPlan &p, const void *dy, const void *w,
                                 const void *ym, void *dx, void *ws, int relu, hipStream_t s);
 

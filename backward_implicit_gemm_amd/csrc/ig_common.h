@@ -145,6 +145,22 @@ struct DgradIgPlan {
 };
 
 // ---------------------------------------------------------------- wgrad ----
+// bf16 wgrad on bf16 MFMA (wgrad_ig_bf16.hip).
+struct WgradBfPlan {
+    int NSTEP;    // MFMA steps per 8-image group, PP / 4
+    int PP;       // output positions padded to a multiple of 4
+    int CCW;      // input channels staged per 128-column tile (widest span)
+    int nblk;     // 8-pixel blocks per channel plane
+    int HWP;      // LDS pixel slots per staged channel (nblk * 8)
+    int ncol;     // 128-column tiles over IC*KH*KW
+    int ngroups;  // 8-image groups, ceil(B / 8)
+    int gps;      // groups per split
+    int splits;   // workgroup rows (partial tiles)
+    size_t lds;       // double-buffered x and dz stages
+    size_t dz_bytes;  // regrouped dz at the front of the workspace
+    size_t ws_bytes;  // dz_bytes + splits * OC * K fp32 partials
+};
+
 struct WgradIgPlan {
     int NW;       // waves per workgroup: 4 split OC, NW/4 split the k tile
     int G;        // images per stage

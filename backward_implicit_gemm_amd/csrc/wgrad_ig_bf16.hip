@@ -1,0 +1,331 @@
+// wgrad_ig_bf16.hip -- weight gradient, bf16 storage, bf16 MFMA with fp32
+// accumulation, split-K over groups of 8 images.
+//
+//     dw[oc][n] = sum over (b, p) of dz[b][oc][p] * x[b][ic][oh*S+kh][ow*S+kw],
+//     n = (ic, kh, kw), p = (oh, ow), dz = dy * (y > 0) (dy without a ReLU).
+//
+// The reduction index is ordered (8-image group, position p, image within
+// the group): one v_mfma_f32_16x16x32_bf16 step covers 4 positions x 8
+// images, and each lane's 8 consecutive reduction elements are the 8 images
+// of one (oc, p) or one (n, p), so both operands are single 16-byte LDS
+// reads once the data is staged image-innermost:
+//   * a pre-pass writes dz as [group][p][oc][8 images] (positions padded to a
+//     multiple of 4 and channels to 128 with zeros), so a workgroup's dz stage
+//     for one group is a contiguous 16-byte copy;
+//   * x is staged per group as [channel][pixel][8 images]: a thread loads 8
+//     pixels of one channel for each of the 8 images and transposes the 8x8
+//     block in registers.
+// A workgroup owns 128 output channels x 128 columns (8 waves of 64 x 32)
+// and a contiguous range of image groups; the next group's global loads are
+// in flight while the current group's MFMAs run (double-buffered LDS).  It
+// writes its fp32 partial tile, and a fixed-order sum over the ranges
+// finishes dw (deterministic, no atomics).
+#include "gc_kernels.h"
+#include "ig_common.h"
+
+namespace gc {
+namespace {
+
+typedef unsigned short u16;
+
+__device__ __forceinline__ uint4 ldg16(const u16 *p)
+{
+    uint4 v;
+    __builtin_memcpy(&v, p, sizeof(v));
+    return v;
+}
+
+// dzg unit ((bg*PP + p)*128 + oc) = 8 images of group bg at (oc, p), masked;
+// zero for positions >= P, channels >= OC and images >= B.
+__global__ void __launch_bounds__(256) dz_groups_bf16(const u16 *__restrict__ dy,
+                                                      const u16 *__restrict__ ym,
+                                                      uint4 *__restrict__ dzg, Geom g, int relu,
+                                                      int PP, int total)
+{
+    for (int u = blockIdx.x * 256 + threadIdx.x; u < total; u += gridDim.x * 256) {
+        const int oc = u & 127;
+        const int t = u >> 7;
+        const int p = t % PP;
+        const int bg = t / PP;
+        u16 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int b = bg * 8 + i;
+            u16 d = 0;
+            if (p < g.P && oc < g.OC && b < g.B) {
+                const uint32_t e = (uint32_t(b) * g.OC + oc) * g.P + p;
+                d = dy[e];
+                if (relu && uint32_t(ym[e]) - 1u >= 0x7F80u) d = 0;   // keep where 0 < y <= +inf
+            }
+            v[i] = d;
+        }
+        uint4 o;
+        o.x = v[0] | (uint32_t(v[1]) << 16);
+        o.y = v[2] | (uint32_t(v[3]) << 16);
+        o.z = v[4] | (uint32_t(v[5]) << 16);
+        o.w = v[6] | (uint32_t(v[7]) << 16);
+        dzg[u] = o;
+    }
+}
+
+struct WgradBfArgs {
+    Geom g;
+    const u16 *x;
+    const uint4 *dzg;
+    float *part;
+    WgradBfPlan p;
+};
+
+constexpr int kWgNT = 512;     // 8 waves
+constexpr int kXU = 2;         // x staging units per thread (8 images x 8 pixels each)
+constexpr int kDU = 4;         // dz staging units per thread (16 bytes each)
+
+template <int NSTEP>
+__global__ void __launch_bounds__(kWgNT) wgrad_ig_bf16(WgradBfArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint4 lds4[];
+    const Geom &g = a.g;
+    const WgradBfPlan &p = a.p;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1;          // output channels 64*wm .. +63
+    const int wn = wave >> 1;         // columns 32*wn .. +31 of the tile
+    const int N = g.K;                // IC*KH*KW columns
+    const int n0 = blockIdx.x * 128;
+    const int c_lo = n0 / g.KK;
+    const int gb = blockIdx.y * p.gps;
+    const int ge = min(gb + p.gps, p.ngroups);
+
+    const int xbuf = p.CCW * p.HWP;               // 16-byte units per x stage
+    const int dbuf = p.PP * 128;                  // 16-byte units per dz stage
+    uint4 *xs = lds4;                             // [2][CCW][HWP]
+    uint4 *ds = lds4 + 2 * xbuf;                  // [2][PP][128]
+
+    // ---- per-lane fragment offsets (16-byte units) -------------------------
+    // B (x): column n = n0 + 32*wn + 16*j + lane%16 -> (ic, kh, kw); position
+    // p = 4*s + lane/16 -> pixel (oh*S, ow*S).  Padded columns and positions
+    // read a valid pixel; their dz is zero or their result is not stored.
+    int xcol[2], xrow[NSTEP], drow[NSTEP];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int n = min(n0 + 32 * wn + 16 * j + (lane & 15), N - 1);
+        uint32_t ic, kk, kh, kw;
+        fdivmod(uint32_t(n), g.fd_KK, ic, kk);
+        fdivmod(kk, g.fd_KW, kh, kw);
+        xcol[j] = (int(ic) - c_lo) * p.HWP + int(kh) * g.W + int(kw);
+    }
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+        const int pp = 4 * s + (lane >> 4);
+        const int pc = min(pp, g.P - 1);
+        uint32_t oh, ow;
+        fdivmod(uint32_t(pc), g.fd_OW, oh, ow);
+        xrow[s] = int(oh) * g.S * g.W + int(ow) * g.S;
+        drow[s] = pp * 128 + 64 * wm + (lane & 15);
+    }
+
+    // ---- staging -----------------------------------------------------------
+    // x unit u = (icl, 8-pixel block): 8 images x 16 bytes, transposed to
+    // 8 pixels x (8 images) in LDS.  dz unit: one 16-byte copy.
+    const int nxu = p.CCW * p.nblk;
+    uint32_t xin[kXU][8][4];
+    uint4 dreg[kDU];
+    auto fetch = [&](int grp) {
+        const int b0 = grp * 8;
+#pragma unroll
+        for (int k = 0; k < kXU; ++k) {
+            const int u = tid + k * kWgNT;
+            const int icl = u / p.nblk, blk = u - icl * p.nblk;
+            const int ic = c_lo + icl;
+            const int pix = blk * 8;
+            const int npix = min(8, g.HW - pix);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (u < nxu && ic < g.IC && b0 + i < g.B) {
+                    const u16 *src = a.x + (uint32_t(b0 + i) * g.IC + ic) * g.HW + pix;
+                    if (npix == 8) {
+                        v = ldg16(src);
+                    } else {
+                        u16 e[8];
+#pragma unroll
+                        for (int t = 0; t < 8; ++t) e[t] = t < npix ? src[t] : u16(0);
+                        v.x = e[0] | (uint32_t(e[1]) << 16);
+                        v.y = e[2] | (uint32_t(e[3]) << 16);
+                        v.z = e[4] | (uint32_t(e[5]) << 16);
+                        v.w = e[6] | (uint32_t(e[7]) << 16);
+                    }
+                }
+                xin[k][i][0] = v.x; xin[k][i][1] = v.y; xin[k][i][2] = v.z; xin[k][i][3] = v.w;
+            }
+        }
+        const uint4 *src = a.dzg + size_t(grp) * dbuf;
+#pragma unroll
+        for (int k = 0; k < kDU; ++k) {
+            const int u = tid + k * kWgNT;
+            dreg[k] = u < dbuf ? src[u] : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto stash = [&](int buf) {
+        uint4 *xd = xs + buf * xbuf;
+#pragma unroll
+        for (int k = 0; k < kXU; ++k) {
+            const int u = tid + k * kWgNT;
+            if (u >= nxu) continue;
+            const int icl = u / p.nblk, blk = u - icl * p.nblk;
+            const int pix = blk * 8;
+            const int npix = min(8, g.HW - pix);
+            uint4 *dst = xd + icl * p.HWP + pix;
+            // word j of pixel pp = images (2j, 2j+1) at that pixel
+#pragma unroll
+            for (int pp = 0; pp < 8; ++pp) {
+                const int wi = pp >> 1;
+                uint32_t o[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t lo = xin[k][2 * j][wi], hi = xin[k][2 * j + 1][wi];
+                    o[j] = (pp & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+                }
+                if (pp < npix) dst[pp] = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        }
+        uint4 *dd = ds + buf * dbuf;
+#pragma unroll
+        for (int k = 0; k < kDU; ++k) {
+            const int u = tid + k * kWgNT;
+            if (u < dbuf) dd[u] = dreg[k];
+        }
+    };
+
+    f32x4 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (gb < ge) {
+        fetch(gb);
+        stash(0);
+    }
+    __syncthreads();
+    for (int grp = gb; grp < ge; ++grp) {
+        const int buf = (grp - gb) & 1;
+        if (grp + 1 < ge) fetch(grp + 1);
+        const uint4 *xb = xs + buf * xbuf;
+        const uint4 *db = ds + buf * dbuf;
+#pragma unroll
+        for (int s = 0; s < NSTEP; ++s) {
+            bf16x8 af[4], bfr[2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] = __builtin_bit_cast(bf16x8, db[drow[s] + 16 * i]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) bfr[j] = __builtin_bit_cast(bf16x8, xb[xcol[j] + xrow[s]]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+        if (grp + 1 < ge) {
+            stash(buf ^ 1);
+            __syncthreads();
+        }
+    }
+
+    // ---- partial tile: lane holds rows 4*(lane/16) + v of column lane%16 ----
+    float *part = a.part + size_t(blockIdx.y) * g.OC * N;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int n = n0 + 32 * wn + 16 * j + (lane & 15);
+        if (n >= N) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int oc = 64 * wm + 16 * i + 4 * (lane >> 4) + v;
+                if (oc < g.OC) part[uint32_t(oc) * N + n] = acc[i][j][v];
+            }
+    }
+}
+
+struct WgradBfVariant {
+    int NSTEP;
+    void (*fn)(WgradBfArgs);
+};
+const WgradBfVariant kWgradBfVariants[] = {
+    {1, wgrad_ig_bf16<1>}, {2, wgrad_ig_bf16<2>}, {3, wgrad_ig_bf16<3>}, {4, wgrad_ig_bf16<4>},
+};
+
+const WgradBfVariant *pick_wgrad_bf(int nstep)
+{
+    for (const auto &v : kWgradBfVariants)
+        if (v.NSTEP == nstep) return &v;
+    return nullptr;
+}
+
+}  // namespace
+
+// Column tiles of 128, image groups of 8 split over `splits` workgroup rows.
+// The number of splits trades MFMA parallelism (at least ~256 workgroups)
+// against the fp32 partial traffic (splits x OC x K x 4 bytes, written and
+// read back once).
+bool plan_wgrad_ig_bf16(const Geom &g, WgradBfPlan &p)
+{
+    if (g.OC > 128 || g.P > 16) return false;
+    const int PP = (g.P + 3) / 4 * 4;
+    const int NSTEP = PP / 4;
+    if (!pick_wgrad_bf(NSTEP)) return false;
+    const int N = g.K;
+    const int ncol = (N + 127) / 128;
+    // widest channel span of any 128-column tile
+    int CCW = 0;
+    for (int t = 0; t < ncol; ++t) {
+        const int lo = t * 128 / g.KK, hi = std::min(g.IC - 1, (std::min(N, t * 128 + 128) - 1) / g.KK);
+        CCW = std::max(CCW, hi - lo + 1);
+    }
+    const int nblk = (g.HW + 7) / 8;
+    if (CCW * nblk > kXU * kWgNT) return false;
+    if (PP * 128 > kDU * kWgNT) return false;
+    const int HWP = nblk * 8;
+    const size_t lds = 2 * (size_t(CCW) * HWP + size_t(PP) * 128) * 16;
+    if (lds > 160 * 1024) return false;
+    const int ngroups = (g.B + 7) / 8;
+    // splits: enough workgroups to cover the CUs, few enough that the
+    // partial traffic stays small against the operand traffic
+    int splits = std::max(1, std::min(ngroups, (256 + ncol - 1) / ncol));
+    const double part_bytes = double(g.OC) * N * 4;
+    const double in_bytes = double(g.B) * g.IC * g.HW * 2;
+    const double budget = std::max(0.5 * in_bytes, 8.0 * 1024 * 1024);
+    while (splits > 1 && splits * part_bytes > budget) --splits;
+    const int gps = (ngroups + splits - 1) / splits;
+    splits = (ngroups + gps - 1) / gps;
+    p.NSTEP = NSTEP; p.PP = PP; p.CCW = CCW; p.nblk = nblk; p.HWP = HWP;
+    p.ncol = ncol; p.ngroups = ngroups; p.gps = gps; p.splits = splits;
+    p.lds = lds;
+    p.dz_bytes = (size_t(ngroups) * PP * 128 * 16 + 255) / 256 * 256;
+    p.ws_bytes = p.dz_bytes + size_t(splits) * g.OC * N * 4;
+    return true;
+}
+
+hipError_t launch_wgrad_ig_bf16(const Geom &g, const WgradBfPlan &p, const void *x, const void *dy,
+                                const void *ym, void *dw, void *ws, int relu, hipStream_t s)
+{
+    const WgradBfVariant *v = pick_wgrad_bf(p.NSTEP);
+    if (!v || p.CCW * p.nblk > kXU * kWgNT || p.PP * 128 > kDU * kWgNT || g.OC > 128)
+        return hipErrorInvalidValue;
+    uint4 *dzg = static_cast<uint4 *>(ws);
+    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + p.dz_bytes);
+    const int total = p.ngroups * p.PP * 128;
+    hipLaunchKernelGGL(dz_groups_bf16, dim3(std::min((total + 255) / 256, 4096)), dim3(256), 0, s,
+                       (const u16 *)dy, (const u16 *)ym, dzg, g, relu, p.PP, total);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
+    if (e != hipSuccess) return e;
+    WgradBfArgs a{g, (const u16 *)x, dzg, part, p};
+    hipLaunchKernelGGL(v->fn, dim3(p.ncol, p.splits), dim3(kWgNT), p.lds, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_wgrad_reduce<bf16_t>(part, dw, p.splits, g.OC * g.K, s);
+}
+
+}  // namespace gc

@@ -106,12 +106,34 @@ def test_wgrad_workspace_errors():
 
 def test_workspace_sizes_are_sane():
     for d in (L1, gb.make_desc(1024, 128, 3, 4, 128, 3, 3, 1), gb.make_desc(3, 2, 5, 5, 3, 2, 2, 1)):
+        K = d.IC * d.KH * d.KW
+        OH, OW = gb.gc_conv_out_dims(d)
+        # regrouped dz: images padded to 8, channels to 128, positions to 4
+        dz_bytes = (d.B + 7) // 8 * 8 * max(d.OC, 128) * ((OH * OW + 3) // 4 * 4) * 2 + 256
         for dt in (gb.GC_F32, gb.GC_BF16):
             n = gb.gc_conv_workspace_bytes(gb.GC_OP_BWD_WEIGHT, d, dt)
-            K = d.IC * d.KH * d.KW
-            assert n % (d.OC * K * 4) == 0 and n >= d.OC * K * 4
-            assert n <= 64 * d.OC * K * 4
+            # fp32 partial tiles (at least one), plus for bf16 at most a
+            # regrouped copy of dz (positions and channels padded)
+            assert n >= d.OC * K * 4
+            if dt == gb.GC_F32:
+                assert n % (d.OC * K * 4) == 0 and n <= 64 * d.OC * K * 4
+            else:
+                assert n <= 64 * d.OC * K * 4 + dz_bytes
+        # packed weights for the bf16 forward and d_input kernels: a padded copy of w
+        for op in (gb.GC_OP_FWD, gb.GC_OP_BWD_DATA):
+            assert gb.gc_conv_workspace_bytes(op, d, gb.GC_F32) == 0
+            n = gb.gc_conv_workspace_bytes(op, d, gb.GC_BF16)
+            assert n == 0 or d.OC * K * 2 <= n <= 16 * max(d.OC, 32) * max(K, 64) * 2
     assert gb.gc_conv_workspace_bytes(99, L1, 0) == 0
+
+
+def test_dgrad_workspace_errors():
+    need = gb.gc_conv_workspace_bytes(gb.GC_OP_BWD_DATA, L1, gb.GC_BF16)
+    assert need > 0
+    assert _call("gc_conv_bwd_data", FAKE, FAKE, FAKE, FAKE, desc=L1, relu=1, dtype=gb.GC_BF16,
+                 ws=None, ws_bytes=0) == gb.GC_ERR_WORKSPACE
+    assert _call("gc_conv_bwd_data", FAKE, FAKE, FAKE, FAKE, desc=L1, relu=1, dtype=gb.GC_BF16,
+                 ws=FAKE, ws_bytes=need - 1) == gb.GC_ERR_WORKSPACE
 
 
 def test_status_strings():
