@@ -16,10 +16,10 @@
 //     pixels of one channel for each of the 8 images and transposes the 8x8
 //     block in registers.
 // A workgroup owns 128 output channels x 128 columns (8 waves of 64 x 32)
-// and a contiguous range of image groups; the next group's global loads are
-// in flight while the current group's MFMAs run (double-buffered LDS).  It
-// writes its fp32 partial tile, and a fixed-order sum over the ranges
-// finishes dw (deterministic, no atomics).
+// and a contiguous range of image groups, pipelined three deep: one group's
+// operands in LDS feeding the MFMAs, the next group's in registers, and the
+// loads of the one after in flight.  It writes its fp32 partial tile, and a
+// fixed-order sum over the ranges finishes dw (deterministic, no atomics).
 #include "gc_kernels.h"
 #include "ig_common.h"
 
@@ -77,8 +77,15 @@ struct WgradBfArgs {
 };
 
 constexpr int kWgNT = 512;     // 8 waves
-constexpr int kXU = 2;         // x staging units per thread (8 images x 8 pixels each)
-constexpr int kDU = 4;         // dz staging units per thread (16 bytes each)
+
+// One stage of staged operands in registers: the x unit of this thread
+// (4 images x 8 pixels of one channel) and its NSTEP dz units (a stage of
+// dz is PP*128 = NSTEP*512 units of 16 bytes).
+template <int NSTEP>
+struct WgStage {
+    uint4 x[4];
+    uint4 d[NSTEP];
+};
 
 template <int NSTEP>
 __global__ void __launch_bounds__(kWgNT) wgrad_ig_bf16(WgradBfArgs a)
@@ -124,76 +131,59 @@ __global__ void __launch_bounds__(kWgNT) wgrad_ig_bf16(WgradBfArgs a)
     }
 
     // ---- staging -----------------------------------------------------------
-    // x unit u = (icl, 8-pixel block): 8 images x 16 bytes, transposed to
-    // 8 pixels x (8 images) in LDS.  dz unit: one 16-byte copy.
-    const int nxu = p.CCW * p.nblk;
-    uint32_t xin[kXU][8][4];
-    uint4 dreg[kDU];
-    auto fetch = [&](int grp) {
-        const int b0 = grp * 8;
+    // x unit (icl, blk, half): pixels [pix, pix+8) of channel c_lo + icl for
+    // images 4*half .. 4*half+3 of the group, pix = min(8*blk, HW-8) so every
+    // 16-byte load stays inside its plane (the last block overlaps its
+    // neighbour and rewrites the same values).  Every thread issues the same
+    // loads, from clamped valid addresses where it has no unit, so the wait
+    // for a stage is an exact count of the loads issued after it.  Images
+    // past the batch are zeroed (their dz is zero too; a zero x keeps
+    // non-finite values out of the sums).
+    const bool xon = tid < 2 * p.CCW * p.nblk;
+    const int xunit = xon ? tid >> 1 : 0;
+    const int xhalf = tid & 1;
+    const int xicl = xunit / p.nblk;
+    const int xpix = min(8 * (xunit - xicl * p.nblk), g.HW - 8);
+    const int xic = min(c_lo + xicl, g.IC - 1);
+    auto fetch = [&](int grp, WgStage<NSTEP> &st) {
+        const int b0 = grp * 8 + 4 * xhalf;
 #pragma unroll
-        for (int k = 0; k < kXU; ++k) {
-            const int u = tid + k * kWgNT;
-            const int icl = u / p.nblk, blk = u - icl * p.nblk;
-            const int ic = c_lo + icl;
-            const int pix = blk * 8;
-            const int npix = min(8, g.HW - pix);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (u < nxu && ic < g.IC && b0 + i < g.B) {
-                    const u16 *src = a.x + (uint32_t(b0 + i) * g.IC + ic) * g.HW + pix;
-                    if (npix == 8) {
-                        v = ldg16(src);
-                    } else {
-                        u16 e[8];
-#pragma unroll
-                        for (int t = 0; t < 8; ++t) e[t] = t < npix ? src[t] : u16(0);
-                        v.x = e[0] | (uint32_t(e[1]) << 16);
-                        v.y = e[2] | (uint32_t(e[3]) << 16);
-                        v.z = e[4] | (uint32_t(e[5]) << 16);
-                        v.w = e[6] | (uint32_t(e[7]) << 16);
-                    }
-                }
-                xin[k][i][0] = v.x; xin[k][i][1] = v.y; xin[k][i][2] = v.z; xin[k][i][3] = v.w;
-            }
+        for (int i = 0; i < 4; ++i) {
+            const int b = min(b0 + i, g.B - 1);
+            st.x[i] = ldg16(a.x + (uint32_t(b) * g.IC + xic) * g.HW + xpix);
         }
         const uint4 *src = a.dzg + size_t(grp) * dbuf;
 #pragma unroll
-        for (int k = 0; k < kDU; ++k) {
-            const int u = tid + k * kWgNT;
-            dreg[k] = u < dbuf ? src[u] : make_uint4(0, 0, 0, 0);
-        }
+        for (int k = 0; k < NSTEP; ++k) st.d[k] = src[tid + k * kWgNT];
     };
-    auto stash = [&](int buf) {
-        uint4 *xd = xs + buf * xbuf;
+    auto stash = [&](int grp, const WgStage<NSTEP> &st, int buf) {
+        if (xon) {
+            const int nb = g.B - grp * 8 - 4 * xhalf;   // images of this half in the batch
+            uint32_t in[4][4];
 #pragma unroll
-        for (int k = 0; k < kXU; ++k) {
-            const int u = tid + k * kWgNT;
-            if (u >= nxu) continue;
-            const int icl = u / p.nblk, blk = u - icl * p.nblk;
-            const int pix = blk * 8;
-            const int npix = min(8, g.HW - pix);
-            uint4 *dst = xd + icl * p.HWP + pix;
-            // word j of pixel pp = images (2j, 2j+1) at that pixel
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = i < nb;
+                in[i][0] = ok ? st.x[i].x : 0u; in[i][1] = ok ? st.x[i].y : 0u;
+                in[i][2] = ok ? st.x[i].z : 0u; in[i][3] = ok ? st.x[i].w : 0u;
+            }
+            // pixel pp's 16-byte slot holds images 0..7; this thread writes
+            // the 8 bytes of its four: word j = images (2j, 2j+1)
+            uint2 *dst = reinterpret_cast<uint2 *>(xs + buf * xbuf + xicl * p.HWP + xpix) + xhalf;
 #pragma unroll
             for (int pp = 0; pp < 8; ++pp) {
                 const int wi = pp >> 1;
-                uint32_t o[4];
+                uint32_t o[2];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t lo = xin[k][2 * j][wi], hi = xin[k][2 * j + 1][wi];
+                for (int j = 0; j < 2; ++j) {
+                    const uint32_t lo = in[2 * j][wi], hi = in[2 * j + 1][wi];
                     o[j] = (pp & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
                 }
-                if (pp < npix) dst[pp] = make_uint4(o[0], o[1], o[2], o[3]);
+                dst[2 * pp] = make_uint2(o[0], o[1]);
             }
         }
         uint4 *dd = ds + buf * dbuf;
 #pragma unroll
-        for (int k = 0; k < kDU; ++k) {
-            const int u = tid + k * kWgNT;
-            if (u < dbuf) dd[u] = dreg[k];
-        }
+        for (int k = 0; k < NSTEP; ++k) dd[tid + k * kWgNT] = st.d[k];
     };
 
     f32x4 acc[4][2];
@@ -202,14 +192,7 @@ __global__ void __launch_bounds__(kWgNT) wgrad_ig_bf16(WgradBfArgs a)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (gb < ge) {
-        fetch(gb);
-        stash(0);
-    }
-    __syncthreads();
-    for (int grp = gb; grp < ge; ++grp) {
-        const int buf = (grp - gb) & 1;
-        if (grp + 1 < ge) fetch(grp + 1);
+    auto mfma_stage = [&](int buf) {
         const uint4 *xb = xs + buf * xbuf;
         const uint4 *db = ds + buf * dbuf;
 #pragma unroll
@@ -225,10 +208,30 @@ __global__ void __launch_bounds__(kWgNT) wgrad_ig_bf16(WgradBfArgs a)
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
-        if (grp + 1 < ge) {
-            stash(buf ^ 1);
-            __syncthreads();
-        }
+    };
+
+    // Pipeline: stage i's operands sit in LDS buffer i&1 while stage i+1's
+    // are in registers and stage i+2's loads are in flight.  The register
+    // slots alternate, so the loop body is written out twice.
+    WgStage<NSTEP> r0, r1;
+    const int ng = ge - gb;
+    if (ng > 0) fetch(gb, r0);
+    if (ng > 1) fetch(gb + 1, r1);
+    if (ng > 0) stash(gb, r0, 0);
+    __syncthreads();
+    for (int i = 0; i < ng; i += 2) {
+        // stage i (LDS 0); r1 holds stage i+1; r0 is free
+        if (i + 2 < ng) fetch(gb + i + 2, r0);
+        mfma_stage(0);
+        if (i + 1 >= ng) break;
+        stash(gb + i + 1, r1, 1);
+        __syncthreads();
+        // stage i+1 (LDS 1); r0 holds stage i+2; r1 is free
+        if (i + 3 < ng) fetch(gb + i + 3, r1);
+        mfma_stage(1);
+        if (i + 2 >= ng) break;
+        stash(gb + i + 2, r0, 0);
+        __syncthreads();
     }
 
     // ---- partial tile: lane holds rows 4*(lane/16) + v of column lane%16 ----
@@ -282,9 +285,9 @@ bool plan_wgrad_ig_bf16(const Geom &g, WgradBfPlan &p)
         const int lo = t * 128 / g.KK, hi = std::min(g.IC - 1, (std::min(N, t * 128 + 128) - 1) / g.KK);
         CCW = std::max(CCW, hi - lo + 1);
     }
+    if (g.HW < 8) return false;
     const int nblk = (g.HW + 7) / 8;
-    if (CCW * nblk > kXU * kWgNT) return false;
-    if (PP * 128 > kDU * kWgNT) return false;
+    if (2 * CCW * nblk > kWgNT) return false;
     const int HWP = nblk * 8;
     const size_t lds = 2 * (size_t(CCW) * HWP + size_t(PP) * 128) * 16;
     if (lds > 160 * 1024) return false;
@@ -310,7 +313,7 @@ hipError_t launch_wgrad_ig_bf16(const Geom &g, const WgradBfPlan &p, const void 
                                 const void *ym, void *dw, void *ws, int relu, hipStream_t s)
 {
     const WgradBfVariant *v = pick_wgrad_bf(p.NSTEP);
-    if (!v || p.CCW * p.nblk > kXU * kWgNT || p.PP * 128 > kDU * kWgNT || g.OC > 128)
+    if (!v || 2 * p.CCW * p.nblk > kWgNT || p.PP * 128 != p.NSTEP * kWgNT || g.OC > 128 || g.HW < 8)
         return hipErrorInvalidValue;
     uint4 *dzg = static_cast<uint4 *>(ws);
     float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + p.dz_bytes);
