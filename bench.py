@@ -46,7 +46,7 @@ PAGE1_US = {
     "layer2_bf16_b1024": (18.4427, 49.1440),
 }
 
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.md")
 
 
 def parse():
@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle leg")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="first run a device copy of this many MB (fp32 multiply by 1), the "
+                         "known-size reference for HBM byte counters")
     return ap.parse_args()
 
 
@@ -86,11 +89,14 @@ def source_digest():
 
 
 def measured_traffic(workload, op):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel sources; else None."""
+    """HBM bytes per call from the committed rocprofv3 counter summary (the
+    first ```json block of profiles/traffic.md), if it was taken on the
+    current kernel sources; else None."""
     try:
-        t = json.load(open(PROFILE_TRAFFIC))
-    except (OSError, ValueError):
+        text = open(PROFILE_TRAFFIC).read()
+        block = text.split("```json", 1)[1].split("```", 1)[0]
+        t = json.loads(block)
+    except (OSError, ValueError, IndexError):
         return None
     if t.get("source_digest") != source_digest():
         return None
@@ -310,6 +316,16 @@ def main():
               "(this library has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
     from backward_implicit_gemm_amd import inputs
+
+    if a.copy_probe_mb > 0:
+        import torch
+        n = a.copy_probe_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     names = [w.name for w in inputs.WORKLOADS]
     todo = names if a.all else [a.workload]
