@@ -1,0 +1,430 @@
+// dgrad_rf_f32.hip -- d_input, fp32 storage, fp32 MFMA (v_mfma_f32_16x16x4_f32),
+// image-group tiling, gather form (no atomics, each dx element written once).
+//
+// Same structure as the bf16 d_input kernel: a workgroup owns G whole images
+// (G a multiple of 4) and stages their masked output gradient dz once in LDS
+// as rows m = p*G + img by columns oc; every wave then holds the A fragments
+// of all its rows for the whole reduction over oc in registers (one fp32 per
+// row block and 4-channel step).  Input channels are walked in chunks of CC;
+// for each chunk the column gradient
+//     dcol[m][(icl,kh,kw)] = sum_oc dz[m][oc] * w[oc][c0+icl][kh][kw]
+// is formed by four MFMA waves splitting its 16-column blocks, while the other
+// four waves gather the previous chunk (see the kernel).  The weights are
+// pre-packed into B-fragment order -- [chunk][column block][16-oc step]
+// [lane] x 4 oc, 16 bytes per lane covering four MFMA steps -- and requested
+// one chunk ahead of their use.  dcol goes to LDS column by column and the
+// chunk's input gradient is gathered from it, four images per 16-byte read:
+//     dx[b][ic][ih][iw] = sum over the taps with oh*S+kh = ih, ow*S+kw = iw
+//                         of dcol[(oh,ow,b)][(ic,kh,kw)]
+// in fp32 in a fixed tap order and stored straight to dx (64 consecutive
+// pixels per store instruction).  dcol is double-buffered, so one barrier per
+// chunk separates its writers from its readers.
+// Only taps that land on an output position are multiplied (algorithmic MACs).
+#include "gc_kernels.h"
+#include "ig_common.h"
+
+namespace gc {
+namespace {
+
+// Packed weights, 16-byte units ((chunk*NBC + nbl)*KS4 + s)*64 + lane: column
+// n = nbl*16 + lane%16 of the chunk is (icl, kk) = (n / KK, n % KK), and the
+// unit holds w[16*s + 4*j + lane/16][chunk*CC + icl][kk] for j = 0..3 (the B
+// value of MFMA step 4*s + j), zero past OC, IC or the chunk's CC*KK columns.
+__global__ void __launch_bounds__(256) pack_w_dgrad_f32(const float *__restrict__ w,
+                                                        float4 *__restrict__ wp, Geom g, int CC,
+                                                        int NBC, int KS4, int total)
+{
+    for (int u = blockIdx.x * 256 + threadIdx.x; u < total; u += gridDim.x * 256) {
+        const int lane = u & 63;
+        int rest = u >> 6;
+        const int s4 = rest % KS4;
+        rest /= KS4;
+        const int nbl = rest % NBC;
+        const int chunk = rest / NBC;
+        const int n = nbl * 16 + (lane & 15);
+        const int icl = n / g.KK, kk = n - icl * g.KK;
+        const int ic = chunk * CC + icl;
+        const bool ok = icl < CC && ic < g.IC;
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int oc = 16 * s4 + 4 * j + (lane >> 4);
+            v[j] = (ok && oc < g.OC) ? w[(size_t(oc) * g.IC + ic) * g.KK + kk] : 0.f;
+        }
+        wp[u] = make_float4(v[0], v[1], v[2], v[3]);
+    }
+}
+
+struct DgradRfArgs {
+    Geom g;
+    const float *dy, *ym;
+    const float4 *wp;
+    float *dx;
+    int relu;
+    DgradBfPlan p;
+    FastDiv fd_ocp;    // OC*P: dz elements per image
+};
+
+__device__ __forceinline__ float comp(const float4 &v, int i)
+{
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// KS4 = OC/16 rounded up: 16-channel steps, each 4 MFMA steps of 4 channels.
+//
+// Roles: waves 0-3 (one per SIMD) run the MFMAs of chunk c while waves 4-7
+// gather chunk c-1 and store chunk c-2's dx tile, all between the same pair
+// of barriers, so the gather's LDS and VALU work hides under the MFMAs.
+template <int MB, int KS4, int TAPS, int NBW>
+__global__ void __launch_bounds__(512) dgrad_rf_f32(DgradRfArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint4 lds4[];
+    const Geom &g = a.g;
+    const DgradBfPlan &p = a.p;
+    constexpr int NT = 512, NMW = 4, NGT = 256;   // threads, MFMA waves, gather threads
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool mfma_role = wave < NMW;
+    const int G = p.G;
+    const int b0 = blockIdx.x * G;
+    const int gimg = min(G, g.B - b0);
+    const int c_begin = blockIdx.y * p.cpg;
+    const int c_end = min(c_begin + p.cpg, p.nchunks);
+
+    constexpr int KS = 4 * KS4;      // MFMA steps over oc
+    float *dz = reinterpret_cast<float *>(lds4);                               // [MB*16][OCP]
+    float *dcol = reinterpret_cast<float *>(reinterpret_cast<char *>(lds4) + p.dz_bytes);
+    const int dcol_buf = p.NBC * 16 * p.RP;                                    // [2][NBC*16][RP]
+    const int zrow = MB * 16;        // rows zrow .. zrow+G-1 of every dcol column stay zero
+
+    // Zero the dz tile (padding rows and channels past OC must read as 0)
+    // and the zero rows of dcol, which stand in for absent taps.
+    for (int i = tid; i < p.dz_bytes / 16; i += NT) lds4[i] = make_uint4(0, 0, 0, 0);
+    {
+        const int per_col = G / 4, n = 2 * p.NBC * 16 * per_col;
+        for (int i = tid; i < n; i += NT) {
+            const int col = i / per_col, k = i - col * per_col;
+            *reinterpret_cast<f32x4 *>(dcol + col * p.RP + zrow + 4 * k) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+
+    auto nbc_of = [&](int c) {
+        const int cc = min(p.CC, g.IC - c * p.CC);
+        return (cc * g.KK + 15) >> 4;
+    };
+
+    // dz: the group's gimg*OC*P contiguous elements of dy (and y), 4 per
+    // 16-byte load, all of a thread's loads in flight together; element
+    // e = (img, oc, p) goes to LDS row m = p*G + img, column oc.  With a ReLU
+    // the element is kept where y > 0.
+    __syncthreads();            // zero fill complete
+    {
+        const int n = gimg * g.OC * g.P;
+        const int n4 = n >> 2;
+        const uint32_t base = uint32_t(b0) * g.OC * g.P;
+        const int step = G * p.OCP;
+        auto put4 = [&](int e0, const float4 &v, const float4 &m, int cnt) {
+            uint32_t img, rem, oc, pp;
+            fdivmod(uint32_t(e0), a.fd_ocp, img, rem);
+            fdivmod(rem, g.fd_P, oc, pp);
+            int dst = (int(pp) * G + int(img)) * p.OCP + int(oc);
+            int ip = int(pp), ioc = int(oc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (i >= cnt) break;
+                float x = comp(v, i);
+                if (a.relu && !(comp(m, i) > 0.f)) x = 0.f;
+                dz[dst] = x;
+                // advance (img, oc, p) by one element in NCHW order
+                ++ip;
+                dst += step;
+                if (ip == g.P) {
+                    ip = 0;
+                    ++ioc;
+                    dst += 1 - g.P * step;
+                    if (ioc == g.OC) {
+                        ioc = 0;
+                        dst += 1 * p.OCP - g.OC;   // next image: row + 1, column 0
+                    }
+                }
+            }
+        };
+        constexpr int U = 4;
+        float4 dv[U], mv[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int u = tid + k * NT;
+            dv[k] = mv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (u < n4) {
+                dv[k] = ld4_f32(a.dy + base + 4 * u);
+                if (a.relu) mv[k] = ld4_f32(a.ym + base + 4 * u);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int u = tid + k * NT;
+            if (u < n4) put4(4 * u, dv[k], mv[k], 4);
+        }
+        for (int u = tid + U * NT; u < n4; u += NT) {
+            const float4 v = ld4_f32(a.dy + base + 4 * u);
+            const float4 m = a.relu ? ld4_f32(a.ym + base + 4 * u) : make_float4(0.f, 0.f, 0.f, 0.f);
+            put4(4 * u, v, m, 4);
+        }
+        if (tid == 0 && 4 * n4 < n) {
+            float tv[4] = {0.f, 0.f, 0.f, 0.f}, tm[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int e = 4 * n4; e < n; ++e) {
+                tv[e - 4 * n4] = a.dy[base + e];
+                tm[e - 4 * n4] = a.relu ? a.ym[base + e] : 0.f;
+            }
+            put4(4 * n4, make_float4(tv[0], tv[1], tv[2], tv[3]),
+                 make_float4(tm[0], tm[1], tm[2], tm[3]), n - 4 * n4);
+        }
+    }
+
+    // Gather role (threads 256..511): thread gt owns input pixel q of the
+    // (image quad, channel) planes r0, r0 + rpi, ...  Pixel (ih, iw) takes
+    // the taps oh*S + kh = ih, ow*S + kw = iw, i.e. oh in [oh_lo, oh_hi] and
+    // ow in [ow_lo, ow_hi]; their dcol offsets are fixed.  Unused tap slots
+    // point at the zero rows, so every thread issues the same TAPS reads.
+    const int gt = tid - NMW * 64;
+    const int rpi = NGT / g.HW;
+    const bool gthr = !mfma_role && gt < rpi * g.HW;
+    const int q = gthr ? gt % g.HW : 0;
+    const int r0 = gthr ? gt / g.HW : 0;
+    int toff[TAPS];
+    {
+        uint32_t ih, iw;
+        fdivmod(uint32_t(q), g.fd_W, ih, iw);
+        auto lo = [&](int i, int k) { return i - k + 1 <= 0 ? 0 : int(fdiv(uint32_t(i - k + g.S), g.fd_S)); };
+        const int oh_lo = lo(int(ih), g.KH), oh_hi = min(g.OH - 1, int(fdiv(ih, g.fd_S)));
+        const int ow_lo = lo(int(iw), g.KW), ow_hi = min(g.OW - 1, int(fdiv(iw, g.fd_S)));
+#pragma unroll
+        for (int j = 0; j < TAPS; ++j) toff[j] = zrow;
+        int j = 0;
+        for (int oh = oh_lo; oh <= oh_hi; ++oh)
+            for (int ow = ow_lo; ow <= ow_hi; ++ow, ++j) {
+                const int off = ((int(ih) - oh * g.S) * g.KW + int(iw) - ow * g.S) * p.RP +
+                                (oh * g.OW + ow) * G;
+#pragma unroll
+                for (int t = 0; t < TAPS; ++t)
+                    if (t == j) toff[t] = off;
+            }
+    }
+    __syncthreads();
+
+    // ---- MFMA role state ---------------------------------------------------
+    // A fragments of every row block and oc step, kept for the whole kernel:
+    // lane holds dz[mb*16 + lane%16][4*ks + lane/16].  Each MFMA wave owns
+    // column blocks nbl = wave and wave + 4 of every chunk; their weight
+    // fragments live in two register sets, bw0 and bw1, each refilled right
+    // after its MFMAs have read it, one block (96 MFMAs) ahead of its use.
+    float af[MB][KS];
+    float4 bw0[KS4], bw1[KS4];
+    auto block_ok = [&](int c, int j) { return wave + NMW * j < nbc_of(c); };
+    auto load_b = [&](float4 (&dst)[KS4], int c, int j) {
+        const float4 *src = a.wp + (uint32_t(c * p.NBC + wave + NMW * j) * KS4 * 64 + lane);
+#pragma unroll
+        for (int s = 0; s < KS4; ++s) dst[s] = src[s * 64];
+    };
+    auto mfma_block = [&](const float4 (&bb)[KS4], float *dbuf, int j) {
+        f32x4 acc[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[mb][ks], comp(bb[ks >> 2], ks & 3),
+                                                               acc[mb], 0, 0, 0);
+        // lane holds rows mb*16 + 4*(lane/16) + v of column nbl*16 + lane%16
+        const int nbl = wave + NMW * j;
+        float *dst = dbuf + (nbl * 16 + (lane & 15)) * p.RP + (lane >> 4) * 4;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) *reinterpret_cast<f32x4 *>(dst + mb * 16) = acc[mb];
+    };
+    if (mfma_role) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const float *row = dz + (mb * 16 + (lane & 15)) * p.OCP + (lane >> 4);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) af[mb][ks] = row[4 * ks];
+        }
+        if (c_begin < c_end && block_ok(c_begin, 0)) load_b(bw0, c_begin, 0);
+    }
+
+    // ---- gather role: sum the taps of 4 images per 16-byte read and store
+    // straight to dx; a store instruction covers 64 consecutive pixels of one
+    // plane, so the 4-byte stores coalesce without staging --------------------
+    const uint32_t plane = uint32_t(g.IC) * g.HW;     // dx elements per image
+    auto gather = [&](int c, const float *dbuf) {
+        if (!gthr) return;
+        const int c0 = c * p.CC;
+        const int cc = min(p.CC, g.IC - c0);
+        const int nplanes = cc * ((gimg + 3) >> 2);
+        int quad = 0, icl = r0;
+        while (icl >= cc) { icl -= cc; ++quad; }
+        for (int pl = r0; pl < nplanes; pl += rpi) {
+            const float *src = dbuf + icl * g.KK * p.RP + quad * 4;
+            f32x4 v[TAPS];
+#pragma unroll
+            for (int j = 0; j < TAPS; ++j) v[j] = *reinterpret_cast<const f32x4 *>(src + toff[j]);
+            f32x4 sum = v[0];
+#pragma unroll
+            for (int j = 1; j < TAPS; ++j) sum += v[j];
+            const int img0 = quad * 4;
+            float *o = a.dx + ((uint32_t(b0 + img0) * g.IC + uint32_t(c0 + icl)) * g.HW + q);
+            if (img0 + 4 <= gimg) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i * plane] = sum[i];
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (img0 + i < gimg) o[i * plane] = sum[i];
+            }
+            icl += rpi;
+            while (icl >= cc) { icl -= cc; ++quad; }
+        }
+    };
+
+    // ---- pipeline: iteration it computes chunk it and gathers chunk it-1;
+    // every dcol buffer changes hands at a barrier -----------------------------
+    for (int it = c_begin; it <= c_end; ++it) {
+        if (mfma_role) {
+            if (it < c_end) {
+                float *dbuf = dcol + ((it - c_begin) & 1) * dcol_buf;
+                const bool ok0 = block_ok(it, 0), ok1 = NBW > 1 && block_ok(it, 1);
+                if (ok1) load_b(bw1, it, 1);
+                if (ok0) mfma_block(bw0, dbuf, 0);
+                if (it + 1 < c_end && block_ok(it + 1, 0)) load_b(bw0, it + 1, 0);
+                if (ok1) mfma_block(bw1, dbuf, 1);
+            }
+        } else if (it > c_begin) {
+            gather(it - 1, dcol + ((it - 1 - c_begin) & 1) * dcol_buf);
+        }
+        __syncthreads();
+    }
+}
+
+struct DgradRfVariant {
+    int NW, MB, KS4, TAPS, NBW;
+    void (*fn)(DgradRfArgs);
+};
+
+#define DR_V(MB, KS4, TAPS, NBW) {8, MB, KS4, TAPS, NBW, dgrad_rf_f32<MB, KS4, TAPS, NBW>}
+#define DR_TAPS(MB, KS4) DR_V(MB, KS4, 2, 2), DR_V(MB, KS4, 4, 2), DR_V(MB, KS4, 9, 2)
+const DgradRfVariant kDgradRfVariants[] = {
+    DR_TAPS(1, 8), DR_TAPS(2, 8), DR_TAPS(3, 8),     // OC 113..128
+    DR_TAPS(1, 4), DR_TAPS(2, 4), DR_TAPS(3, 4),     // OC 49..64
+    DR_TAPS(1, 2), DR_TAPS(2, 2), DR_TAPS(3, 2),     // OC 17..32
+    DR_TAPS(1, 1), DR_TAPS(2, 1), DR_TAPS(3, 1),     // OC 1..16
+};
+#undef DR_TAPS
+#undef DR_V
+
+const DgradRfVariant *pick_dgrad_rf(int NW, int MB, int KS4, int TAPS, int NBW)
+{
+    for (const auto &v : kDgradRfVariants)
+        if (v.NW == NW && v.MB == MB && v.KS4 == KS4 && v.TAPS == TAPS && v.NBW == NBW) return &v;
+    return nullptr;
+}
+
+// Most taps any input pixel receives.
+int max_taps_rf(const Geom &g)
+{
+    int best = 0;
+    for (int ih = 0; ih < g.H; ++ih)
+        for (int iw = 0; iw < g.W; ++iw) {
+            int n = 0;
+            for (int oh = 0; oh < g.OH; ++oh) {
+                const int kh = ih - oh * g.S;
+                if (kh < 0 || kh >= g.KH) continue;
+                for (int ow = 0; ow < g.OW; ++ow) {
+                    const int kw = iw - ow * g.S;
+                    if (kw >= 0 && kw < g.KW) ++n;
+                }
+            }
+            best = std::max(best, n);
+        }
+    return best;
+}
+
+}  // namespace
+
+// Four MFMA waves take up to two column blocks each per chunk (NBC <= 8); the
+// chunk time is the longer of their MFMA work and the gather waves' work.
+// MB*KS fragments stay in registers, so MB is capped at 3 for 128 channels.
+bool plan_dgrad_rf_f32(const Geom &g, DgradBfPlan &p)
+{
+    constexpr int NW = 8, NGT = 256;
+    if (g.HW > NGT || g.P > 16) return false;
+    const int ks4 = (g.OC + 15) / 16;
+    const int KS4 = ks4 <= 1 ? 1 : ks4 <= 2 ? 2 : ks4 <= 4 ? 4 : ks4 <= 8 ? 8 : 0;
+    if (!KS4) return false;
+    const int mt = max_taps_rf(g);
+    const int TAPS = mt <= 2 ? 2 : mt <= 4 ? 4 : mt <= 9 ? 9 : 0;
+    if (!TAPS) return false;
+    const int rpi = NGT / g.HW;
+    double best = 1e30;
+    bool found = false;
+    for (int G = 4; G <= 64; G += 4) {
+        const int MB = (G * g.P + 15) / 16;
+        if (MB > 3) break;
+        if (G > 4 && G - 4 >= g.B) break;
+        const int OCP = 16 * KS4 + 4;     // A-fragment reads: bank 4*row + lane/16, no conflicts
+        const int RP = MB * 16 + G + (((G / 4) & 1) ? 0 : 4);
+        const size_t dz_bytes = size_t(MB) * 16 * OCP * 4;
+        const int ngroups = (g.B + G - 1) / G;
+        for (int CC = 1; CC <= g.IC; ++CC) {
+            const int NBC = (CC * g.KK + 15) / 16;
+            if (NBC > 8) break;
+            const int NBW = 2;
+            const size_t lds = dz_bytes + 2 * size_t(NBC) * 16 * RP * 4;
+            if (lds > 160 * 1024) break;
+            const int nchunks = (g.IC + CC - 1) / CC;
+            int cgroups = 1;
+            while (ngroups * cgroups < 256 && cgroups < nchunks) ++cgroups;
+            const int cpg = (nchunks + cgroups - 1) / cgroups;
+            cgroups = (nchunks + cpg - 1) / cpg;
+            const double mfma = double((NBC + 3) / 4) * MB * 4 * KS4 * 32;
+            const double passes = double((CC * (G / 4) + rpi - 1) / rpi);
+            const double gather = passes * 4 * (mt * 16.0 + 40.0) + 600.0;
+            const double chunk = std::max(mfma, gather) + 300.0;
+            const double per_wg = cpg * chunk + 2500.0;
+            const double t = std::ceil(double(ngroups) * cgroups / 256.0) * per_wg;
+            if (t < best - 1e-9) {
+                if (!pick_dgrad_rf(NW, MB, KS4, TAPS, NBW)) continue;
+                best = t;
+                p.NW = NW; p.G = G; p.MB = MB; p.KS = KS4; p.TAPS = TAPS; p.NBW = NBW; p.GP = 0;
+                p.CC = CC; p.NBC = NBC; p.nchunks = nchunks; p.cgroups = cgroups; p.cpg = cpg;
+                p.RP = RP; p.OCP = OCP; p.dz_bytes = int(dz_bytes); p.ORUN = 0;
+                p.lds = lds;
+                p.ws_bytes = size_t(nchunks) * NBC * KS4 * 64 * 16;
+                found = true;
+            }
+        }
+    }
+    return found;
+}
+
+hipError_t launch_dgrad_rf_f32(const Geom &g, const DgradBfPlan &p, const void *dy, const void *w,
+                               const void *ym, void *dx, void *ws, int relu, hipStream_t s)
+{
+    const DgradRfVariant *v = pick_dgrad_rf(p.NW, p.MB, p.KS, p.TAPS, p.NBW);
+    if (!v || p.NW != 8 || g.HW > 256 || p.G % 4 || p.G * g.P > 16 * p.MB || p.NBC > 4 * p.NBW ||
+        p.RP < 16 * p.MB + p.G)
+        return hipErrorInvalidValue;
+    const int total = p.nchunks * p.NBC * p.KS * 64;
+    if (size_t(total) * 16 > p.ws_bytes) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pack_w_dgrad_f32, dim3(std::min((total + 255) / 256, 2048)), dim3(256), 0, s,
+                       (const float *)w, (float4 *)ws, g, p.CC, p.NBC, p.KS, total);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    DgradRfArgs a{g, (const float *)dy, (const float *)ym, (const float4 *)ws, (float *)dx, relu, p,
+                  make_fastdiv(g.OC * g.P)};
+    e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
+    if (e != hipSuccess) return e;
+    dim3 grid((g.B + p.G - 1) / p.G, p.cgroups);
+    hipLaunchKernelGGL(v->fn, grid, dim3(64 * p.NW), p.lds, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace gc

@@ -6,6 +6,7 @@
 
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 
 #include "../../include/gc.h"
 #include "gc_kernels.h"
@@ -53,10 +54,11 @@ bool use_ig() { return g_policy.load(std::memory_order_relaxed) == GC_POLICY_AUT
 
 // Plans depend only on the geometry, and some take a search (the bf16
 // forward's LDS pitch) that costs far more host time than a launch, so each
-// planner's answers are kept per geometry.  Thread-safe; a full table
-// overwrites its entries round-robin.
-template <typename P>
-bool cached_plan(const Geom &g, bool (*planner)(const Geom &, P &), P &out)
+// planner's answers are kept per geometry, one table per planner (two
+// planners may share a plan type).  Thread-safe; a full table overwrites its
+// entries round-robin.
+template <typename P, bool (*Planner)(const Geom &, P &)>
+bool cached_plan(const Geom &g, P &out)
 {
     struct Entry {
         int key[8];
@@ -77,7 +79,7 @@ bool cached_plan(const Geom &g, bool (*planner)(const Geom &, P &), P &out)
             }
     }
     P p{};
-    const bool ok = planner(g, p);
+    const bool ok = Planner(g, p);
     std::lock_guard<std::mutex> lk(m);
     Entry &e = table[used < kSlots ? used++ : (next++ % kSlots)];
     std::copy(key, key + 8, e.key);
@@ -89,27 +91,31 @@ bool cached_plan(const Geom &g, bool (*planner)(const Geom &, P &), P &out)
 
 bool fwd_f32_plan(const Geom &g, FwdIgPlan &p)
 {
-    return use_ig() && cached_plan(g, plan_fwd_ig_f32, p);
+    return use_ig() && cached_plan<std::remove_reference_t<decltype(p)>, plan_fwd_ig_f32>(g, p);
 }
 bool fwd_bf16_plan(const Geom &g, FwdBfPlan &p)
 {
-    return use_ig() && cached_plan(g, plan_fwd_ig_bf16, p);
+    return use_ig() && cached_plan<std::remove_reference_t<decltype(p)>, plan_fwd_ig_bf16>(g, p);
 }
 bool dgrad_bf16_plan(const Geom &g, DgradBfPlan &p)
 {
-    return use_ig() && cached_plan(g, plan_dgrad_ig_bf16, p);
+    return use_ig() && cached_plan<std::remove_reference_t<decltype(p)>, plan_dgrad_ig_bf16>(g, p);
+}
+bool dgrad_f32_rf_plan(const Geom &g, DgradBfPlan &p)
+{
+    return use_ig() && cached_plan<std::remove_reference_t<decltype(p)>, plan_dgrad_rf_f32>(g, p);
 }
 bool wgrad_bf16_plan(const Geom &g, WgradBfPlan &p)
 {
-    return use_ig() && cached_plan(g, plan_wgrad_ig_bf16, p);
+    return use_ig() && cached_plan<std::remove_reference_t<decltype(p)>, plan_wgrad_ig_bf16>(g, p);
 }
 bool dgrad_plan(const Geom &g, DgradIgPlan &p)
 {
-    return use_ig() && cached_plan(g, plan_dgrad_ig_f32, p);
+    return use_ig() && cached_plan<std::remove_reference_t<decltype(p)>, plan_dgrad_ig_f32>(g, p);
 }
 bool wgrad_plan(const Geom &g, WgradIgPlan &p)
 {
-    return use_ig() && cached_plan(g, plan_wgrad_ig_f32, p);
+    return use_ig() && cached_plan<std::remove_reference_t<decltype(p)>, plan_wgrad_ig_f32>(g, p);
 }
 
 // Number of fp32 partial tiles wgrad writes for this problem, and the plan
@@ -174,6 +180,7 @@ size_t gc_conv_workspace_bytes(int op, const gc_conv_desc *d, int dtype)
     case GC_OP_BWD_DATA: {
         DgradBfPlan p;
         if (dtype == GC_BF16 && dgrad_bf16_plan(g, p)) return p.ws_bytes;
+        if (dtype == GC_F32 && dgrad_f32_rf_plan(g, p)) return p.ws_bytes;
         return 0;
     }
     case GC_OP_BWD_WEIGHT: return wgrad_ws_bytes(g, dtype);
@@ -220,12 +227,15 @@ int gc_conv_bwd_data(const void *dy, const void *w, const void *y_mask, void *dx
         (y_mask && !aligned(y_mask, dtype)))
         return GC_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (dtype == GC_BF16) {
+    {
         DgradBfPlan bp;
-        if (dgrad_bf16_plan(g, bp)) {
+        const bool bf = dtype == GC_BF16 && dgrad_bf16_plan(g, bp);
+        const bool rf = !bf && dtype == GC_F32 && dgrad_f32_rf_plan(g, bp);
+        if (bf || rf) {
             if (!workspace || ws_bytes < bp.ws_bytes) return GC_ERR_WORKSPACE;
             if (reinterpret_cast<uintptr_t>(workspace) % 16) return GC_ERR_WORKSPACE;
-            return hip_status(launch_dgrad_ig_bf16(g, bp, dy, w, y_mask, dx, workspace, relu, s));
+            return hip_status(bf ? launch_dgrad_ig_bf16(g, bp, dy, w, y_mask, dx, workspace, relu, s)
+                                 : launch_dgrad_rf_f32(g, bp, dy, w, y_mask, dx, workspace, relu, s));
         }
     }
     DgradIgPlan p;

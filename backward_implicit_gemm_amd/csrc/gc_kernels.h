@@ -44,6 +44,11 @@ bool plan_fwd_ig_bf16(const Geom &g, FwdBfPlan &p);
 hipError_t launch_fwd_ig_bf16(const Geom &g, const FwdBfPlan &p, const void *x, const void *w,
                               void *y, void *ws, int relu, hipStream_t s);
 bool plan_dgrad_ig_bf16(const Geom &g, DgradBfPlan &p);
+// fp32 d_input with register-held dz fragments (dgrad_rf_f32.hip); the plan
+// struct is shared with the bf16 kernel, KS holding the 16-channel steps.
+bool plan_dgrad_rf_f32(const Geom &g, DgradBfPlan &p);
+hipError_t launch_dgrad_rf_f32(const Geom &g, const DgradBfPlan &p, const void *dy, const void *w,
+                               const void *ym, void *dx, void *ws, int relu, hipStream_t s);
 bool plan_wgrad_ig_bf16(const Geom &g, WgradBfPlan &p);
 // dz regrouping, the partial-tile kernel and the fixed-order reduction into dw
 hipError_t launch_wgrad_ig_bf16(const Geom &g, const WgradBfPlan &p, const void *x, const void *dy,

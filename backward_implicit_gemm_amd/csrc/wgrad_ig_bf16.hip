@@ -35,27 +35,60 @@ __device__ __forceinline__ uint4 ldg16(const u16 *p)
     return v;
 }
 
-// dzg unit ((bg*PP + p)*128 + oc) = 8 images of group bg at (oc, p), masked;
-// zero for positions >= P, channels >= OC and images >= B.
-__global__ void __launch_bounds__(256) dz_groups_bf16(const u16 *__restrict__ dy,
-                                                      const u16 *__restrict__ ym,
-                                                      uint4 *__restrict__ dzg, Geom g, int relu,
-                                                      int PP, int total)
+// dzg unit ((bg*PP + p)*128 + oc) = the 8 images of group bg at (oc, p),
+// masked; zero for positions >= P, channels >= OC and images >= B.  One
+// workgroup per group: the group's images are contiguous in dy and y
+// (8*OC*P elements each), so they are copied into LDS with 16-byte loads and
+// transposed there.
+constexpr int kDzNT = 256;
+constexpr int kDzChunks = 8;      // 16-byte loads per thread per tensor: 8*OC*P <= 8*256*8
+__global__ void __launch_bounds__(kDzNT) dz_groups_bf16(const u16 *__restrict__ dy,
+                                                        const u16 *__restrict__ ym,
+                                                        uint4 *__restrict__ dzg, Geom g, int relu,
+                                                        int PP)
 {
-    for (int u = blockIdx.x * 256 + threadIdx.x; u < total; u += gridDim.x * 256) {
-        const int oc = u & 127;
-        const int t = u >> 7;
-        const int p = t % PP;
-        const int bg = t / PP;
+    extern __shared__ __attribute__((aligned(16))) uint4 dz_lds[];
+    const int bg = blockIdx.x, tid = threadIdx.x;
+    const int nimg = min(8, g.B - bg * 8);
+    const int per = g.OC * g.P;                      // elements per image
+    const int m = nimg * per;                        // contiguous elements of the group
+    const uint32_t base = uint32_t(bg) * 8 * per;
+    u16 *sdy = reinterpret_cast<u16 *>(dz_lds);      // [8][per]
+    u16 *sym = sdy + 8 * per;
+    const int m8 = m >> 3;
+    uint4 vd[kDzChunks], vm[kDzChunks];
+#pragma unroll
+    for (int k = 0; k < kDzChunks; ++k) {
+        const int c = tid + k * kDzNT;
+        vd[k] = vm[k] = make_uint4(0, 0, 0, 0);
+        if (c < m8) {
+            vd[k] = ldg16(dy + base + 8 * c);
+            if (relu) vm[k] = ldg16(ym + base + 8 * c);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kDzChunks; ++k) {
+        const int c = tid + k * kDzNT;
+        if (c < m8) {
+            __builtin_memcpy(sdy + 8 * c, &vd[k], 16);
+            __builtin_memcpy(sym + 8 * c, &vm[k], 16);
+        }
+    }
+    for (int e = 8 * m8 + tid; e < m; e += kDzNT) {
+        sdy[e] = dy[base + e];
+        sym[e] = relu ? ym[base + e] : u16(0);
+    }
+    __syncthreads();
+    for (int u = tid; u < PP * 128; u += kDzNT) {
+        const int p = u >> 7, oc = u & 127;
         u16 v[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int b = bg * 8 + i;
             u16 d = 0;
-            if (p < g.P && oc < g.OC && b < g.B) {
-                const uint32_t e = (uint32_t(b) * g.OC + oc) * g.P + p;
-                d = dy[e];
-                if (relu && uint32_t(ym[e]) - 1u >= 0x7F80u) d = 0;   // keep where 0 < y <= +inf
+            if (i < nimg && p < g.P && oc < g.OC) {
+                const int e = i * per + oc * g.P + p;
+                d = sdy[e];
+                if (relu && uint32_t(sym[e]) - 1u >= 0x7F80u) d = 0;   // keep where 0 < y <= +inf
             }
             v[i] = d;
         }
@@ -64,7 +97,7 @@ __global__ void __launch_bounds__(256) dz_groups_bf16(const u16 *__restrict__ dy
         o.y = v[2] | (uint32_t(v[3]) << 16);
         o.z = v[4] | (uint32_t(v[5]) << 16);
         o.w = v[6] | (uint32_t(v[7]) << 16);
-        dzg[u] = o;
+        dzg[(uint32_t(bg) * PP + p) * 128 + oc] = o;
     }
 }
 
@@ -97,9 +130,15 @@ __global__ void __launch_bounds__(kWgNT) wgrad_ig_bf16(WgradBfArgs a)
     const int wm = wave & 1;          // output channels 64*wm .. +63
     const int wn = wave >> 1;         // columns 32*wn .. +31 of the tile
     const int N = g.K;                // IC*KH*KW columns
-    const int n0 = blockIdx.x * 128;
+    // Workgroups are dealt to the 8 XCDs round-robin by id; ids are laid out
+    // so that all column tiles of one split (one image range) share an XCD,
+    // whose L2 then serves that range's dz and x to every tile.
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int split = (slot / p.ncol) * 8 + xcd;
+    if (split >= p.splits) return;
+    const int n0 = (slot % p.ncol) * 128;
     const int c_lo = n0 / g.KK;
-    const int gb = blockIdx.y * p.gps;
+    const int gb = split * p.gps;
     const int ge = min(gb + p.gps, p.ngroups);
 
     const int xbuf = p.CCW * p.HWP;               // 16-byte units per x stage
@@ -235,7 +274,7 @@ __global__ void __launch_bounds__(kWgNT) wgrad_ig_bf16(WgradBfArgs a)
     }
 
     // ---- partial tile: lane holds rows 4*(lane/16) + v of column lane%16 ----
-    float *part = a.part + size_t(blockIdx.y) * g.OC * N;
+    float *part = a.part + size_t(split) * g.OC * N;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int n = n0 + 32 * wn + 16 * j + (lane & 15);
@@ -292,13 +331,16 @@ bool plan_wgrad_ig_bf16(const Geom &g, WgradBfPlan &p)
     const size_t lds = 2 * (size_t(CCW) * HWP + size_t(PP) * 128) * 16;
     if (lds > 160 * 1024) return false;
     const int ngroups = (g.B + 7) / 8;
-    // splits: enough workgroups to cover the CUs, few enough that the
-    // partial traffic stays small against the operand traffic
+    // splits: enough workgroups to cover the CUs, in multiples of 8 so the
+    // XCDs get equal shares, few enough that the partial traffic stays small
+    // against the operand traffic
     int splits = std::max(1, std::min(ngroups, (256 + ncol - 1) / ncol));
+    if (splits > 8) splits = splits / 8 * 8;
     const double part_bytes = double(g.OC) * N * 4;
     const double in_bytes = double(g.B) * g.IC * g.HW * 2;
-    const double budget = std::max(0.5 * in_bytes, 8.0 * 1024 * 1024);
-    while (splits > 1 && splits * part_bytes > budget) --splits;
+    const double budget = std::max(0.75 * in_bytes, 12.0 * 1024 * 1024);
+    while (splits > 8 && splits * part_bytes > budget) splits -= 8;
+    while (splits > 1 && splits <= 8 && splits * part_bytes > budget) --splits;
     const int gps = (ngroups + splits - 1) / splits;
     splits = (ngroups + gps - 1) / gps;
     p.NSTEP = NSTEP; p.PP = PP; p.CCW = CCW; p.nblk = nblk; p.HWP = HWP;
@@ -312,20 +354,25 @@ bool plan_wgrad_ig_bf16(const Geom &g, WgradBfPlan &p)
 hipError_t launch_wgrad_ig_bf16(const Geom &g, const WgradBfPlan &p, const void *x, const void *dy,
                                 const void *ym, void *dw, void *ws, int relu, hipStream_t s)
 {
+    hipError_t e;
     const WgradBfVariant *v = pick_wgrad_bf(p.NSTEP);
     if (!v || 2 * p.CCW * p.nblk > kWgNT || p.PP * 128 != p.NSTEP * kWgNT || g.OC > 128 || g.HW < 8)
         return hipErrorInvalidValue;
     uint4 *dzg = static_cast<uint4 *>(ws);
     float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + p.dz_bytes);
-    const int total = p.ngroups * p.PP * 128;
-    hipLaunchKernelGGL(dz_groups_bf16, dim3(std::min((total + 255) / 256, 4096)), dim3(256), 0, s,
-                       (const u16 *)dy, (const u16 *)ym, dzg, g, relu, p.PP, total);
-    hipError_t e = hipGetLastError();
+    const size_t dz_lds = size_t(2) * 8 * g.OC * g.P * sizeof(u16);
+    if (g.OC * g.P * 8 > kDzChunks * kDzNT * 8) return hipErrorInvalidValue;
+    e = allow_max_lds(reinterpret_cast<const void *>(&dz_groups_bf16));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(dz_groups_bf16, dim3(p.ngroups), dim3(kDzNT), dz_lds, s,
+                       (const u16 *)dy, (const u16 *)ym, dzg, g, relu, p.PP);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
     if (e != hipSuccess) return e;
     WgradBfArgs a{g, (const u16 *)x, dzg, part, p};
-    hipLaunchKernelGGL(v->fn, dim3(p.ncol, p.splits), dim3(kWgNT), p.lds, s, a);
+    const int slots = (p.splits + 7) / 8 * p.ncol;    // per XCD
+    hipLaunchKernelGGL(v->fn, dim3(8 * slots), dim3(kWgNT), p.lds, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_wgrad_reduce<bf16_t>(part, dw, p.splits, g.OC * g.K, s);

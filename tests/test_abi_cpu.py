@@ -120,19 +120,21 @@ def test_workspace_sizes_are_sane():
             else:
                 assert n <= 64 * d.OC * K * 4 + dz_bytes
         # packed weights for the bf16 forward and d_input kernels: a padded copy of w
-        for op in (gb.GC_OP_FWD, gb.GC_OP_BWD_DATA):
-            assert gb.gc_conv_workspace_bytes(op, d, gb.GC_F32) == 0
-            n = gb.gc_conv_workspace_bytes(op, d, gb.GC_BF16)
-            assert n == 0 or d.OC * K * 2 <= n <= 16 * max(d.OC, 32) * max(K, 64) * 2
+        assert gb.gc_conv_workspace_bytes(gb.GC_OP_FWD, d, gb.GC_F32) == 0
+        for op, dt, es in ((gb.GC_OP_FWD, gb.GC_BF16, 2), (gb.GC_OP_BWD_DATA, gb.GC_BF16, 2),
+                           (gb.GC_OP_BWD_DATA, gb.GC_F32, 4)):
+            n = gb.gc_conv_workspace_bytes(op, d, dt)
+            assert n == 0 or d.OC * K * es <= n <= 16 * max(d.OC, 32) * max(K, 64) * es
     assert gb.gc_conv_workspace_bytes(99, L1, 0) == 0
 
 
-def test_dgrad_workspace_errors():
-    need = gb.gc_conv_workspace_bytes(gb.GC_OP_BWD_DATA, L1, gb.GC_BF16)
+@pytest.mark.parametrize("dtype", [gb.GC_F32, gb.GC_BF16])
+def test_dgrad_workspace_errors(dtype):
+    need = gb.gc_conv_workspace_bytes(gb.GC_OP_BWD_DATA, L1, dtype)
     assert need > 0
-    assert _call("gc_conv_bwd_data", FAKE, FAKE, FAKE, FAKE, desc=L1, relu=1, dtype=gb.GC_BF16,
+    assert _call("gc_conv_bwd_data", FAKE, FAKE, FAKE, FAKE, desc=L1, relu=1, dtype=dtype,
                  ws=None, ws_bytes=0) == gb.GC_ERR_WORKSPACE
-    assert _call("gc_conv_bwd_data", FAKE, FAKE, FAKE, FAKE, desc=L1, relu=1, dtype=gb.GC_BF16,
+    assert _call("gc_conv_bwd_data", FAKE, FAKE, FAKE, FAKE, desc=L1, relu=1, dtype=dtype,
                  ws=FAKE, ws_bytes=need - 1) == gb.GC_ERR_WORKSPACE
 
 
