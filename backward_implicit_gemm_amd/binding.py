@@ -15,12 +15,12 @@ LIB_PATH = os.path.join(_HERE, "libgc.so")
 
 GC_OK, GC_ERR_INVALID_ARG, GC_ERR_UNSUPPORTED, GC_ERR_WORKSPACE, GC_ERR_HIP = range(5)
 GC_F32, GC_BF16 = 0, 1
-GC_OP_FWD, GC_OP_BWD_DATA, GC_OP_BWD_WEIGHT = 0, 1, 2
+GC_OP_FWD, GC_OP_BWD_DATA, GC_OP_BWD_WEIGHT, GC_OP_BWD_BIAS = 0, 1, 2, 3
 
 EXPORTED = (
     "gc_conv_out_dims", "gc_conv_workspace_bytes", "gc_conv_fwd", "gc_conv_bwd_data",
     "gc_conv_bwd_weight", "gc_status_string", "gc_fastdiv_selfcheck", "gc_version",
-    "gc_set_kernel_policy",
+    "gc_set_kernel_policy", "gc_conv_fwd_bias", "gc_conv_bwd_bias",
 )
 GC_POLICY_AUTO, GC_POLICY_GENERIC = 0, 1
 
@@ -54,6 +54,10 @@ def lib():
     L.gc_conv_workspace_bytes.restype = sz
     L.gc_conv_fwd.argtypes = [vp, vp, vp, vp, sz, dp, i, i, vp]
     L.gc_conv_fwd.restype = i
+    L.gc_conv_fwd_bias.argtypes = [vp, vp, vp, vp, vp, sz, dp, i, i, vp]
+    L.gc_conv_fwd_bias.restype = i
+    L.gc_conv_bwd_bias.argtypes = [vp, vp, vp, vp, sz, dp, i, i, vp]
+    L.gc_conv_bwd_bias.restype = i
     L.gc_conv_bwd_data.argtypes = [vp, vp, vp, vp, vp, sz, dp, i, i, vp]
     L.gc_conv_bwd_data.restype = i
     L.gc_conv_bwd_weight.argtypes = [vp, vp, vp, vp, vp, sz, dp, i, i, vp]
@@ -165,6 +169,29 @@ def gc_conv_fwd(x, w, y, relu, stride, workspace=None, stream=None):
     return y
 
 
+def gc_conv_fwd_bias(x, w, bias, y, relu, stride, workspace=None, stream=None):
+    """y = relu?(conv(x, w) + bias) via the C entry point gc_conv_fwd_bias."""
+    dt = _dtype_code(x)
+    desc = desc_from(x.shape, w.shape, stride)
+    wp, wn = _ws(workspace)
+    st = lib().gc_conv_fwd_bias(_dev(x, "x", dt), _dev(w, "w", dt), _dev(bias, "bias", dt),
+                                _dev(y, "y", dt), wp, wn, ctypes.byref(desc), int(relu), dt,
+                                _stream(stream))
+    _check("gc_conv_fwd_bias", st)
+    return y
+
+
+def gc_conv_bwd_bias(dy, y_mask, db, relu, x_shape, w_shape, stride, workspace, stream=None):
+    """db[oc] = sum of dy (masked by y_mask > 0 when relu) via gc_conv_bwd_bias."""
+    dt = _dtype_code(dy)
+    desc = desc_from(x_shape, w_shape, stride)
+    wp, wn = _ws(workspace)
+    st = lib().gc_conv_bwd_bias(_dev(dy, "dy", dt), _dev(y_mask, "y_mask", dt), _dev(db, "db", dt),
+                                wp, wn, ctypes.byref(desc), int(relu), dt, _stream(stream))
+    _check("gc_conv_bwd_bias", st)
+    return db
+
+
 def gc_conv_bwd_data(dy, w, y_mask, dx, relu, stride, workspace=None, stream=None):
     """dx from dy (masked by y_mask > 0 when relu) via gc_conv_bwd_data."""
     dt = _dtype_code(dy)
@@ -202,7 +229,7 @@ class Conv:
         OH, OW = gc_conv_out_dims(self.desc)
         self.y_shape = (x_shape[0], w_shape[0], OH, OW)
         self.ws = {op: workspace_for(op, self.desc, self.dt, device)
-                   for op in (GC_OP_FWD, GC_OP_BWD_DATA, GC_OP_BWD_WEIGHT)}
+                   for op in (GC_OP_FWD, GC_OP_BWD_DATA, GC_OP_BWD_WEIGHT, GC_OP_BWD_BIAS)}
 
     def fwd(self, x, w, y, stream=None):
         return gc_conv_fwd(x, w, y, self.relu, self.stride, self.ws[GC_OP_FWD], stream)
@@ -214,3 +241,10 @@ class Conv:
     def bwd_weight(self, x, dy, y, dw, stream=None):
         return gc_conv_bwd_weight(x, dy, y if self.relu else None, dw, self.relu, self.stride,
                                   self.ws[GC_OP_BWD_WEIGHT], stream)
+
+    def fwd_bias(self, x, w, bias, y, stream=None):
+        return gc_conv_fwd_bias(x, w, bias, y, self.relu, self.stride, self.ws[GC_OP_FWD], stream)
+
+    def bwd_bias(self, dy, y, db, stream=None):
+        return gc_conv_bwd_bias(dy, y if self.relu else None, db, self.relu, self.x_shape,
+                                self.w_shape, self.stride, self.ws[GC_OP_BWD_BIAS], stream)

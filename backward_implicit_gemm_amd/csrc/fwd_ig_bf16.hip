@@ -66,6 +66,7 @@ struct FwdBfArgs {
     Geom g;
     const u16 *x;
     const uint4 *wf;
+    const u16 *bias;
     u16 *y;
     int relu;
     int G;        // images per workgroup
@@ -248,6 +249,7 @@ __global__ void __launch_bounds__(64 * NW) fwd_ig_bf16(FwdBfArgs a)
                 uint32_t img, pp;
                 fdivmod(r, g.fd_P, img, pp);
                 float val = acc[mb][v];
+                if (a.bias) val += __uint_as_float(uint32_t(a.bias[n]) << 16);
                 if (a.relu && !(val > 0.f)) val = 0.f;
                 a.y[(size_t(b0 + int(img)) * g.OC + n) * g.P + int(pp)] = from_f32<bf16_t>(val);
             }
@@ -356,7 +358,7 @@ bool plan_fwd_ig_bf16(const Geom &g, FwdBfPlan &p)
 }
 
 hipError_t launch_fwd_ig_bf16(const Geom &g, const FwdBfPlan &p, const void *x, const void *w,
-                              void *y, void *ws, int relu, hipStream_t s)
+                              const void *bias, void *y, void *ws, int relu, hipStream_t s)
 {
     const FwdBfVariant *v = pick_fwd_bf(p.NW, p.MB, p.TS, p.NCG, p.G * p.nblk);
     if (!v) return hipErrorInvalidValue;
@@ -368,7 +370,7 @@ hipError_t launch_fwd_ig_bf16(const Geom &g, const FwdBfPlan &p, const void *x, 
                        (const u16 *)w, (uint4 *)ws, g, p.NCG, p.TS, total);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    FwdBfArgs a{g, (const u16 *)x, (const uint4 *)ws, (u16 *)y, relu, p.G, p.WP, p.IS, p.NCG, p.nblk};
+    FwdBfArgs a{g, (const u16 *)x, (const uint4 *)ws, (const u16 *)bias, (u16 *)y, relu, p.G, p.WP, p.IS, p.NCG, p.nblk};
     dim3 grid((g.B + p.G - 1) / p.G, (g.OC + 16 * p.NW - 1) / (16 * p.NW));
     e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
     if (e != hipSuccess) return e;

@@ -22,7 +22,7 @@ namespace {
 
 struct FwdIgArgs {
     Geom g;
-    const float *x, *w;
+    const float *x, *w, *bias;
     float *y;
     int relu;
     FwdIgPlan p;
@@ -210,6 +210,7 @@ __global__ void __launch_bounds__(64 * NW) fwd_ig_f32(FwdIgArgs a)
                 const int n = n0 + ncol0 + nb * 16;
                 if (n >= g.OC) continue;
                 float val = acc[mb][nb][v];
+                if (a.bias) val += a.bias[n];
                 if (a.relu && !(val > 0.f)) val = 0.f;
                 yrow[size_t(n) * g.P] = val;
             }
@@ -302,11 +303,11 @@ bool plan_fwd_ig_f32(const Geom &g, FwdIgPlan &p)
 }
 
 hipError_t launch_fwd_ig_f32(const Geom &g, const FwdIgPlan &p, const void *x, const void *w,
-                             void *y, int relu, hipStream_t s)
+                             const void *bias, void *y, int relu, hipStream_t s)
 {
     const FwdVariant *v = pick_fwd(p.NW, p.MB, p.KCH, p.XV, p.WV);
     if (!v || v->KS != p.KS || 4 * p.KS + 2 > p.KCHP) return hipErrorInvalidValue;
-    FwdIgArgs a{g, (const float *)x, (const float *)w, (float *)y, relu, p,
+    FwdIgArgs a{g, (const float *)x, (const float *)w, (const float *)bias, (float *)y, relu, p,
                 make_fastdiv(p.XCS / 4), make_fastdiv(p.KCH / 4)};
     dim3 grid((g.B + p.G - 1) / p.G, (g.OC + 16 * p.NW - 1) / (16 * p.NW));
     hipError_t e = allow_max_lds(reinterpret_cast<const void *>(v->fn));

@@ -184,33 +184,68 @@ size_t gc_conv_workspace_bytes(int op, const gc_conv_desc *d, int dtype)
         return 0;
     }
     case GC_OP_BWD_WEIGHT: return wgrad_ws_bytes(g, dtype);
+    case GC_OP_BWD_BIAS: return bias_grad_ws_bytes(g);
     default: return 0;
     }
 }
 
-int gc_conv_fwd(const void *x, const void *w, void *y, void *workspace, size_t ws_bytes,
-                const gc_conv_desc *d, int relu, int dtype, void *stream)
+static int conv_fwd(const void *x, const void *w, const void *bias, void *y, void *workspace,
+             size_t ws_bytes, const gc_conv_desc *d, int relu, int dtype, void *stream)
 {
     Geom g;
     int st = check_desc(d, &g);
     if (st != GC_OK) return st;
     if (!valid_dtype(dtype) || (relu != 0 && relu != 1)) return GC_ERR_INVALID_ARG;
     if (!x || !w || !y) return GC_ERR_INVALID_ARG;
-    if (!aligned(x, dtype) || !aligned(w, dtype) || !aligned(y, dtype)) return GC_ERR_INVALID_ARG;
+    if (!aligned(x, dtype) || !aligned(w, dtype) || !aligned(y, dtype) ||
+        (bias && !aligned(bias, dtype)))
+        return GC_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == GC_F32) {
         FwdIgPlan p;
         if (fwd_f32_plan(g, p))
-            return hip_status(launch_fwd_ig_f32(g, p, x, w, y, relu, s));
-        return hip_status(launch_fwd_generic<float>(g, x, w, y, relu, s));
+            return hip_status(launch_fwd_ig_f32(g, p, x, w, bias, y, relu, s));
+        return hip_status(launch_fwd_generic<float>(g, x, w, bias, y, relu, s));
     }
     FwdBfPlan p;
     if (fwd_bf16_plan(g, p)) {
         if (!workspace || ws_bytes < p.ws_bytes) return GC_ERR_WORKSPACE;
         if (reinterpret_cast<uintptr_t>(workspace) % 16) return GC_ERR_WORKSPACE;
-        return hip_status(launch_fwd_ig_bf16(g, p, x, w, y, workspace, relu, s));
+        return hip_status(launch_fwd_ig_bf16(g, p, x, w, bias, y, workspace, relu, s));
     }
-    return hip_status(launch_fwd_generic<bf16_t>(g, x, w, y, relu, s));
+    return hip_status(launch_fwd_generic<bf16_t>(g, x, w, bias, y, relu, s));
+}
+
+int gc_conv_fwd(const void *x, const void *w, void *y, void *workspace, size_t ws_bytes,
+                const gc_conv_desc *d, int relu, int dtype, void *stream)
+{
+    return conv_fwd(x, w, nullptr, y, workspace, ws_bytes, d, relu, dtype, stream);
+}
+
+int gc_conv_fwd_bias(const void *x, const void *w, const void *bias, void *y, void *workspace,
+                     size_t ws_bytes, const gc_conv_desc *d, int relu, int dtype, void *stream)
+{
+    if (!bias) return GC_ERR_INVALID_ARG;
+    return conv_fwd(x, w, bias, y, workspace, ws_bytes, d, relu, dtype, stream);
+}
+
+int gc_conv_bwd_bias(const void *dy, const void *y_mask, void *db, void *workspace,
+                     size_t ws_bytes, const gc_conv_desc *d, int relu, int dtype, void *stream)
+{
+    Geom g;
+    int st = check_desc(d, &g);
+    if (st != GC_OK) return st;
+    if (!valid_dtype(dtype) || (relu != 0 && relu != 1)) return GC_ERR_INVALID_ARG;
+    if (!dy || !db) return GC_ERR_INVALID_ARG;
+    if ((relu == 1) != (y_mask != nullptr)) return GC_ERR_INVALID_ARG;
+    if (!aligned(dy, dtype) || !aligned(db, dtype) || (y_mask && !aligned(y_mask, dtype)))
+        return GC_ERR_INVALID_ARG;
+    if (!workspace || ws_bytes < bias_grad_ws_bytes(g)) return GC_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 16) return GC_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float *part = static_cast<float *>(workspace);
+    return hip_status(dtype == GC_F32 ? launch_bias_grad<float>(g, dy, y_mask, db, part, relu, s)
+                                      : launch_bias_grad<bf16_t>(g, dy, y_mask, db, part, relu, s));
 }
 
 int gc_conv_bwd_data(const void *dy, const void *w, const void *y_mask, void *dx,

@@ -7,8 +7,8 @@ namespace gc {
 
 // Shape-generic implicit GEMM (igemm_generic.hip).
 template <typename T>
-hipError_t launch_fwd_generic(const Geom &g, const void *x, const void *w, void *y, int relu,
-                              hipStream_t s);
+hipError_t launch_fwd_generic(const Geom &g, const void *x, const void *w, const void *bias,
+                              void *y, int relu, hipStream_t s);
 template <typename T>
 hipError_t launch_dgrad_generic(const Geom &g, const void *dy, const void *w, const void *ym,
                                 void *dx, int relu, hipStream_t s);
@@ -26,7 +26,7 @@ struct DgradBfPlan;
 struct WgradBfPlan;
 bool plan_fwd_ig_f32(const Geom &g, FwdIgPlan &p);
 hipError_t launch_fwd_ig_f32(const Geom &g, const FwdIgPlan &p, const void *x, const void *w,
-                             void *y, int relu, hipStream_t s);
+                             const void *bias, void *y, int relu, hipStream_t s);
 // d_input and wgrad run on fp32 MFMA for both storage types (T = float or
 // bf16_t; bf16 is widened exactly while staging).
 bool plan_dgrad_ig_f32(const Geom &g, DgradIgPlan &p);
@@ -42,7 +42,13 @@ hipError_t launch_wgrad_ig(const Geom &g, const WgradIgPlan &p, const void *x, c
 struct FwdBfPlan;
 bool plan_fwd_ig_bf16(const Geom &g, FwdBfPlan &p);
 hipError_t launch_fwd_ig_bf16(const Geom &g, const FwdBfPlan &p, const void *x, const void *w,
-                              void *y, void *ws, int relu, hipStream_t s);
+                              const void *bias, void *y, void *ws, int relu, hipStream_t s);
+// Bias gradient db[oc] = sum over (b, oh, ow) of dz (bias_grad.hip): fp32
+// partials per image chunk in `part`, then the fixed-order reduction.
+size_t bias_grad_ws_bytes(const Geom &g);
+template <typename T>
+hipError_t launch_bias_grad(const Geom &g, const void *dy, const void *ym, void *db, float *part,
+                            int relu, hipStream_t s);
 bool plan_dgrad_ig_bf16(const Geom &g, DgradBfPlan &p);
 // fp32 d_input with register-held dz fragments (dgrad_rf_f32.hip); the plan
 // struct is shared with the bf16 kernel, KS holding the 16-channel steps.

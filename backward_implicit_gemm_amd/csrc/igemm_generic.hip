@@ -40,7 +40,7 @@ template <> struct Lds<bf16_t> { static constexpr int PAD = 8; };
 
 template <typename T>
 struct FwdOp {
-    Geom g; const T *x, *w; T *y; int relu;
+    Geom g; const T *x, *w, *bias; T *y; int relu;
     __device__ int M() const { return g.B * g.P; }
     __device__ int N() const { return g.OC; }
     __device__ int K() const { return g.K; }
@@ -67,6 +67,7 @@ struct FwdOp {
     __device__ void store(int m, int n, float v) const {
         uint32_t b, p;
         fdivmod(m, g.fd_P, b, p);
+        if (bias) v += to_f32(bias[n]);
         if (relu && !(v > 0.f)) v = 0.f;
         y[(int(b) * g.OC + n) * g.P + int(p)] = from_f32<T>(v);
     }
@@ -335,10 +336,10 @@ __global__ void __launch_bounds__(NT) wgrad_generic(WgradOp<T> op, int kspan)
 // ------------------------------------------------------------ launch ----
 
 template <typename T>
-hipError_t launch_fwd_generic(const Geom &g, const void *x, const void *w, void *y, int relu,
-                              hipStream_t s)
+hipError_t launch_fwd_generic(const Geom &g, const void *x, const void *w, const void *bias,
+                              void *y, int relu, hipStream_t s)
 {
-    FwdOp<T> op{g, (const T *)x, (const T *)w, (T *)y, relu};
+    FwdOp<T> op{g, (const T *)x, (const T *)w, (const T *)bias, (T *)y, relu};
     dim3 grid((g.B * g.P + TM - 1) / TM, (g.OC + TN - 1) / TN, 1);
     hipLaunchKernelGGL(fwd_generic<T>, grid, dim3(NT), 0, s, op);
     return hipGetLastError();
@@ -383,8 +384,10 @@ hipError_t launch_wgrad_generic(const Geom &g, const void *x, const void *dy, co
     return hipGetLastError();
 }
 
-template hipError_t launch_fwd_generic<float>(const Geom &, const void *, const void *, void *, int, hipStream_t);
-template hipError_t launch_fwd_generic<bf16_t>(const Geom &, const void *, const void *, void *, int, hipStream_t);
+template hipError_t launch_fwd_generic<float>(const Geom &, const void *, const void *, const void *,
+                                              void *, int, hipStream_t);
+template hipError_t launch_fwd_generic<bf16_t>(const Geom &, const void *, const void *, const void *,
+                                              void *, int, hipStream_t);
 template hipError_t launch_dgrad_generic<float>(const Geom &, const void *, const void *, const void *, void *, int, hipStream_t);
 template hipError_t launch_dgrad_generic<bf16_t>(const Geom &, const void *, const void *, const void *, void *, int, hipStream_t);
 template hipError_t launch_wgrad_generic<float>(const Geom &, const void *, const void *, const void *, float *, int, int, hipStream_t);

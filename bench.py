@@ -199,7 +199,35 @@ def run_gpu(wl, steps, warmup):
         torch.cuda.synchronize()
         per_call[name] = start.elapsed_time(end) / (replays * reps) * 1e3
         del g
-    return ms_step, ms_eager, per_call
+
+    # The bias entry points (forward with a bias, bias gradient), timed the
+    # same way; not part of the step.
+    bias_calls = []
+    for i, c in enumerate(convs):
+        L = layers[i]
+        bound = 1.0 / (L.IC * L.KH * L.KW) ** 0.5
+        b = inputs.uniform((L.OC,), 900 + i, bound, wl.dtype).to(dev)
+        db = torch.empty_like(b)
+        yb = torch.empty_like(ys[i])
+        bias_calls.append((f"fwd_bias{i + 1}", lambda c=c, i=i, b=b, yb=yb: c.fwd_bias(xs[i], ws[i], b, yb)))
+        bias_calls.append((f"bwd_bias{i + 1}", lambda c=c, i=i, db=db: c.bwd_bias(dys[i], ys[i], db)))
+    bias_us = {}
+    for name, f in bias_calls:
+        f()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                f()
+        g.replay()
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(replays):
+            g.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        bias_us[name] = start.elapsed_time(end) / (replays * reps) * 1e3
+        del g
+    return ms_step, ms_eager, per_call, bias_us
 
 
 def cpu_baseline(wl, budget_s):
@@ -247,7 +275,7 @@ CALL_KERNELS = {
               "bf16": ["dz_groups_bf16", "wgrad_ig_bf16", "wgrad_reduce"]},
 }
 
-def report(wl, ms_step, ms_eager, per_call, steps, warmup, cpu):
+def report(wl, ms_step, ms_eager, per_call, bias_us, steps, warmup, cpu):
     L0 = wl.layers[0]
     esize = 4 if wl.dtype == "f32" else 2
     flops_step = sum(3 * layer_flops(L) for L in wl.layers)
@@ -301,6 +329,7 @@ def report(wl, ms_step, ms_eager, per_call, steps, warmup, cpu):
         "tflops": {"fwd": round(sum(layer_flops(L) for L in wl.layers) / (fwd_us * 1e-6) / 1e12, 3),
                    "bwd": round(sum(2 * layer_flops(L) for L in wl.layers) / (bwd_us * 1e-6) / 1e12, 3)},
         "roofline": roof,
+        "bias_us_per_call": {k: round(v, 3) for k, v in bias_us.items()},
         "cpu_baseline": cpu,
     }
     if vs is not None:
@@ -334,11 +363,11 @@ def main():
             print(f"unknown workload {name}; choose from {names}", file=sys.stderr)
             sys.exit(2)
         wl = inputs.WORKLOADS[names.index(name)]
-        ms, ms_eager, per_call = run_gpu(wl, a.steps, a.warmup)
+        ms, ms_eager, per_call, bias_us = run_gpu(wl, a.steps, a.warmup)
         cpu = None
         if not a.no_cpu and name == DEFAULT_WORKLOAD:
             cpu = cpu_baseline(wl, a.cpu_seconds)
-        print(json.dumps(report(wl, ms, ms_eager, per_call, a.steps, a.warmup, cpu)), flush=True)
+        print(json.dumps(report(wl, ms, ms_eager, per_call, bias_us, a.steps, a.warmup, cpu)), flush=True)
 
 
 if __name__ == "__main__":

@@ -8,8 +8,11 @@
  * layer-2 benchmark lines), and a backward pass that produces the weight
  * gradient ("wgrad") and the input gradient ("d_input"), in fp32 or bf16
  * (its precision=fp32 / precision=bf16 runs).  Stride S, no padding, dilation
- * 1, one group, no bias.  Output size: OH = (H-KH)/S + 1, OW = (W-KW)/S + 1
- * (integer division; the page's layer 1 maps 11x15, K=5, S=3 to 3x4).
+ * 1, one group.  Output size: OH = (H-KH)/S + 1, OW = (W-KW)/S + 1 (integer
+ * division; the page's layer 1 maps 11x15, K=5, S=3 to 3x4).  The same page
+ * also times a separate bias-gradient kernel for these layers; the bias
+ * entry points below add a per-channel bias to the forward pass and compute
+ * its gradient.
  *
  *   y [b,oc,oh,ow] = f( sum_{ic,kh,kw} x[b,ic,oh*S+kh,ow*S+kw] * w[oc,ic,kh,kw] )
  *   dz             = relu ? dy * (y > 0) : dy          (derivative 0 at 0)
@@ -40,7 +43,8 @@
  *     enqueued when an error is returned before the launch.
  *   - Every element count (B*IC*H*W, B*OC*OH*OW, OC*IC*KH*KW) must be below
  *     2^31; larger tensors are rejected with GC_ERR_INVALID_ARG.
- *   - Entry points are reentrant and keep no state between calls.
+ *   - Entry points are reentrant.  The only state is an internal,
+ *     thread-safe cache of kernel plans per problem shape.
  */
 #ifndef GC_H
 #define GC_H
@@ -62,7 +66,12 @@ typedef enum {
 
 typedef enum { GC_F32 = 0, GC_BF16 = 1 } gc_dtype;
 
-typedef enum { GC_OP_FWD = 0, GC_OP_BWD_DATA = 1, GC_OP_BWD_WEIGHT = 2 } gc_op;
+typedef enum {
+    GC_OP_FWD = 0,          /* gc_conv_fwd and gc_conv_fwd_bias */
+    GC_OP_BWD_DATA = 1,     /* gc_conv_bwd_data */
+    GC_OP_BWD_WEIGHT = 2,   /* gc_conv_bwd_weight */
+    GC_OP_BWD_BIAS = 3      /* gc_conv_bwd_bias */
+} gc_op;
 
 /* Problem size.  No padding, dilation 1, one group. */
 typedef struct {
@@ -85,6 +94,22 @@ size_t gc_conv_workspace_bytes(int op, const gc_conv_desc *d, int dtype);
 int gc_conv_fwd(const void *x, const void *w, void *y,
                 void *workspace, size_t ws_bytes,
                 const gc_conv_desc *d, int relu, int dtype, void *stream);
+
+/* Forward pass with a bias: y = f(conv(x, w) + bias[oc]).  bias [OC] has the
+ * storage type and is added in fp32 before the ReLU; everything else is as in
+ * gc_conv_fwd (same workspace size).  bias must not be NULL. */
+int gc_conv_fwd_bias(const void *x, const void *w, const void *bias, void *y,
+                     void *workspace, size_t ws_bytes,
+                     const gc_conv_desc *d, int relu, int dtype, void *stream);
+
+/* Bias gradient: db[oc] = sum_{b,oh,ow} dz[b,oc,oh,ow], dz = dy masked by
+ * (y_mask > 0) when relu == 1 (y_mask NULL when relu == 0).  db [OC] out.
+ * Summed in fp32 in two stages whose order is fixed by the shape (partials
+ * per chunk of images in `workspace`, then an ordered sum), so the result is
+ * bit-identical from run to run. */
+int gc_conv_bwd_bias(const void *dy, const void *y_mask, void *db,
+                     void *workspace, size_t ws_bytes,
+                     const gc_conv_desc *d, int relu, int dtype, void *stream);
 
 /* d_input: dx from dy and w.  With relu == 1, dy is masked by (y_mask > 0),
  * y_mask being the forward output y; y_mask must be NULL when relu == 0.

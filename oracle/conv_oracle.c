@@ -24,7 +24,8 @@
  *   - ReLU: y = pre if pre > 0 else 0; its derivative is taken as 0 at 0, so
  *     the backward mask is (y_mask > 0) strictly, where y_mask is the forward
  *     output handed in by the caller (not recomputed here);
- *   - no bias term.
+ *   - the plain passes have no bias; the *_bias functions add the bias
+ *     forward and its gradient (see there).
  *
  * Layouts: x is NCHW [B][IC][H][W], w is OIHW [OC][IC][KH][KW], y/dy are NCHW
  * [B][OC][OH][OW].  All arrays are fp64.  OpenMP splits only over independent
@@ -143,6 +144,49 @@ void oracle_conv_bwd_weight(const double *x, const double *dy, const double *y_m
                                  * x[idx4(b, IC, ic, H, oh * S + kh, W, ow * S + kw)];
                 dw[idx4(oc, IC, ic, KH, kh, KW, kw)] = acc;
             }
+    }
+}
+
+/*
+ * Bias.  The same page times a separate per-channel bias-gradient kernel for
+ * these two layers at the encoder's batch (its bias-grad timing lines); the
+ * layer then reads y = f(conv(x, w) + bias[oc]).  Forward with a bias, and
+ * the bias gradient db[oc] = sum_{b,oh,ow} dz[b,oc,oh,ow] (dz the
+ * ReLU-masked dy, as above).  d_input and wgrad do not change with a bias.
+ */
+void oracle_conv_fwd_bias(const double *x, const double *w, const double *bias, double *y,
+                          int B, int IC, int H, int W, int OC, int KH, int KW,
+                          int S, int relu)
+{
+    const int OH = oracle_out_dim(H, KH, S), OW = oracle_out_dim(W, KW, S);
+    if (OH < 1 || OW < 1) return;
+#pragma omp parallel for schedule(static)
+    for (i64 b = 0; b < B; ++b)
+        for (int oc = 0; oc < OC; ++oc)
+            for (int oh = 0; oh < OH; ++oh)
+                for (int ow = 0; ow < OW; ++ow) {
+                    double acc = bias[oc];
+                    for (int ic = 0; ic < IC; ++ic)
+                        for (int kh = 0; kh < KH; ++kh)
+                            for (int kw = 0; kw < KW; ++kw)
+                                acc += x[idx4(b, IC, ic, H, oh * S + kh, W, ow * S + kw)]
+                                     * w[idx4(oc, IC, ic, KH, kh, KW, kw)];
+                    if (relu && !(acc > 0.0)) acc = 0.0;
+                    y[idx4(b, OC, oc, OH, oh, OW, ow)] = acc;
+                }
+}
+
+void oracle_conv_bwd_bias(const double *dy, const double *y_mask, double *db,
+                          int B, int OC, int OH, int OW, int relu)
+{
+#pragma omp parallel for schedule(static)
+    for (int oc = 0; oc < OC; ++oc) {
+        double acc = 0.0;
+        for (i64 b = 0; b < B; ++b)
+            for (int oh = 0; oh < OH; ++oh)
+                for (int ow = 0; ow < OW; ++ow)
+                    acc += masked_dy(dy, y_mask, relu, idx4(b, OC, oc, OH, oh, OW, ow));
+        db[oc] = acc;
     }
 }
 

@@ -75,8 +75,11 @@ def _bind(lib):
     lib.oracle_conv_fwd_at.argtypes = [dp, dp, ip, i, dp] + dims
     lib.oracle_conv_bwd_data_at.argtypes = [dp, dp, dp, ip, i, dp] + dims
     lib.oracle_conv_bwd_weight_at.argtypes = [dp, dp, dp, ip, i, dp] + dims
+    lib.oracle_conv_fwd_bias.argtypes = [dp, dp, dp, dp] + dims
+    lib.oracle_conv_bwd_bias.argtypes = [dp, dp, dp, i, i, i, i, i]
     for f in ("oracle_conv_fwd", "oracle_conv_bwd_data", "oracle_conv_bwd_weight",
-              "oracle_conv_fwd_at", "oracle_conv_bwd_data_at", "oracle_conv_bwd_weight_at"):
+              "oracle_conv_fwd_at", "oracle_conv_bwd_data_at", "oracle_conv_bwd_weight_at",
+              "oracle_conv_fwd_bias", "oracle_conv_bwd_bias"):
         getattr(lib, f).restype = None
     return lib
 
@@ -120,6 +123,28 @@ def conv_fwd(x, w, stride, relu):
     _load().oracle_conv_fwd(_ptr(x), _ptr(w), _ptr(y), B, IC, H, W, OC, KH, KW,
                             int(stride), int(bool(relu)))
     return y
+
+
+def conv_fwd_bias(x, w, bias, stride, relu):
+    """y = f(conv(x, w) + bias[oc]), fp64; bias has OC entries."""
+    x, w, bias = _f64(x), _f64(w), _f64(bias)
+    B, IC, H, W, OC, KH, KW, OH, OW = _dims(x.shape, w.shape, stride)
+    if bias.shape != (OC,):
+        raise ValueError("bias shape mismatch")
+    y = np.empty((B, OC, OH, OW), np.float64)
+    _load().oracle_conv_fwd_bias(_ptr(x), _ptr(w), _ptr(bias), _ptr(y), B, IC, H, W, OC, KH, KW,
+                                 int(stride), int(bool(relu)))
+    return y
+
+
+def conv_bwd_bias(dy, y_mask, relu):
+    """db[oc] = sum over (b, oh, ow) of dy, masked by (y_mask > 0) when relu."""
+    dy = _f64(dy)
+    B, OC, OH, OW = (int(v) for v in dy.shape)
+    m = _mask_arg(y_mask, relu, dy.shape)
+    db = np.empty((OC,), np.float64)
+    _load().oracle_conv_bwd_bias(_ptr(dy), _ptr(m), _ptr(db), B, OC, OH, OW, int(bool(relu)))
+    return db
 
 
 def _mask_arg(y_mask, relu, shape):

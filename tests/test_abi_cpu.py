@@ -138,6 +138,33 @@ def test_dgrad_workspace_errors(dtype):
                  ws=FAKE, ws_bytes=need - 1) == gb.GC_ERR_WORKSPACE
 
 
+def test_bias_argument_errors():
+    lib = gb.lib()
+    d = L1
+    # fwd_bias needs a bias pointer; the rest is validated as for gc_conv_fwd
+    assert lib.gc_conv_fwd_bias(FAKE, FAKE, None, FAKE, None, 0, ctypes.byref(d), 1, 0,
+                                None) == gb.GC_ERR_INVALID_ARG
+    odd = ctypes.c_void_p(0x10002)
+    assert lib.gc_conv_fwd_bias(FAKE, FAKE, odd, FAKE, None, 0, ctypes.byref(d), 1, gb.GC_F32,
+                                None) == gb.GC_ERR_INVALID_ARG
+    assert gb.gc_conv_workspace_bytes(gb.GC_OP_FWD, d, gb.GC_BF16) > 0
+    assert lib.gc_conv_fwd_bias(FAKE, FAKE, FAKE, FAKE, None, 0, ctypes.byref(d), 1, gb.GC_BF16,
+                                None) == gb.GC_ERR_WORKSPACE
+    # bwd_bias: the mask must match relu; null outputs and bad flags are rejected
+    def bb(dy, m, db, relu, dt, desc=d, ws=FAKE, wn=1 << 30):
+        return lib.gc_conv_bwd_bias(dy, m, db, ws, wn, ctypes.byref(desc), relu, dt, None)
+    assert bb(FAKE, None, FAKE, 1, 0) == gb.GC_ERR_INVALID_ARG
+    assert bb(FAKE, FAKE, FAKE, 0, 0) == gb.GC_ERR_INVALID_ARG
+    assert bb(FAKE, FAKE, None, 1, 0) == gb.GC_ERR_INVALID_ARG
+    assert bb(FAKE, FAKE, FAKE, 2, 0) == gb.GC_ERR_INVALID_ARG
+    assert bb(FAKE, FAKE, FAKE, 1, 5) == gb.GC_ERR_INVALID_ARG
+    assert bb(FAKE, None, FAKE, 0, 0, desc=gb.make_desc(1, 1, 2, 2, 1, 3, 3, 1)) == gb.GC_ERR_INVALID_ARG
+    need = gb.gc_conv_workspace_bytes(gb.GC_OP_BWD_BIAS, d, gb.GC_F32)
+    assert need >= d.OC * 4
+    assert bb(FAKE, FAKE, FAKE, 1, 0, ws=None, wn=0) == gb.GC_ERR_WORKSPACE
+    assert bb(FAKE, FAKE, FAKE, 1, 0, wn=need - 1) == gb.GC_ERR_WORKSPACE
+
+
 def test_status_strings():
     for s in range(5):
         assert gb.status_string(s).startswith("GC_")

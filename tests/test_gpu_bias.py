@@ -1,0 +1,121 @@
+"""GPU parity for the bias entry points (gc_conv_fwd_bias, gc_conv_bwd_bias)
+against the oracle's forward-with-bias and bias gradient.
+
+The bias is drawn like the weights, U(+-1/sqrt(IC*KH*KW)).  The bias
+gradient of each layer takes the GPU's own forward output as its ReLU mask,
+as the other backward passes do.
+"""
+import numpy as np
+import pytest
+import torch
+
+from backward_implicit_gemm_amd import binding as gb
+from backward_implicit_gemm_amd import inputs
+from oracle import oracle as orc
+
+from parity import TOL, Layer, draw, f64, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    gb.lib()
+
+
+def _bias(layer, seed, dtype):
+    bound = 1.0 / np.sqrt(layer.IC * layer.KH * layer.KW)
+    return inputs.uniform((layer.OC,), seed, bound, dtype)
+
+
+def _run(layer, dtype, x, w, b, dy):
+    dev = "cuda"
+    td = inputs.torch_dtype(dtype)
+    conv = gb.Conv(layer.x_shape, layer.w_shape, layer.stride, layer.relu, td, dev)
+    xd, wd, bd, dyd = (t.to(dev) for t in (x, w, b, dy))
+    y = torch.full(layer.y_shape, float("nan"), dtype=td, device=dev)
+    db = torch.full((layer.OC,), float("nan"), dtype=td, device=dev)
+    conv.fwd_bias(xd, wd, bd, y)
+    conv.bwd_bias(dyd, y, db)
+    torch.cuda.synchronize()
+    return conv, y, db
+
+
+def _check(layer, dtype, x, w, b, dy):
+    conv, y, db = _run(layer, dtype, x, w, b, dy)
+    y_ref = orc.conv_fwd_bias(f64(x), f64(w), f64(b), layer.stride, layer.relu)
+    db_ref = orc.conv_bwd_bias(f64(dy), f64(y), layer.relu)
+    ey, eb = rel_err(f64(y), y_ref), rel_err(f64(db), db_ref)
+    assert ey <= TOL[dtype] and eb <= TOL[dtype], (ey, eb)
+    return ey, eb, y, db
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3], ids=[w.name for w in inputs.WORKLOADS[:4]])
+def test_workload_bias_parity(idx):
+    wl = inputs.WORKLOADS[idx]
+    layer = Layer.of(wl.layers[0])
+    x, w, dy = inputs.layer_inputs(wl.layers[0], wl.seeds, wl.dtype)
+    b = _bias(layer, wl.seeds[1] + 100, wl.dtype)
+    ey, eb, _, _ = _check(layer, wl.dtype, x, w, b, dy)
+    print(f"{wl.name}: y(bias)={ey:.2e} db={eb:.2e}", flush=True)
+
+
+BIAS_SHAPES = [
+    (1, 1, 1, 1, 1, 1, 1, 1),
+    (3, 3, 7, 8, 4, 3, 3, 2),
+    (17, 59, 11, 15, 128, 5, 5, 3),
+    (17, 128, 3, 4, 128, 3, 3, 1),
+    (2, 65, 10, 10, 33, 3, 2, 4),
+    (5, 7, 6, 6, 130, 6, 6, 1),
+    (2, 3, 32, 32, 8, 5, 5, 2),
+    (9, 59, 11, 15, 128, 5, 5, 3),
+    (300, 8, 5, 5, 16, 3, 3, 1),        # more images than a bias-grad workgroup has threads
+]
+
+
+@pytest.fixture
+def kernel_policy(request):
+    prev = gb.gc_set_kernel_policy(request.param)
+    yield request.param
+    gb.gc_set_kernel_policy(prev)
+
+
+@pytest.mark.parametrize("kernel_policy", [gb.GC_POLICY_AUTO, gb.GC_POLICY_GENERIC],
+                         ids=["auto", "generic"], indirect=True)
+@pytest.mark.parametrize("shape", BIAS_SHAPES, ids=["x".join(map(str, s)) for s in BIAS_SHAPES])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("relu", [0, 1])
+def test_bias_shapes(shape, dtype, relu, kernel_policy):
+    layer = Layer(*shape, relu)
+    x, w, dy = draw(layer, (sum(shape), 5, 6 + relu), dtype)
+    b = _bias(layer, 77, dtype)
+    _check(layer, dtype, x, w, b, dy)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bias_integer_inputs_exact(dtype):
+    layer = Layer(64, 59, 11, 15, 128, 5, 5, 3, 1)
+    x = inputs.integers(layer.x_shape, 31, dtype=dtype)
+    w = inputs.integers(layer.w_shape, 32, dtype=dtype)
+    b = inputs.integers((layer.OC,), 33, dtype=dtype)
+    dy = inputs.integers(layer.y_shape, 34, dtype=dtype)
+    _, y, db = _run(layer, dtype, x, w, b, dy)
+    y_ref = orc.conv_fwd_bias(f64(x), f64(w), f64(b), layer.stride, 1)
+    db_ref = orc.conv_bwd_bias(f64(dy), f64(y), 1)
+    td = inputs.torch_dtype(dtype)
+    rne = lambda a: torch.from_numpy(a).to(torch.float32).to(td).to(torch.float64).numpy()
+    assert np.array_equal(f64(y), rne(y_ref))
+    assert np.array_equal(f64(db), rne(db_ref))
+
+
+def test_bias_grad_deterministic():
+    layer = Layer(1024, 59, 11, 15, 128, 5, 5, 3, 1)
+    x, w, dy = draw(layer, (1, 2, 3), "f32")
+    b = _bias(layer, 4, "f32")
+    conv, y, db = _run(layer, "f32", x, w, b, dy)
+    dyd = dy.cuda()
+    for _ in range(3):
+        db2 = torch.empty_like(db)
+        conv.bwd_bias(dyd, y, db2)
+        torch.cuda.synchronize()
+        assert torch.equal(db2.view(torch.int32), db.view(torch.int32))

@@ -327,6 +327,71 @@ def test_matches_torch_conv2d_fp64(shape, relu):
 
 
 # --------------------------------------------------------------------------
+# Bias: forward with a per-channel bias and the bias gradient
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(2, 3, 7, 8, 4, 3, 3, 2), (3, 59, 11, 15, 8, 5, 5, 3),
+                                   (4, 16, 3, 4, 8, 3, 3, 1)])
+@pytest.mark.parametrize("relu", [0, 1])
+def test_bias_matches_torch_fp64(shape, relu):
+    """torch conv2d with a bias, and autograd's bias gradient, in fp64 on the CPU."""
+    B, IC, H, W, OC, KH, KW, S = shape
+    r = rng(7 * sum(shape) + relu)
+    x = r.standard_normal((B, IC, H, W))
+    w = r.standard_normal((OC, IC, KH, KW))
+    b = r.standard_normal(OC)
+    bt = torch.tensor(b, requires_grad=True)
+    yt = torch.nn.functional.conv2d(torch.tensor(x), torch.tensor(w), bt, stride=S)
+    if relu:
+        yt = torch.relu(yt)
+    dy = r.standard_normal(tuple(yt.shape))
+    yt.backward(torch.tensor(dy))
+    y = orc.conv_fwd_bias(x, w, b, S, relu)
+    np.testing.assert_allclose(y, yt.detach().numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(orc.conv_bwd_bias(dy, y, relu), bt.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_bias_closed_forms():
+    """dy = 1: db = B*OH*OW without a mask, and the count of positive outputs
+    of each channel with one; a zero bias leaves the forward unchanged and a
+    constant bias with w = 0 is copied to every output."""
+    B, OC, OH, OW = 3, 5, 4, 6
+    dy = np.ones((B, OC, OH, OW))
+    np.testing.assert_array_equal(orc.conv_bwd_bias(dy, None, 0), np.full(OC, B * OH * OW))
+    ym = np.zeros((B, OC, OH, OW))
+    for oc in range(OC):
+        ym.reshape(B, OC, -1)[:, oc, :oc + 1] = 1.0      # oc+1 positives per image
+        ym.reshape(B, OC, -1)[:, oc, oc + 1:oc + 3] = -2.0
+    np.testing.assert_array_equal(orc.conv_bwd_bias(dy, ym, 1), B * (np.arange(OC) + 1.0))
+    x = rng(3).standard_normal((2, 3, 7, 8))
+    w = rng(4).standard_normal((4, 3, 3, 3))
+    np.testing.assert_array_equal(orc.conv_fwd_bias(x, w, np.zeros(4), 2, 0), orc.conv_fwd(x, w, 2, 0))
+    y = orc.conv_fwd_bias(x, np.zeros_like(w), np.arange(4.0) - 1.5, 2, 1)
+    np.testing.assert_array_equal(y, np.broadcast_to(np.maximum(np.arange(4.0) - 1.5, 0)[None, :, None, None], y.shape))
+
+
+def test_bias_finite_differences():
+    """dL/dbias for L = <relu(conv(x, w) + bias), dy>, central differences in fp64
+    on inputs whose pre-activations stay away from the kink."""
+    r = rng(11)
+    x = r.standard_normal((2, 3, 11, 15))
+    w = r.standard_normal((4, 3, 5, 5))
+    b = r.standard_normal(4)
+    pre = orc.conv_fwd_bias(x, w, b, 3, 0)
+    b = b + np.where(np.abs(pre).min(axis=(0, 2, 3)) < 1e-2, 0.05, 0.0)   # keep off the kink
+    y = orc.conv_fwd_bias(x, w, b, 3, 1)
+    dy = r.standard_normal(y.shape)
+    h = 1e-6
+    num = np.empty(4)
+    for oc in range(4):
+        bp, bm = b.copy(), b.copy()
+        bp[oc] += h; bm[oc] -= h
+        num[oc] = (np.sum(orc.conv_fwd_bias(x, w, bp, 3, 1) * dy) -
+                   np.sum(orc.conv_fwd_bias(x, w, bm, 3, 1) * dy)) / (2 * h)
+    np.testing.assert_allclose(orc.conv_bwd_bias(dy, y, 1), num, rtol=1e-6, atol=1e-6)
+
+
+# --------------------------------------------------------------------------
 # A second formulation written here: im2col + matrix products
 # --------------------------------------------------------------------------
 
@@ -443,6 +508,11 @@ PLANTS = [
     ("wgrad: last output column dropped", "for (int ow = 0; ow < OW; ++ow)\n                            acc += masked_dy",
      "for (int ow = 0; ow < OW - 1; ++ow)\n                            acc += masked_dy"),
     ("out size rounds up", "return (in - k) / s + 1;", "return (in - k + s - 1) / s + 1;"),
+    ("fwd_bias: bias dropped", "double acc = bias[oc];", "double acc = 0.0;"),
+    ("fwd_bias: bias of the wrong channel", "double acc = bias[oc];", "double acc = bias[(oc + 1) % OC];"),
+    ("bwd_bias: last output row dropped",
+     "for (int oh = 0; oh < OH; ++oh)\n                for (int ow = 0; ow < OW; ++ow)\n                    acc += masked_dy",
+     "for (int oh = 0; oh < OH - 1; ++oh)\n                for (int ow = 0; ow < OW; ++ow)\n                    acc += masked_dy"),
 ]
 
 
@@ -457,6 +527,8 @@ def _pins_pass():
         lambda: test_adjoint_identity((2, 3, 7, 8, 4, 3, 3, 2), 1),
         lambda: test_matches_torch_conv2d_fp64((2, 3, 11, 15, 4, 5, 5, 3), 1),
         lambda: test_matches_torch_conv2d_fp64((2, 3, 7, 8, 4, 3, 2, 2), 1),
+        test_bias_closed_forms,
+        lambda: test_bias_matches_torch_fp64((2, 3, 7, 8, 4, 3, 3, 2), 1),
     ]
     for c in checks:
         try:
