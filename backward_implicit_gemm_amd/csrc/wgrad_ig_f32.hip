@@ -44,8 +44,13 @@ __global__ void __launch_bounds__(64 * NW) wgrad_ig_f32(WgradIgArgs<T> a)
     const int wm = wave & 3, wn = wave >> 2;   // oc group, k group of this wave
     constexpr int OCR = MBW * 64;   // oc rows covered by the four oc groups
 
-    const int k0 = blockIdx.x * p.BNK;
-    const int split = blockIdx.y;
+    // Workgroups are dealt to the 8 XCDs round-robin by id; ids are laid out
+    // so that all column tiles of one split share an XCD and its L2, which
+    // then serves that split's images of x and dy to every tile.
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int split = (slot / p.nkt) * 8 + xcd;
+    if (split >= p.splits) return;
+    const int k0 = (slot % p.nkt) * p.BNK;
     const int bs = split * p.GS;
     const int be = min(g.B, bs + p.GS);
     const int ic_lo = k0 / g.KK;
@@ -284,7 +289,7 @@ hipError_t launch_wgrad_ig(const Geom &g, const WgradIgPlan &p, const void *x, c
     if (!v || 4 * v->RS != p.R4 || p.G * g.P > p.R4) return hipErrorInvalidValue;
     WgradIgArgs<T> a{g, (const T *)x, (const T *)dy, (const T *)ym, part, relu, p,
                      make_fastdiv(g.OC * g.P)};
-    dim3 grid(p.nkt, p.splits);
+    dim3 grid(8 * ((p.splits + 7) / 8) * p.nkt);
     hipError_t e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(v->fn, grid, dim3(64 * p.NW), p.lds, s, a);
