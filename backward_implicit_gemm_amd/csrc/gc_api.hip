@@ -93,6 +93,10 @@ bool fwd_f32_plan(const Geom &g, FwdIgPlan &p)
 {
     return use_ig() && cached_plan<std::remove_reference_t<decltype(p)>, plan_fwd_ig_f32>(g, p);
 }
+bool fwd_f32_rf_plan(const Geom &g, FwdBfPlan &p)
+{
+    return use_ig() && cached_plan<FwdBfPlan, plan_fwd_rf_f32>(g, p);
+}
 bool fwd_bf16_plan(const Geom &g, FwdBfPlan &p)
 {
     return use_ig() && cached_plan<std::remove_reference_t<decltype(p)>, plan_fwd_ig_bf16>(g, p);
@@ -175,6 +179,7 @@ size_t gc_conv_workspace_bytes(int op, const gc_conv_desc *d, int dtype)
     case GC_OP_FWD: {
         FwdBfPlan p;
         if (dtype == GC_BF16 && fwd_bf16_plan(g, p)) return p.ws_bytes;
+        if (dtype == GC_F32 && fwd_f32_rf_plan(g, p)) return p.ws_bytes;
         return 0;
     }
     case GC_OP_BWD_DATA: {
@@ -202,6 +207,12 @@ static int conv_fwd(const void *x, const void *w, const void *bias, void *y, voi
         return GC_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == GC_F32) {
+        FwdBfPlan rp;
+        if (fwd_f32_rf_plan(g, rp)) {
+            if (!workspace || ws_bytes < rp.ws_bytes) return GC_ERR_WORKSPACE;
+            if (reinterpret_cast<uintptr_t>(workspace) % 16) return GC_ERR_WORKSPACE;
+            return hip_status(launch_fwd_rf_f32(g, rp, x, w, bias, y, workspace, relu, s));
+        }
         FwdIgPlan p;
         if (fwd_f32_plan(g, p))
             return hip_status(launch_fwd_ig_f32(g, p, x, w, bias, y, relu, s));

@@ -49,6 +49,11 @@ size_t bias_grad_ws_bytes(const Geom &g);
 template <typename T>
 hipError_t launch_bias_grad(const Geom &g, const void *dy, const void *ym, void *db, float *part,
                             int relu, hipStream_t s);
+// fp32 forward with channels-innermost staging and packed weight fragments
+// (fwd_rf_f32.hip); the plan struct is shared with the bf16 forward.
+bool plan_fwd_rf_f32(const Geom &g, FwdBfPlan &p);
+hipError_t launch_fwd_rf_f32(const Geom &g, const FwdBfPlan &p, const void *x, const void *w,
+                             const void *bias, void *y, void *ws, int relu, hipStream_t s);
 bool plan_dgrad_ig_bf16(const Geom &g, DgradBfPlan &p);
 // fp32 d_input with register-held dz fragments (dgrad_rf_f32.hip); the plan
 // struct is shared with the bf16 kernel, KS holding the 16-channel steps.

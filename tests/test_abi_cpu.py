@@ -120,9 +120,8 @@ def test_workspace_sizes_are_sane():
             else:
                 assert n <= 64 * d.OC * K * 4 + dz_bytes
         # packed weights for the bf16 forward and d_input kernels: a padded copy of w
-        assert gb.gc_conv_workspace_bytes(gb.GC_OP_FWD, d, gb.GC_F32) == 0
         for op, dt, es in ((gb.GC_OP_FWD, gb.GC_BF16, 2), (gb.GC_OP_BWD_DATA, gb.GC_BF16, 2),
-                           (gb.GC_OP_BWD_DATA, gb.GC_F32, 4)):
+                           (gb.GC_OP_FWD, gb.GC_F32, 4), (gb.GC_OP_BWD_DATA, gb.GC_F32, 4)):
             n = gb.gc_conv_workspace_bytes(op, d, dt)
             assert n == 0 or d.OC * K * es <= n <= 16 * max(d.OC, 32) * max(K, 64) * es
     assert gb.gc_conv_workspace_bytes(99, L1, 0) == 0
