@@ -117,6 +117,10 @@ bool dgrad_plan(const Geom &g, DgradIgPlan &p)
 {
     return use_ig() && cached_plan<std::remove_reference_t<decltype(p)>, plan_dgrad_ig_f32>(g, p);
 }
+bool wgrad_f32_rf_plan(const Geom &g, WgradRfPlan &p)
+{
+    return use_ig() && cached_plan<WgradRfPlan, plan_wgrad_rf_f32>(g, p);
+}
 bool wgrad_plan(const Geom &g, WgradIgPlan &p)
 {
     return use_ig() && cached_plan<std::remove_reference_t<decltype(p)>, plan_wgrad_ig_f32>(g, p);
@@ -140,6 +144,8 @@ size_t wgrad_ws_bytes(const Geom &g, int dtype)
 {
     WgradBfPlan bp;
     if (dtype == GC_BF16 && wgrad_bf16_plan(g, bp)) return bp.ws_bytes;
+    WgradRfPlan rp;
+    if (dtype == GC_F32 && wgrad_f32_rf_plan(g, rp)) return rp.ws_bytes;
     return size_t(wgrad_splits(g, dtype, nullptr, nullptr)) * g.OC * g.K * sizeof(float);
 }
 
@@ -313,6 +319,14 @@ int gc_conv_bwd_weight(const void *x, const void *dy, const void *y_mask, void *
             if (!workspace || ws_bytes < bp.ws_bytes) return GC_ERR_WORKSPACE;
             if (reinterpret_cast<uintptr_t>(workspace) % 256) return GC_ERR_WORKSPACE;
             return hip_status(launch_wgrad_ig_bf16(g, bp, x, dy, y_mask, dw, workspace, relu, s));
+        }
+    }
+    if (dtype == GC_F32) {
+        WgradRfPlan rp;
+        if (wgrad_f32_rf_plan(g, rp)) {
+            if (!workspace || ws_bytes < rp.ws_bytes) return GC_ERR_WORKSPACE;
+            if (reinterpret_cast<uintptr_t>(workspace) % 16) return GC_ERR_WORKSPACE;
+            return hip_status(launch_wgrad_rf_f32(g, rp, x, dy, y_mask, dw, workspace, relu, s));
         }
     }
     WgradIgPlan ig;

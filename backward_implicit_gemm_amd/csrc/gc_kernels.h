@@ -24,6 +24,7 @@ struct DgradIgPlan;
 struct WgradIgPlan;
 struct DgradBfPlan;
 struct WgradBfPlan;
+struct WgradRfPlan;
 bool plan_fwd_ig_f32(const Geom &g, FwdIgPlan &p);
 hipError_t launch_fwd_ig_f32(const Geom &g, const FwdIgPlan &p, const void *x, const void *w,
                              const void *bias, void *y, int relu, hipStream_t s);
@@ -60,6 +61,11 @@ bool plan_dgrad_ig_bf16(const Geom &g, DgradBfPlan &p);
 bool plan_dgrad_rf_f32(const Geom &g, DgradBfPlan &p);
 hipError_t launch_dgrad_rf_f32(const Geom &g, const DgradBfPlan &p, const void *dy, const void *w,
                                const void *ym, void *dx, void *ws, int relu, hipStream_t s);
+// fp32 wgrad with image-quad staging: partial tiles then the fixed-order
+// reduction into dw (fp32 storage only)
+bool plan_wgrad_rf_f32(const Geom &g, WgradRfPlan &p);
+hipError_t launch_wgrad_rf_f32(const Geom &g, const WgradRfPlan &p, const void *x, const void *dy,
+                               const void *ym, void *dw, void *ws, int relu, hipStream_t s);
 bool plan_wgrad_ig_bf16(const Geom &g, WgradBfPlan &p);
 // dz regrouping, the partial-tile kernel and the fixed-order reduction into dw
 hipError_t launch_wgrad_ig_bf16(const Geom &g, const WgradBfPlan &p, const void *x, const void *dy,

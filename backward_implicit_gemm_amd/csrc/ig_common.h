@@ -161,6 +161,28 @@ struct WgradBfPlan {
     size_t ws_bytes;  // dz_bytes + splits * OC * K fp32 partials
 };
 
+// fp32 wgrad with image-quad staging (wgrad_rf_f32.hip).
+struct WgradRfPlan {
+    int NBWV;     // 16-column blocks per wave
+    int MBLK;     // 16-row oc blocks, ceil(OC / 16)
+    int WN;       // waves per oc block (they split the column blocks)
+    int NBW;      // 16-column blocks per workgroup, WN * NBWV
+    int chunks;   // column chunks, ceil(ceil(K / 16) / NBW)
+    int NQ;       // 4-image quads, ceil(B / 4)
+    int QB;       // quads per staging phase
+    int QPS;      // quads per split
+    int splits;   // partial tiles
+    int SPP;      // 4-step MFMA blocks per phase, ceil(QB * P / 4)
+    int CCS;      // channels staged per chunk (widest span)
+    int XU;       // x staging units per quad, ceil(CCS * H * W / 4)
+    int DU;       // dz staging units per quad, ceil(OC * P / 4)
+    int WP, IS;   // x LDS slots per pixel row / per channel
+    int OCP;      // dz LDS slots per output position (>= OC)
+    int bufsz;    // 16-byte slots per LDS buffer (x, dz, one zero slot)
+    size_t lds;
+    size_t ws_bytes;   // splits * OC * K fp32 partials
+};
+
 struct WgradIgPlan {
     int NW;       // waves per workgroup: 4 split OC, NW/4 split the k tile
     int G;        // images per stage
