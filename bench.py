@@ -13,8 +13,10 @@ forward and backward separately over 50 warmup and 200 timed iterations.
 Prints one JSON line per workload: throughput in TFLOP/s of algorithmic work
 (2*B*OC*OH*OW*IC*KH*KW per pass, three passes per step) over K steps, each
 step replayed as one HIP graph between HIP events on the launch stream; the
-same K steps issued eagerly (host work included); per-call GPU times from
-graphs of back-to-back copies of each call; a roofline entry for the
+same K steps issued eagerly (host work included); the step timed cold
+(caches flushed by a 640 MB write before each replay); the launch floor (a
+graph of as many one-element kernels as a step launches); per-call GPU times
+from graphs of back-to-back copies of each call; a roofline entry for the
 dominant call; and the CPU oracle timed on this host on a bounded sample
 (default workload only).
 """
@@ -171,6 +173,41 @@ def run_gpu(wl, steps, warmup):
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / steps
 
+    # Cold protocol: before each timed step, write 640 MB (more than the
+    # 256 MB MALL and every XCD's L2 together) so the step starts from HBM.
+    flush = torch.empty(640 << 20, dtype=torch.uint8, device=dev)
+    cold_n = max(3, min(20, steps // 10))
+    cold_ms = 0.0
+    for _ in range(cold_n):
+        flush.fill_(1)
+        start.record(stream)
+        step_graph.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        cold_ms += start.elapsed_time(end)
+    ms_cold = cold_ms / cold_n
+    del flush
+
+    # Launch floor: the same number of kernels as one step, each a one-element
+    # add, replayed as a graph; the least time a step of that many dependent
+    # launches can take.
+    nk = sum(len(CALL_KERNELS[name.rstrip("0123456789")][wl.dtype]) for name, _ in calls)
+    tiny = torch.zeros(1, device=dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(nk):
+            tiny.add_(1.0)
+    g.replay()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    floor = {"kernels_per_step": nk, "us_per_step": round(start.elapsed_time(end) / steps * 1e3, 3)}
+    floor["us_per_kernel"] = round(floor["us_per_step"] / nk, 3)
+    del g
+
     # The same steps issued eagerly through the C ABI, host work included.
     start.record(stream)
     for _ in range(steps):
@@ -227,7 +264,7 @@ def run_gpu(wl, steps, warmup):
         torch.cuda.synchronize()
         bias_us[name] = start.elapsed_time(end) / (replays * reps) * 1e3
         del g
-    return ms_step, ms_eager, per_call, bias_us
+    return ms_step, ms_eager, per_call, bias_us, ms_cold, floor
 
 
 def cpu_baseline(wl, budget_s):
@@ -275,7 +312,7 @@ CALL_KERNELS = {
               "bf16": ["dz_groups_bf16", "wgrad_ig_bf16", "wgrad_reduce"]},
 }
 
-def report(wl, ms_step, ms_eager, per_call, bias_us, steps, warmup, cpu):
+def report(wl, ms_step, ms_eager, per_call, bias_us, ms_cold, floor, steps, warmup, cpu):
     L0 = wl.layers[0]
     esize = 4 if wl.dtype == "f32" else 2
     flops_step = sum(3 * layer_flops(L) for L in wl.layers)
@@ -313,6 +350,8 @@ def report(wl, ms_step, ms_eager, per_call, bias_us, steps, warmup, cpu):
         "warmup": warmup,
         "ms_per_step": round(ms_step, 5),
         "ms_per_step_eager": round(ms_eager, 5),
+        "ms_per_step_cold": round(ms_cold, 5),
+        "launch_floor": floor,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": vs,
@@ -363,11 +402,12 @@ def main():
             print(f"unknown workload {name}; choose from {names}", file=sys.stderr)
             sys.exit(2)
         wl = inputs.WORKLOADS[names.index(name)]
-        ms, ms_eager, per_call, bias_us = run_gpu(wl, a.steps, a.warmup)
+        ms, ms_eager, per_call, bias_us, ms_cold, floor = run_gpu(wl, a.steps, a.warmup)
         cpu = None
         if not a.no_cpu and name == DEFAULT_WORKLOAD:
             cpu = cpu_baseline(wl, a.cpu_seconds)
-        print(json.dumps(report(wl, ms, ms_eager, per_call, bias_us, a.steps, a.warmup, cpu)), flush=True)
+        print(json.dumps(report(wl, ms, ms_eager, per_call, bias_us, ms_cold, floor, a.steps, a.warmup,
+                                cpu)), flush=True)
 
 
 if __name__ == "__main__":
