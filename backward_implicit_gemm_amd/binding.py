@@ -15,12 +15,12 @@ LIB_PATH = os.path.join(_HERE, "libgc.so")
 
 GC_OK, GC_ERR_INVALID_ARG, GC_ERR_UNSUPPORTED, GC_ERR_WORKSPACE, GC_ERR_HIP = range(5)
 GC_F32, GC_BF16 = 0, 1
-GC_OP_FWD, GC_OP_BWD_DATA, GC_OP_BWD_WEIGHT, GC_OP_BWD_BIAS = 0, 1, 2, 3
+GC_OP_FWD, GC_OP_BWD_DATA, GC_OP_BWD_WEIGHT, GC_OP_BWD_BIAS, GC_OP_BWD = 0, 1, 2, 3, 4
 
 EXPORTED = (
     "gc_conv_out_dims", "gc_conv_workspace_bytes", "gc_conv_fwd", "gc_conv_bwd_data",
     "gc_conv_bwd_weight", "gc_status_string", "gc_fastdiv_selfcheck", "gc_version",
-    "gc_set_kernel_policy", "gc_conv_fwd_bias", "gc_conv_bwd_bias",
+    "gc_set_kernel_policy", "gc_conv_fwd_bias", "gc_conv_bwd_bias", "gc_conv_bwd",
 )
 GC_POLICY_AUTO, GC_POLICY_GENERIC = 0, 1
 
@@ -62,6 +62,8 @@ def lib():
     L.gc_conv_bwd_data.restype = i
     L.gc_conv_bwd_weight.argtypes = [vp, vp, vp, vp, vp, sz, dp, i, i, vp]
     L.gc_conv_bwd_weight.restype = i
+    L.gc_conv_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, dp, i, i, vp]
+    L.gc_conv_bwd.restype = i
     L.gc_status_string.argtypes = [i]
     L.gc_status_string.restype = ctypes.c_char_p
     L.gc_fastdiv_selfcheck.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
@@ -216,6 +218,18 @@ def gc_conv_bwd_weight(x, dy, y_mask, dw, relu, stride, workspace, stream=None):
     return dw
 
 
+def gc_conv_bwd(x, w, dy, y_mask, dx, dw, relu, stride, workspace, stream=None):
+    """dx and dw together (dy masked by y_mask > 0 when relu) via gc_conv_bwd."""
+    dt = _dtype_code(x)
+    desc = desc_from(x.shape, w.shape, stride)
+    wp, wn = _ws(workspace)
+    st = lib().gc_conv_bwd(_dev(x, "x", dt), _dev(w, "w", dt), _dev(dy, "dy", dt),
+                           _dev(y_mask, "y_mask", dt), _dev(dx, "dx", dt), _dev(dw, "dw", dt),
+                           wp, wn, ctypes.byref(desc), int(relu), dt, _stream(stream))
+    _check("gc_conv_bwd", st)
+    return dx, dw
+
+
 class Conv:
     """One convolution layer's three passes with their workspaces allocated
     once (torch allocates; the library only receives pointers)."""
@@ -229,7 +243,8 @@ class Conv:
         OH, OW = gc_conv_out_dims(self.desc)
         self.y_shape = (x_shape[0], w_shape[0], OH, OW)
         self.ws = {op: workspace_for(op, self.desc, self.dt, device)
-                   for op in (GC_OP_FWD, GC_OP_BWD_DATA, GC_OP_BWD_WEIGHT, GC_OP_BWD_BIAS)}
+                   for op in (GC_OP_FWD, GC_OP_BWD_DATA, GC_OP_BWD_WEIGHT, GC_OP_BWD_BIAS,
+                              GC_OP_BWD)}
 
     def fwd(self, x, w, y, stream=None):
         return gc_conv_fwd(x, w, y, self.relu, self.stride, self.ws[GC_OP_FWD], stream)
@@ -241,6 +256,10 @@ class Conv:
     def bwd_weight(self, x, dy, y, dw, stream=None):
         return gc_conv_bwd_weight(x, dy, y if self.relu else None, dw, self.relu, self.stride,
                                   self.ws[GC_OP_BWD_WEIGHT], stream)
+
+    def bwd(self, x, w, dy, y, dx, dw, stream=None):
+        return gc_conv_bwd(x, w, dy, y if self.relu else None, dx, dw, self.relu, self.stride,
+                           self.ws[GC_OP_BWD], stream)
 
     def fwd_bias(self, x, w, bias, y, stream=None):
         return gc_conv_fwd_bias(x, w, bias, y, self.relu, self.stride, self.ws[GC_OP_FWD], stream)

@@ -117,6 +117,11 @@ bool dgrad_plan(const Geom &g, DgradIgPlan &p)
 {
     return use_ig() && cached_plan<std::remove_reference_t<decltype(p)>, plan_dgrad_ig_f32>(g, p);
 }
+bool bwd_fused_plan(const Geom &g, BwdFusedBfPlan &p)
+{
+    return use_ig() && cached_plan<BwdFusedBfPlan, plan_bwd_fused_bf16>(g, p);
+}
+size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
 bool wgrad_f32_rf_plan(const Geom &g, WgradRfPlan &p)
 {
     return use_ig() && cached_plan<WgradRfPlan, plan_wgrad_rf_f32>(g, p);
@@ -196,6 +201,13 @@ size_t gc_conv_workspace_bytes(int op, const gc_conv_desc *d, int dtype)
     }
     case GC_OP_BWD_WEIGHT: return wgrad_ws_bytes(g, dtype);
     case GC_OP_BWD_BIAS: return bias_grad_ws_bytes(g);
+    case GC_OP_BWD: {
+        BwdFusedBfPlan p;
+        if (dtype == GC_BF16 && bwd_fused_plan(g, p)) return p.ws_bytes;
+        // d_input's workspace, then wgrad's at the next 256-byte boundary
+        return round256(gc_conv_workspace_bytes(GC_OP_BWD_DATA, d, dtype)) +
+               gc_conv_workspace_bytes(GC_OP_BWD_WEIGHT, d, dtype);
+    }
     default: return 0;
     }
 }
@@ -351,6 +363,38 @@ int gc_conv_bwd_weight(const void *x, const void *dy, const void *y_mask, void *
         if (e == hipSuccess) e = launch_wgrad_reduce<bf16_t>(part, dw, splits, g.OC * g.K, s);
     }
     return hip_status(e);
+}
+
+int gc_conv_bwd(const void *x, const void *w, const void *dy, const void *y_mask, void *dx,
+                void *dw, void *workspace, size_t ws_bytes, const gc_conv_desc *d, int relu,
+                int dtype, void *stream)
+{
+    Geom g;
+    int st = check_desc(d, &g);
+    if (st != GC_OK) return st;
+    if (!valid_dtype(dtype) || (relu != 0 && relu != 1)) return GC_ERR_INVALID_ARG;
+    if (!x || !w || !dy || !dx || !dw) return GC_ERR_INVALID_ARG;
+    if ((relu == 1) != (y_mask != nullptr)) return GC_ERR_INVALID_ARG;
+    if (!aligned(x, dtype) || !aligned(w, dtype) || !aligned(dy, dtype) || !aligned(dx, dtype) ||
+        !aligned(dw, dtype) || (y_mask && !aligned(y_mask, dtype)))
+        return GC_ERR_INVALID_ARG;
+    BwdFusedBfPlan fp;
+    if (dtype == GC_BF16 && bwd_fused_plan(g, fp)) {
+        if (!workspace || ws_bytes < fp.ws_bytes) return GC_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(workspace) % 256) return GC_ERR_WORKSPACE;
+        return hip_status(launch_bwd_fused_bf16(g, fp, x, w, dy, y_mask, dx, dw, workspace, relu,
+                                                static_cast<hipStream_t>(stream)));
+    }
+    // no fused plan: d_input, then wgrad, each in its part of the workspace
+    const size_t wd = gc_conv_workspace_bytes(GC_OP_BWD_DATA, d, dtype);
+    const size_t ww = gc_conv_workspace_bytes(GC_OP_BWD_WEIGHT, d, dtype);
+    const size_t off = round256(wd);
+    if (off + ww > 0 && (!workspace || ws_bytes < off + ww)) return GC_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256) return GC_ERR_WORKSPACE;
+    st = gc_conv_bwd_data(dy, w, y_mask, dx, wd ? workspace : nullptr, wd, d, relu, dtype, stream);
+    if (st != GC_OK) return st;
+    void *wsw = ww ? static_cast<char *>(workspace) + off : nullptr;
+    return gc_conv_bwd_weight(x, dy, y_mask, dw, wsw, ww, d, relu, dtype, stream);
 }
 
 int gc_set_kernel_policy(int policy)

@@ -25,6 +25,7 @@ struct WgradIgPlan;
 struct DgradBfPlan;
 struct WgradBfPlan;
 struct WgradRfPlan;
+struct BwdFusedBfPlan;
 bool plan_fwd_ig_f32(const Geom &g, FwdIgPlan &p);
 hipError_t launch_fwd_ig_f32(const Geom &g, const FwdIgPlan &p, const void *x, const void *w,
                              const void *bias, void *y, int relu, hipStream_t s);
@@ -66,6 +67,12 @@ hipError_t launch_dgrad_rf_f32(const Geom &g, const DgradBfPlan &p, const void *
 bool plan_wgrad_rf_f32(const Geom &g, WgradRfPlan &p);
 hipError_t launch_wgrad_rf_f32(const Geom &g, const WgradRfPlan &p, const void *x, const void *dy,
                                const void *ym, void *dw, void *ws, int relu, hipStream_t s);
+// bf16 backward (d_input + wgrad) in three launches: pre-passes, both main
+// kernels in one grid, reduction.  Same results as the separate calls.
+bool plan_bwd_fused_bf16(const Geom &g, BwdFusedBfPlan &p);
+hipError_t launch_bwd_fused_bf16(const Geom &g, const BwdFusedBfPlan &p, const void *x,
+                                 const void *w, const void *dy, const void *ym, void *dx, void *dw,
+                                 void *ws, int relu, hipStream_t s);
 bool plan_wgrad_ig_bf16(const Geom &g, WgradBfPlan &p);
 // dz regrouping, the partial-tile kernel and the fixed-order reduction into dw
 hipError_t launch_wgrad_ig_bf16(const Geom &g, const WgradBfPlan &p, const void *x, const void *dy,

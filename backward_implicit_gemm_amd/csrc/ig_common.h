@@ -200,4 +200,14 @@ struct WgradIgPlan {
     size_t lds;
 };
 
+// bf16 backward in three launches (bwd_fused_bf16.hip): the d_input and
+// wgrad plans it runs, and where wgrad's part of the workspace starts.
+struct BwdFusedBfPlan {
+    DgradBfPlan d;
+    WgradBfPlan w;
+    size_t ws_w_offset;   // d.ws_bytes rounded up to 256
+    size_t ws_bytes;      // ws_w_offset + w.ws_bytes
+    int fuse_main;        // both main kernels in one grid
+};
+
 }  // namespace gc

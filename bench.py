@@ -16,7 +16,8 @@ step replayed as one HIP graph between HIP events on the launch stream; the
 same K steps issued eagerly (host work included); the step timed cold
 (caches flushed by a 640 MB write before each replay); the launch floor (a
 graph of as many one-element kernels as a step launches); per-call GPU times
-from graphs of back-to-back copies of each call; a roofline entry for the
+from graphs of back-to-back copies of each call; the backward through
+gc_conv_bwd (d_input and wgrad in one call) per call and as a step; a roofline entry for the
 dominant call; and the CPU oracle timed on this host on a bounded sample
 (default workload only).
 """
@@ -237,6 +238,43 @@ def run_gpu(wl, steps, warmup):
         per_call[name] = start.elapsed_time(end) / (replays * reps) * 1e3
         del g
 
+    # The whole backward of each layer through gc_conv_bwd (one call for
+    # d_input and wgrad; fewer launches where a fused plan exists), per call
+    # and as a step with the forward calls.
+    fused_calls = [(f"bwd{i + 1}", lambda c=c, i=i: c.bwd(xs[i], ws[i], dys[i], ys[i], dxs[i], dws[i]))
+                   for i, c in reversed(list(enumerate(convs)))]
+    fused = {"us_per_call": {}}
+    for name, f in fused_calls:
+        f()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                f()
+        g.replay()
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(replays):
+            g.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        fused["us_per_call"][name] = round(start.elapsed_time(end) / (replays * reps) * 1e3, 3)
+        del g
+    fwd_calls = [c for c in calls if c[0].startswith("fwd")]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _, f in fwd_calls + fused_calls:
+            f()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    fused["ms_per_step"] = round(start.elapsed_time(end) / steps, 5)
+    del g
+
     # The bias entry points (forward with a bias, bias gradient), timed the
     # same way; not part of the step.
     bias_calls = []
@@ -264,7 +302,7 @@ def run_gpu(wl, steps, warmup):
         torch.cuda.synchronize()
         bias_us[name] = start.elapsed_time(end) / (replays * reps) * 1e3
         del g
-    return ms_step, ms_eager, per_call, bias_us, ms_cold, floor
+    return ms_step, ms_eager, per_call, bias_us, ms_cold, floor, fused
 
 
 def cpu_baseline(wl, budget_s):
@@ -312,7 +350,7 @@ CALL_KERNELS = {
               "bf16": ["dz_groups_bf16", "wgrad_ig_bf16", "wgrad_reduce"]},
 }
 
-def report(wl, ms_step, ms_eager, per_call, bias_us, ms_cold, floor, steps, warmup, cpu):
+def report(wl, ms_step, ms_eager, per_call, bias_us, ms_cold, floor, steps, warmup, cpu, fused=None):
     L0 = wl.layers[0]
     esize = 4 if wl.dtype == "f32" else 2
     flops_step = sum(3 * layer_flops(L) for L in wl.layers)
@@ -369,6 +407,7 @@ def report(wl, ms_step, ms_eager, per_call, bias_us, ms_cold, floor, steps, warm
                    "bwd": round(sum(2 * layer_flops(L) for L in wl.layers) / (bwd_us * 1e-6) / 1e12, 3)},
         "roofline": roof,
         "bias_us_per_call": {k: round(v, 3) for k, v in bias_us.items()},
+        "fused_bwd": fused,
         "cpu_baseline": cpu,
     }
     if vs is not None:
@@ -402,12 +441,12 @@ def main():
             print(f"unknown workload {name}; choose from {names}", file=sys.stderr)
             sys.exit(2)
         wl = inputs.WORKLOADS[names.index(name)]
-        ms, ms_eager, per_call, bias_us, ms_cold, floor = run_gpu(wl, a.steps, a.warmup)
+        ms, ms_eager, per_call, bias_us, ms_cold, floor, fused = run_gpu(wl, a.steps, a.warmup)
         cpu = None
         if not a.no_cpu and name == DEFAULT_WORKLOAD:
             cpu = cpu_baseline(wl, a.cpu_seconds)
         print(json.dumps(report(wl, ms, ms_eager, per_call, bias_us, ms_cold, floor, a.steps, a.warmup,
-                                cpu)), flush=True)
+                                cpu, fused)), flush=True)
 
 
 if __name__ == "__main__":

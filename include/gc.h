@@ -70,7 +70,8 @@ typedef enum {
     GC_OP_FWD = 0,          /* gc_conv_fwd and gc_conv_fwd_bias */
     GC_OP_BWD_DATA = 1,     /* gc_conv_bwd_data */
     GC_OP_BWD_WEIGHT = 2,   /* gc_conv_bwd_weight */
-    GC_OP_BWD_BIAS = 3      /* gc_conv_bwd_bias */
+    GC_OP_BWD_BIAS = 3,     /* gc_conv_bwd_bias */
+    GC_OP_BWD = 4           /* gc_conv_bwd */
 } gc_op;
 
 /* Problem size.  No padding, dilation 1, one group. */
@@ -126,6 +127,20 @@ int gc_conv_bwd_data(const void *dy, const void *w, const void *y_mask, void *dx
 int gc_conv_bwd_weight(const void *x, const void *dy, const void *y_mask, void *dw,
                        void *workspace, size_t ws_bytes,
                        const gc_conv_desc *d, int relu, int dtype, void *stream);
+
+/* The whole backward of a layer in one call: dx as gc_conv_bwd_data and dw
+ * as gc_conv_bwd_weight compute them, with the same arguments and the same
+ * results bit for bit.  The PR page times d_input and wgrad together as one
+ * "backward"; this entry point runs them with fewer launches: for bf16
+ * shapes with a fused plan, one pre-pass launch (dz regrouping for wgrad and
+ * weight packing for d_input), then the two main kernels -- in one launch
+ * holding both grids side by side where the d_input grid fits the chip in
+ * one round, else one after the other -- and the fixed-order reduction of
+ * wgrad's partials; for other shapes the two calls one after the other.  The workspace
+ * (gc_conv_workspace_bytes(GC_OP_BWD, ...)) must be 256-byte aligned. */
+int gc_conv_bwd(const void *x, const void *w, const void *dy, const void *y_mask, void *dx,
+                void *dw, void *workspace, size_t ws_bytes,
+                const gc_conv_desc *d, int relu, int dtype, void *stream);
 
 /* Human-readable name of a status code. */
 const char *gc_status_string(int status);

@@ -199,3 +199,42 @@ def test_fastdiv_rejects_bad_args():
 
 def test_version():
     assert gb.lib().gc_version() >= 100
+
+
+def _bwd(*ptrs, desc, relu, dtype, ws=None, ws_bytes=0):
+    return gb.lib().gc_conv_bwd(*ptrs, ws, ws_bytes, ctypes.byref(desc), relu, dtype, None)
+
+
+L2 = gb.make_desc(1024, 128, 3, 4, 128, 3, 3, 1)
+
+
+@pytest.mark.parametrize("dtype", [gb.GC_F32, gb.GC_BF16])
+def test_bwd_argument_errors(dtype):
+    F = FAKE
+    for i in range(5):      # each of x, w, dy, dx, dw missing
+        ptrs = [F, F, F, F, F]
+        ptrs[i] = None
+        x, w, dy, dx, dw = ptrs
+        assert _bwd(x, w, dy, F, dx, dw, desc=L1, relu=1, dtype=dtype) == gb.GC_ERR_INVALID_ARG
+    assert _bwd(F, F, F, None, F, F, desc=L1, relu=1, dtype=dtype) == gb.GC_ERR_INVALID_ARG
+    assert _bwd(F, F, F, F, F, F, desc=L2, relu=0, dtype=dtype) == gb.GC_ERR_INVALID_ARG
+    assert _bwd(F, F, F, F, F, F, desc=L1, relu=3, dtype=dtype) == gb.GC_ERR_INVALID_ARG
+    for d, relu, m in ((L1, 1, F), (L2, 0, None)):
+        need = gb.gc_conv_workspace_bytes(gb.GC_OP_BWD, d, dtype)
+        assert need > 0
+        assert _bwd(F, F, F, m, F, F, desc=d, relu=relu, dtype=dtype) == gb.GC_ERR_WORKSPACE
+        assert _bwd(F, F, F, m, F, F, desc=d, relu=relu, dtype=dtype,
+                    ws=F, ws_bytes=need - 1) == gb.GC_ERR_WORKSPACE
+        off = ctypes.c_void_p(0x10010)     # 16- but not 256-byte aligned
+        assert _bwd(F, F, F, m, F, F, desc=d, relu=relu, dtype=dtype,
+                    ws=off, ws_bytes=need) == gb.GC_ERR_WORKSPACE
+
+
+def test_bwd_workspace_covers_both_passes():
+    for d in (L1, L2, gb.make_desc(16384, 59, 11, 15, 128, 5, 5, 3),
+              gb.make_desc(16384, 128, 3, 4, 128, 3, 3, 1), gb.make_desc(3, 2, 5, 5, 3, 2, 2, 1)):
+        for dt in (gb.GC_F32, gb.GC_BF16):
+            nd = gb.gc_conv_workspace_bytes(gb.GC_OP_BWD_DATA, d, dt)
+            nw = gb.gc_conv_workspace_bytes(gb.GC_OP_BWD_WEIGHT, d, dt)
+            n = gb.gc_conv_workspace_bytes(gb.GC_OP_BWD, d, dt)
+            assert max(nd, nw) <= n <= nd + nw + 256, (d.B, d.IC, dt, nd, nw, n)

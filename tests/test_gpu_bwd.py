@@ -1,0 +1,107 @@
+"""GPU tests of gc_conv_bwd, the whole backward of a layer in one call.
+
+It must give dx and dw bit for bit equal to gc_conv_bwd_data followed by
+gc_conv_bwd_weight (bf16 shapes with a fused plan run the same kernel bodies
+in fewer launches; other shapes make the two calls), and so match the oracle
+to the same tolerance.  The layer shapes are those of the policy network at
+B=1024 and of the two-layer chain at B=16384.
+"""
+import numpy as np
+import pytest
+import torch
+
+from backward_implicit_gemm_amd import binding as gb
+from backward_implicit_gemm_amd import inputs
+
+from parity import TOL, Layer, draw, f64, oracle_layer, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    gb.lib()
+
+
+def _both(layer, dtype, x, w, dy):
+    """(y, dx, dw) from gc_conv_bwd and (dx, dw) from the separate calls."""
+    dev = "cuda"
+    td = inputs.torch_dtype(dtype)
+    conv = gb.Conv(layer.x_shape, layer.w_shape, layer.stride, layer.relu, td, dev)
+    xd, wd, dyd = x.to(dev), w.to(dev), dy.to(dev)
+    y = torch.empty(layer.y_shape, dtype=td, device=dev)
+    conv.fwd(xd, wd, y)
+    dx = torch.full(layer.x_shape, float("nan"), dtype=td, device=dev)
+    dw = torch.full(layer.w_shape, float("nan"), dtype=td, device=dev)
+    conv.bwd(xd, wd, dyd, y, dx, dw)
+    dx2 = torch.full_like(dx, float("nan"))
+    dw2 = torch.full_like(dw, float("nan"))
+    conv.bwd_data(dyd, wd, y, dx2)
+    conv.bwd_weight(xd, dyd, y, dw2)
+    torch.cuda.synchronize()
+    return y, dx, dw, dx2, dw2
+
+
+def _bits_equal(a, b):
+    view = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
+    return torch.equal(a.view(view), b.view(view))
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3], ids=[w.name for w in inputs.WORKLOADS[:4]])
+def test_workload_bwd_matches_separate_calls_and_oracle(idx):
+    wl = inputs.WORKLOADS[idx]
+    L = wl.layers[0]
+    layer = Layer.of(L)
+    x, w, dy = inputs.layer_inputs(L, wl.seeds, wl.dtype)
+    y, dx, dw, dx2, dw2 = _both(layer, wl.dtype, x, w, dy)
+    assert _bits_equal(dx, dx2) and _bits_equal(dw, dw2)
+    _, dx_ref, dw_ref = oracle_layer(layer, x, w, dy, y)
+    edx, edw = rel_err(f64(dx), dx_ref), rel_err(f64(dw), dw_ref)
+    print(f"{wl.name}: gc_conv_bwd dx={edx:.2e} dw={edw:.2e}", flush=True)
+    assert edx <= TOL[wl.dtype] and edw <= TOL[wl.dtype]
+
+
+@pytest.mark.parametrize("layer_idx", [0, 1], ids=["conv1", "conv2"])
+def test_chain_shapes_b16384_match_separate_calls(layer_idx):
+    wl = inputs.WORKLOADS[4]
+    layer = Layer.of(wl.layers[layer_idx])
+    x, w, dy = draw(layer, (71 + layer_idx, 72, 73), "bf16")
+    _, dx, dw, dx2, dw2 = _both(layer, "bf16", x, w, dy)
+    assert _bits_equal(dx, dx2) and _bits_equal(dw, dw2)
+    assert torch.isfinite(dx.float()).all() and torch.isfinite(dw.float()).all()
+
+
+SHAPES = [
+    (17, 59, 11, 15, 128, 5, 5, 3),
+    (37, 128, 3, 4, 96, 3, 3, 1),
+    (3, 3, 7, 8, 4, 3, 3, 2),
+    (2, 65, 10, 10, 33, 3, 2, 4),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=["x".join(map(str, s)) for s in SHAPES])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("relu", [0, 1])
+def test_bwd_shapes(shape, dtype, relu):
+    layer = Layer(*shape, relu)
+    x, w, dy = draw(layer, (sum(shape), 8, 9 + relu), dtype)
+    y, dx, dw, dx2, dw2 = _both(layer, dtype, x, w, dy)
+    assert _bits_equal(dx, dx2) and _bits_equal(dw, dw2)
+    _, dx_ref, dw_ref = oracle_layer(layer, x, w, dy, y)
+    assert rel_err(f64(dx), dx_ref) <= TOL[dtype] and rel_err(f64(dw), dw_ref) <= TOL[dtype]
+
+
+def test_bwd_repeated_calls_are_identical():
+    wl = inputs.WORKLOADS[2]     # layer 1, bf16: the fused path
+    L = wl.layers[0]
+    layer = Layer.of(L)
+    x, w, dy = inputs.layer_inputs(L, wl.seeds, wl.dtype)
+    y, dx, dw, _, _ = _both(layer, wl.dtype, x, w, dy)
+    conv = gb.Conv(layer.x_shape, layer.w_shape, layer.stride, layer.relu, torch.bfloat16, "cuda")
+    xd, wd, dyd = x.cuda(), w.cuda(), dy.cuda()
+    for _ in range(3):
+        dx3, dw3 = torch.empty_like(dx), torch.empty_like(dw)
+        conv.bwd(xd, wd, dyd, y, dx3, dw3)
+        torch.cuda.synchronize()
+        assert _bits_equal(dx3, dx) and _bits_equal(dw3, dw)
+    assert np.isfinite(f64(dw)).all()
