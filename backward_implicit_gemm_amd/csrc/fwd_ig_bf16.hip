@@ -114,43 +114,34 @@ __global__ void __launch_bounds__(64 * NW) fwd_ig_bf16(FwdBfArgs a)
         ring[j] = j < NFRAG ? wf_wave[size_t(j) * 64] : make_uint4(0, 0, 0, 0);
 
     // x staging, one unit per thread per phase: unit u = (cg, img, 8-pixel
-    // block) of the phase's channel groups; 8 loads of 8 pixels, an 8x8
-    // register transpose, 8 stores of 8 channels (channels innermost).
-    // Images past the batch and channels past IC get zeros, so every LDS slot
-    // an MFMA reads is written (row and image padding slots are never read).
+    // block) of the phase's channel groups; 8 loads of 8 pixels (one per
+    // channel), an 8x8 register transpose, 8 stores of 8 channels (channels
+    // innermost).  The loads are buffer loads without branches, so they stay
+    // in flight through the phase's MFMAs: channels past IC and images past
+    // the batch use an offset past the end of x and read zeros, and the last
+    // block of a plane is moved back to end with it (HW >= 8), rewriting some
+    // of its neighbour's slots with the same values.  Every LDS slot an MFMA
+    // reads is written (row and image padding slots are never read).
     const int units_per_cg = a.G * a.nblk;
+    const int u_blk = tid % a.nblk, u_img = (tid / a.nblk) % a.G, u_cgl = tid / units_per_cg;
+    const int u_w0 = min(8 * u_blk, g.HW - 8);
+    const bool u_img_ok = u_img < gimg;
+    const uint32_t plane_bytes = uint32_t(g.HW) * 2;
+    const uint32_t u_off = (uint32_t(b0 + u_img) * g.IC * g.HW + u_w0) * 2;
+    const __amdgpu_buffer_rsrc_t xrs = tensor_rsrc(a.x, uint32_t(g.B) * g.IC * plane_bytes);
     uint32_t in[8][4];
-    int u_cg = 0, u_img = 0, u_pix = 0, u_npix = 0;
+    int u_cg = 0;
     bool u_on = false;
     auto fetch_x = [&](int ph) {
         const int cg0 = ph * CPP;
         const int ncg = min(CPP, NCG - cg0);
-        const int u = tid;
-        u_on = u < ncg * units_per_cg;
-        const int blk = u % a.nblk;
-        const int rest = u / a.nblk;
-        u_img = rest % a.G;
-        u_cg = cg0 + rest / a.G;
-        u_pix = blk * 8;
-        u_npix = min(8, g.HW - u_pix);
+        u_on = u_cgl < ncg;
+        u_cg = cg0 + u_cgl;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             const int ic = u_cg * 8 + c;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (u_on && u_img < gimg && ic < g.IC) {
-                const u16 *src = a.x + (size_t(b0 + u_img) * g.IC + ic) * g.HW + u_pix;
-                if (u_npix == 8) {
-                    v = ldg16_any(src);
-                } else {
-                    u16 e[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) e[i] = i < u_npix ? src[i] : u16(0);
-                    v.x = e[0] | (uint32_t(e[1]) << 16);
-                    v.y = e[2] | (uint32_t(e[3]) << 16);
-                    v.z = e[4] | (uint32_t(e[5]) << 16);
-                    v.w = e[6] | (uint32_t(e[7]) << 16);
-                }
-            }
+            const uint4 v = bload16u(xrs, u_on && u_img_ok && ic < g.IC ? u_off + uint32_t(ic) * plane_bytes
+                                                                       : kOffNone);
             in[c][0] = v.x; in[c][1] = v.y; in[c][2] = v.z; in[c][3] = v.w;
         }
     };
@@ -159,7 +150,7 @@ __global__ void __launch_bounds__(64 * NW) fwd_ig_bf16(FwdBfArgs a)
         // word j of pixel p = channels (2j, 2j+1) at pixel p; pixel (ih, iw)
         // lives in slot ih*WP + iw of its image
         uint4 *dst = xs + u_cg * gstride + u_img * a.IS;
-        int ih = u_pix / g.W, iw = u_pix - ih * g.W;
+        int ih = u_w0 / g.W, iw = u_w0 - ih * g.W;
 #pragma unroll
         for (int pp = 0; pp < 8; ++pp) {
             const int wi = pp >> 1;
@@ -170,7 +161,7 @@ __global__ void __launch_bounds__(64 * NW) fwd_ig_bf16(FwdBfArgs a)
                 o[j] = (pp & 1) ? ((lo_src >> 16) | (hi_src & 0xFFFF0000u))
                                 : ((lo_src & 0xFFFFu) | (hi_src << 16));
             }
-            if (pp < u_npix) dst[ih * a.WP + iw] = make_uint4(o[0], o[1], o[2], o[3]);
+            dst[ih * a.WP + iw] = make_uint4(o[0], o[1], o[2], o[3]);
             if (++iw == g.W) { iw = 0; ++ih; }
         }
     };
@@ -328,6 +319,9 @@ void pick_lds_pitch(const Geom &g, int G, int MB, int TS, int &WP_out, int &IS_o
 bool plan_fwd_ig_bf16(const Geom &g, FwdBfPlan &p)
 {
     if (g.P > 64 || g.KK > 36) return false;
+    // staging windows of 8 pixels inside a plane; x addressed by 32-bit
+    // buffer offsets
+    if (g.HW < 8 || size_t(g.B) * g.IC * g.HW * 2 >= (size_t(1) << 31)) return false;
     const int TS = (g.KK + 3) / 4;
     // Few rows per image (layer-2-like): 4 waves and twice the images, so each
     // workgroup streams half the weights for twice the rows.
@@ -355,6 +349,16 @@ bool plan_fwd_ig_bf16(const Geom &g, FwdBfPlan &p)
         return true;
     }
     return false;
+}
+
+hipError_t launch_pack_w_fwd_bf16(const Geom &g, int NCG, int TS, int nblocks, const void *w,
+                                  void *wf, size_t ws_bytes, hipStream_t s)
+{
+    const int total = nblocks * NCG * TS * 64;
+    if (size_t(total) * 16 > ws_bytes) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pack_w_fwd_bf16, dim3(std::min((total + 255) / 256, 1024)), dim3(256), 0, s,
+                       (const u16 *)w, (uint4 *)wf, g, NCG, TS, total);
+    return hipGetLastError();
 }
 
 hipError_t launch_fwd_ig_bf16(const Geom &g, const FwdBfPlan &p, const void *x, const void *w,

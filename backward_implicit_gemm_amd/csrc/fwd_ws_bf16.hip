@@ -1,0 +1,286 @@
+// fwd_ws_bf16.hip -- forward convolution, bf16 storage, fp32 accumulation,
+// with loader waves and MFMA waves.
+//
+// Same contraction and operand layout as fwd_ig_bf16.hip: y = x * w as an
+// implicit GEMM on v_mfma_f32_16x16x32_bf16, the reduction ordered (channel
+// group of 8, tap, channel) so that both operands are single 16-byte reads;
+// x staged channels-innermost [group][image][pixel][8] through 8x8 register
+// transposes; weights pre-packed into fragment order and streamed from L2
+// through register rings.
+//
+// What differs is who waits for what.  A wave's vector-memory counter is in
+// order: when one wave issues both the x staging loads (from HBM) and the
+// weight-ring loads (from L2), every ring wait after an x load also waits for
+// that x load, and the MFMAs stall on HBM latency.  Here the two never share
+// a wave:
+//   * 4 loader waves issue the buffer loads of the whole x tile at once (one
+//     register set per staging phase; channels past IC and images past the
+//     batch use an offset past the end of x and read zeros; the last 8-pixel
+//     block of a plane is moved back to end with it), then transpose and store
+//     phase after phase, with a barrier after each;
+//   * 4 MFMA waves (one per SIMD) each own NBW 16-channel blocks, stream their
+//     weight fragments, and start on phase ph as soon as its barrier passes.
+// With NBW = 2 each A fragment read from LDS feeds two MFMAs.  The whole x
+// tile has its own LDS, so no phase waits for a buffer to drain.
+#include "gc_kernels.h"
+#include "ig_common.h"
+
+namespace gc {
+
+void pick_lds_pitch(const Geom &g, int G, int MB, int TS, int &WP_out, int &IS_out);
+
+namespace {
+
+typedef unsigned short u16;
+
+constexpr int kMfmaWaves = 4, kLoadWaves = 4;
+constexpr int kThreads = 64 * (kMfmaWaves + kLoadWaves);
+constexpr int kLoaders = 64 * kLoadWaves;
+
+struct FwdWsArgs {
+    Geom g;
+    const u16 *x;
+    const uint4 *wf;
+    const u16 *bias;
+    u16 *y;
+    int relu;
+    int G;        // images per workgroup
+    int WP;       // LDS pixel slots per image row (>= W)
+    int IS;       // LDS pixel slots per image (>= H*WP)
+    int nblk;     // 8-pixel blocks per image plane
+};
+
+template <int NBW, int MB, int TS, int NCG, int CPP, int D>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) fwd_ws_bf16(FwdWsArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint4 lds4[];
+    const Geom &g = a.g;
+    constexpr int NPH = (NCG + CPP - 1) / CPP;
+    constexpr int NFRAG = NCG * TS;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b0 = blockIdx.x * a.G;
+    const int gimg = min(a.G, g.B - b0);
+    const int gstride = a.G * a.IS;                  // 16-byte slots per channel group
+
+    if (wave >= kMfmaWaves) {
+        // ---- loader waves: unit (channel group, image, 8-pixel block) ----
+        const int lt = tid - 64 * kMfmaWaves;
+        const int units_per_cg = a.G * a.nblk;
+        const int u_blk = lt % a.nblk, u_img = (lt / a.nblk) % a.G, u_cgl = lt / units_per_cg;
+        const bool u_unit = u_cgl < CPP;
+        const int u_w0 = min(8 * u_blk, g.HW - 8);
+        const bool img_ok = u_img < gimg;
+        const uint32_t plane = uint32_t(g.HW) * 2;
+        const uint32_t u_off = (uint32_t(b0 + u_img) * g.IC * g.HW + u_w0) * 2;
+        const __amdgpu_buffer_rsrc_t xrs = tensor_rsrc(a.x, uint32_t(g.B) * g.IC * plane);
+        uint32_t in[NPH][8][4];
+#pragma unroll
+        for (int ph = 0; ph < NPH; ++ph) {
+            const int cg = ph * CPP + u_cgl;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const int ic = cg * 8 + c;
+                const bool ok = u_unit && cg < NCG && img_ok && ic < g.IC;
+                const uint4 v = bload16u(xrs, ok ? u_off + uint32_t(ic) * plane : kOffNone);
+                in[ph][c][0] = v.x; in[ph][c][1] = v.y; in[ph][c][2] = v.z; in[ph][c][3] = v.w;
+            }
+        }
+        const int ih0 = u_w0 / g.W, iw0 = u_w0 - ih0 * g.W;
+#pragma unroll
+        for (int ph = 0; ph < NPH; ++ph) {
+            const int cg = ph * CPP + u_cgl;
+            if (u_unit && cg < NCG) {
+                // word j of pixel p = channels (2j, 2j+1) at pixel p
+                uint4 *dst = lds4 + cg * gstride + u_img * a.IS;
+                int ih = ih0, iw = iw0;
+#pragma unroll
+                for (int pp = 0; pp < 8; ++pp) {
+                    const int wi = pp >> 1;
+                    uint32_t o[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t lo_src = in[ph][2 * j][wi], hi_src = in[ph][2 * j + 1][wi];
+                        o[j] = (pp & 1) ? ((lo_src >> 16) | (hi_src & 0xFFFF0000u))
+                                        : ((lo_src & 0xFFFFu) | (hi_src << 16));
+                    }
+                    dst[ih * a.WP + iw] = make_uint4(o[0], o[1], o[2], o[3]);
+                    if (++iw == g.W) { iw = 0; ++ih; }
+                }
+            }
+            __syncthreads();                         // phase ph is in LDS
+        }
+        return;
+    }
+
+    // ---- MFMA waves: NBW 16-channel blocks each ----
+    const int nb0 = (blockIdx.y * kMfmaWaves + wave) * NBW;
+    const uint4 *wf_wave = a.wf + size_t(nb0) * NFRAG * 64 + lane;
+    // fragment f of block j streams through ring[j][f % D], D fragments ahead
+    uint4 ring[NBW][D];
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+        for (int i = 0; i < D; ++i)
+            ring[j][i] = i < NFRAG ? wf_wave[(size_t(j) * NFRAG + i) * 64] : make_uint4(0, 0, 0, 0);
+
+    const int rows = gimg * g.P;
+    int rowoff[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int r = mb * 16 + (lane & 15);
+        rowoff[mb] = 0;
+        if (r < rows) {
+            uint32_t img, pp, oh, ow;
+            fdivmod(r, g.fd_P, img, pp);
+            fdivmod(pp, g.fd_OW, oh, ow);
+            rowoff[mb] = int(img) * a.IS + int(oh) * g.S * a.WP + int(ow) * g.S;
+        }
+    }
+    int toff[TS];
+#pragma unroll
+    for (int s = 0; s < TS; ++s) {
+        const int t = 4 * s + (lane >> 4);
+        toff[s] = 0;
+        if (t < g.KK) {
+            uint32_t kh, kw;
+            fdivmod(t, g.fd_KW, kh, kw);
+            toff[s] = int(kh) * a.WP + int(kw);
+        }
+    }
+
+    f32x4 acc[NBW][MB];
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[j][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int ph = 0; ph < NPH; ++ph) {
+        __syncthreads();                             // wait for phase ph
+#pragma unroll
+        for (int cg = ph * CPP; cg < (ph + 1) * CPP && cg < NCG; ++cg) {
+            const uint4 *xb = lds4 + cg * gstride;
+            uint4 af[TS][MB];
+#pragma unroll
+            for (int st = 0; st < TS; ++st)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) af[st][mb] = xb[rowoff[mb] + toff[st]];
+#pragma unroll
+            for (int st = 0; st < TS; ++st) {
+                const int f = cg * TS + st;
+                bf16x8 bv[NBW];
+#pragma unroll
+                for (int j = 0; j < NBW; ++j) {
+                    bv[j] = __builtin_bit_cast(bf16x8, ring[j][f % D]);
+                    if (f + D < NFRAG) ring[j][f % D] = wf_wave[(size_t(j) * NFRAG + f + D) * 64];
+                }
+#pragma unroll
+                for (int j = 0; j < NBW; ++j)
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        acc[j][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, af[st][mb]), bv[j], acc[j][mb], 0, 0, 0);
+            }
+        }
+    }
+
+    // epilogue: row r = mb*16 + 4*(lane/16) + v, column (nb0 + j)*16 + lane%16
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+        const int n = (nb0 + j) * 16 + (lane & 15);
+        if (n >= g.OC) continue;
+        const float bn = a.bias ? __uint_as_float(uint32_t(a.bias[n]) << 16) : 0.f;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = mb * 16 + (lane >> 4) * 4 + v;
+                if (r >= rows) continue;
+                uint32_t img, pp;
+                fdivmod(r, g.fd_P, img, pp);
+                float val = acc[j][mb][v] + bn;
+                if (a.relu && !(val > 0.f)) val = 0.f;
+                a.y[(size_t(b0 + int(img)) * g.OC + n) * g.P + int(pp)] = from_f32<bf16_t>(val);
+            }
+    }
+}
+
+struct FwdWsVariant {
+    int NBW, MB, TS, NCG, CPP;
+    void (*fn)(FwdWsArgs);
+};
+#define WS_V(NBW, MB, TS, NCG, CPP, D) {NBW, MB, TS, NCG, CPP, fwd_ws_bf16<NBW, MB, TS, NCG, CPP, D>}
+const FwdWsVariant kFwdWsVariants[] = {
+    WS_V(2, 3, 7, 8, 3, 12),    // 59 -> 128, 11x15, 5x5, stride 3: 4 images, 48 rows
+    WS_V(2, 1, 7, 8, 8, 12),    // the same layer, one image per workgroup
+    WS_V(1, 1, 3, 16, 16, 16),  // 128 -> 128, 3x4, 3x3: 8 images, 16 rows
+    WS_V(1, 4, 3, 16, 4, 16),   // the same layer at large batch: 32 images
+};
+#undef WS_V
+
+const FwdWsVariant *pick_fwd_ws(int NBW, int MB, int TS, int NCG, int CPP)
+{
+    for (const auto &v : kFwdWsVariants)
+        if (v.NBW == NBW && v.MB == MB && v.TS == TS && v.NCG == NCG && v.CPP == CPP) return &v;
+    return nullptr;
+}
+
+}  // namespace
+
+// G as in fwd_ig_bf16 (the most images that still give 256 workgroups, four
+// for 12-row images); NBW 2 where 64 rows or fewer fill the M blocks, else 1
+// with twice the column tiles; CPP the channel groups the 256 loader threads
+// stage per phase.
+bool plan_fwd_ws_bf16(const Geom &g, FwdWsPlan &p)
+{
+    if (g.P > 64 || g.KK > 36 || g.HW < 8) return false;
+    if (size_t(g.B) * g.IC * g.HW * 2 >= (size_t(1) << 31)) return false;
+    const int TS = (g.KK + 3) / 4;
+    const int NCG = (g.IC + 7) / 8;
+    const int nblk = (g.HW + 7) / 8;
+    double best_fill = -1.0;
+    for (int NBW : {2, 1}) {
+        FwdWsPlan q{};
+        q.NBW = NBW; q.TS = TS; q.NCG = NCG; q.nblk = nblk;
+        q.ntile = (g.OC + 64 * NBW - 1) / (64 * NBW);
+        int G = std::max(1, 64 / g.P);
+        while (G > 1 && ((g.B + G - 1) / G) * q.ntile < 256) --G;
+        if (g.P == 12 && G > 4) G = 4;
+        if (G > g.B) G = g.B;
+        q.G = G;
+        q.MB = (G * g.P + 15) / 16;
+        const int units_per_cg = G * nblk;
+        if (units_per_cg > kLoaders) continue;
+        q.CPP = std::min(NCG, kLoaders / units_per_cg);
+        if (!pick_fwd_ws(NBW, q.MB, TS, NCG, q.CPP)) continue;
+        pick_lds_pitch(g, G, q.MB, TS, q.WP, q.IS);
+        q.lds = sizeof(uint4) * size_t(NCG) * G * q.IS;
+        if (q.lds > 150 * 1024) continue;
+        q.ws_bytes = size_t(q.ntile) * kMfmaWaves * NBW * NCG * TS * 64 * 16;
+        const double fill = double(G * g.P) / (16.0 * q.MB);
+        if (fill > best_fill) {
+            best_fill = fill;
+            p = q;
+        }
+    }
+    return best_fill >= 0.0;
+}
+
+hipError_t launch_fwd_ws_bf16(const Geom &g, const FwdWsPlan &p, const void *x, const void *w,
+                              const void *bias, void *y, void *ws, int relu, hipStream_t s)
+{
+    const FwdWsVariant *v = pick_fwd_ws(p.NBW, p.MB, p.TS, p.NCG, p.CPP);
+    if (!v || p.G * p.nblk * p.CPP > kLoaders || g.HW < 8 || p.G * g.P > 16 * p.MB)
+        return hipErrorInvalidValue;
+    hipError_t e = launch_pack_w_fwd_bf16(g, p.NCG, p.TS, p.ntile * kMfmaWaves * p.NBW, w, ws,
+                                          p.ws_bytes, s);
+    if (e != hipSuccess) return e;
+    FwdWsArgs a{g, (const u16 *)x, (const uint4 *)ws, (const u16 *)bias, (u16 *)y, relu,
+                p.G, p.WP, p.IS, p.nblk};
+    e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(v->fn, dim3((g.B + p.G - 1) / p.G, p.ntile), dim3(kThreads), p.lds, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace gc

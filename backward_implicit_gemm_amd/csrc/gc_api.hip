@@ -97,6 +97,10 @@ bool fwd_f32_rf_plan(const Geom &g, FwdBfPlan &p)
 {
     return use_ig() && cached_plan<FwdBfPlan, plan_fwd_rf_f32>(g, p);
 }
+bool fwd_bf16_ws_plan(const Geom &g, FwdWsPlan &p)
+{
+    return use_ig() && cached_plan<FwdWsPlan, plan_fwd_ws_bf16>(g, p);
+}
 bool fwd_bf16_plan(const Geom &g, FwdBfPlan &p)
 {
     return use_ig() && cached_plan<std::remove_reference_t<decltype(p)>, plan_fwd_ig_bf16>(g, p);
@@ -188,6 +192,8 @@ size_t gc_conv_workspace_bytes(int op, const gc_conv_desc *d, int dtype)
     if (check_desc(d, &g) != GC_OK || !valid_dtype(dtype)) return 0;
     switch (op) {
     case GC_OP_FWD: {
+        FwdWsPlan wp;
+        if (dtype == GC_BF16 && fwd_bf16_ws_plan(g, wp)) return wp.ws_bytes;
         FwdBfPlan p;
         if (dtype == GC_BF16 && fwd_bf16_plan(g, p)) return p.ws_bytes;
         if (dtype == GC_F32 && fwd_f32_rf_plan(g, p)) return p.ws_bytes;
@@ -235,6 +241,12 @@ static int conv_fwd(const void *x, const void *w, const void *bias, void *y, voi
         if (fwd_f32_plan(g, p))
             return hip_status(launch_fwd_ig_f32(g, p, x, w, bias, y, relu, s));
         return hip_status(launch_fwd_generic<float>(g, x, w, bias, y, relu, s));
+    }
+    FwdWsPlan wp;
+    if (fwd_bf16_ws_plan(g, wp)) {
+        if (!workspace || ws_bytes < wp.ws_bytes) return GC_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(workspace) % 16) return GC_ERR_WORKSPACE;
+        return hip_status(launch_fwd_ws_bf16(g, wp, x, w, bias, y, workspace, relu, s));
     }
     FwdBfPlan p;
     if (fwd_bf16_plan(g, p)) {

@@ -42,7 +42,17 @@ hipError_t launch_wgrad_ig(const Geom &g, const WgradIgPlan &p, const void *x, c
 
 // Image-group kernels, bf16 storage.
 struct FwdBfPlan;
+struct FwdWsPlan;
 bool plan_fwd_ig_bf16(const Geom &g, FwdBfPlan &p);
+// packs w into the B-fragment order of the bf16 forward for `nblocks`
+// 16-channel blocks (shared by fwd_ig_bf16 and fwd_ws_bf16)
+hipError_t launch_pack_w_fwd_bf16(const Geom &g, int NCG, int TS, int nblocks, const void *w,
+                                  void *wf, size_t ws_bytes, hipStream_t s);
+// bf16 forward with loader and MFMA waves; plan_* returns false when a shape
+// does not fit it
+bool plan_fwd_ws_bf16(const Geom &g, FwdWsPlan &p);
+hipError_t launch_fwd_ws_bf16(const Geom &g, const FwdWsPlan &p, const void *x, const void *w,
+                              const void *bias, void *y, void *ws, int relu, hipStream_t s);
 hipError_t launch_fwd_ig_bf16(const Geom &g, const FwdBfPlan &p, const void *x, const void *w,
                               const void *bias, void *y, void *ws, int relu, hipStream_t s);
 // Bias gradient db[oc] = sum over (b, oh, ow) of dz (bias_grad.hip): fp32

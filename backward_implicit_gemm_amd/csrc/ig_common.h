@@ -67,6 +67,32 @@ constexpr int IG_NT = 256;   // threads per workgroup (4 waves)
 // completed.  Placed where only loads issued long ago are outstanding, it
 // retires them before later stores are issued, so a later use of the loaded
 // registers does not wait for those stores as well.
+// Buffer resource over a whole tensor of `bytes` bytes (< 2^31): a load
+// whose offset is at or past the end returns zeros, so staging loads need no
+// branches for images past the batch or channels past the tensor.  Word 3
+// selects the 32-bit data format of the gfx9 buffer descriptor, with no
+// swizzle and no index stride.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tensor_rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, int(bytes), 0x00020000);
+}
+// 16 bytes at byte offset `off` of the tensor (zeros past its end)
+__device__ __forceinline__ float4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    float4 f;
+    __builtin_memcpy(&f, &v, 16);
+    return f;
+}
+__device__ __forceinline__ uint4 bload16u(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    uint4 u;
+    __builtin_memcpy(&u, &v, 16);
+    return u;
+}
+constexpr uint32_t kOffNone = 0xFFFFFFF0u;   // an offset past the end of every tensor
+
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ---------------------------------------------------------------- forward --
@@ -97,6 +123,21 @@ struct FwdBfPlan {
     int NCG;      // channel groups of 8
     size_t lds;
     size_t ws_bytes;   // packed weights
+};
+
+// bf16 forward with loader and MFMA waves (fwd_ws_bf16.hip).
+struct FwdWsPlan {
+    int NBW;      // 16-channel blocks per MFMA wave (4 MFMA waves)
+    int G;        // images per workgroup
+    int MB;       // 16-row M blocks
+    int TS;       // tap steps: ceil(KH*KW/4)
+    int WP, IS;   // LDS pixel slots per image row / per image
+    int nblk;     // 8-pixel blocks per image plane
+    int NCG;      // channel groups of 8
+    int CPP;      // channel groups per staging phase
+    int ntile;    // column tiles of 64*NBW channels
+    size_t lds;       // the whole x tile
+    size_t ws_bytes;  // packed weights
 };
 
 // ---------------------------------------------------------------- d_input --

@@ -42,21 +42,6 @@ __device__ __forceinline__ float comp(const float4 &v, int i)
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// Buffer resource over a whole tensor of `bytes` bytes: a load whose offset
-// is at or past the end returns zeros.  Word 3 selects the 32-bit data format
-// of the gfx9 buffer descriptor, with no swizzle and no index stride.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tensor_rsrc(const void *p, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, int(bytes), 0x00020000);
-}
-__device__ __forceinline__ float4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    float4 f;
-    __builtin_memcpy(&f, &v, 16);
-    return f;
-}
-constexpr uint32_t kOffNone = 0xFFFFFFF0u;   // an offset past the end of every tensor
 
 template <int NBWV, bool RELU>
 __global__ void __launch_bounds__(1024) wgrad_rf_f32(WgradRfArgs a)
