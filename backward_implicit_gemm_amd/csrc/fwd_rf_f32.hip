@@ -289,6 +289,16 @@ bool plan_fwd_rf_f32(const Geom &g, FwdBfPlan &p)
     return false;
 }
 
+hipError_t launch_pack_w_fwd_f32(const Geom &g, int NCG, int TS, int nblocks, const void *w,
+                                 void *wf, size_t ws_bytes, hipStream_t s)
+{
+    const int total = nblocks * NCG * TS * 64;
+    if (size_t(total) * 16 > ws_bytes) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pack_w_fwd_f32, dim3(std::min((total + 255) / 256, 1024)), dim3(256), 0, s,
+                       (const float *)w, (float4 *)wf, g, NCG, TS, total);
+    return hipGetLastError();
+}
+
 hipError_t launch_fwd_rf_f32(const Geom &g, const FwdBfPlan &p, const void *x, const void *w,
                              const void *bias, void *y, void *ws, int relu, hipStream_t s)
 {

@@ -1,0 +1,288 @@
+// fwd_ws_f32.hip -- forward convolution, fp32 storage, fp32 MFMA
+// (v_mfma_f32_16x16x4_f32), with loader waves and MFMA waves.
+//
+// Same contraction and operand layout as fwd_rf_f32.hip: the reduction in
+// blocks of 16 k = 4 channels x 4 taps, so a lane's four MFMA steps read four
+// consecutive channels at one tap: x staged channels-innermost
+// [group][image][pixel][4] through 4x4 register transposes, weights
+// pre-packed into float4 fragments and streamed from L2 through a register
+// ring.  The roles are split as in fwd_ws_bf16.hip, because a wave's
+// vector-memory counter is in order and the x loads (HBM) would otherwise
+// hold up every later weight-ring wait (L2):
+//   * NWM loader waves: branch-free buffer loads (channels past IC and images
+//     past the batch read zeros past the end of x; the last 4-pixel block of
+//     a plane is moved back to end with it), register transposes, LDS stores;
+//   * NWM MFMA waves, one 16-channel block each, A fragments read one tap step
+//     ahead of their MFMAs.
+// The fp32 x tile is too large for LDS at once, so the staging phases go
+// through two buffers: in iteration ph the MFMA waves consume phase ph while
+// the loaders store phase ph+1 (loaded during the previous iteration) into
+// the other buffer and issue the loads of phase ph+2; one barrier per
+// iteration hands the buffers over.
+#include "gc_kernels.h"
+#include "ig_common.h"
+
+namespace gc {
+
+void pick_lds_pitch(const Geom &g, int G, int MB, int TS, int &WP_out, int &IS_out);
+
+namespace {
+
+struct FwdWsF32Args {
+    Geom g;
+    const float *x;
+    const float4 *wf;
+    const float *bias;
+    float *y;
+    int relu;
+    int G;        // images per workgroup
+    int WP;       // LDS pixel slots per image row (>= W)
+    int IS;       // LDS pixel slots per image (>= H*WP)
+    int nblk;     // 4-pixel blocks per image plane
+};
+
+__device__ __forceinline__ float comp(const float4 &v, int i)
+{
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// GS: LDS slots per staged channel group, a compile-time bound on G*IS, so
+// that the offsets of the groups and buffers are instruction immediates.
+template <int NWM, int MB, int TS, int NCG, int CPP, int D, int GS>
+__global__ void __launch_bounds__(128 * NWM) __attribute__((amdgpu_waves_per_eu(1, NWM / 2)))
+fwd_ws_f32(FwdWsF32Args a)
+{
+    extern __shared__ __attribute__((aligned(16))) float4 lds4f[];
+    const Geom &g = a.g;
+    constexpr int NPH = (NCG + CPP - 1) / CPP;
+    constexpr int NFRAG = NCG * TS;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b0 = blockIdx.x * a.G;
+    const int gimg = min(a.G, g.B - b0);
+    constexpr int gstride = GS;                     // float4 slots per channel group
+    constexpr int bufsz = CPP * gstride;            // one phase buffer
+
+    if (wave >= NWM) {
+        // ---- loader waves: unit (channel group, image, 4-pixel block) ----
+        const int lt = tid - 64 * NWM;
+        const int units_per_cg = a.G * a.nblk;
+        const int u_blk = lt % a.nblk, u_img = (lt / a.nblk) % a.G, u_cgl = lt / units_per_cg;
+        const bool u_unit = u_cgl < CPP;
+        const int u_w0 = min(4 * u_blk, g.HW - 4);
+        const bool img_ok = u_img < gimg;
+        const uint32_t plane = uint32_t(g.HW) * 4;
+        const uint32_t u_off = (uint32_t(b0 + u_img) * g.IC * g.HW + u_w0) * 4;
+        const __amdgpu_buffer_rsrc_t xrs = tensor_rsrc(a.x, uint32_t(g.B) * g.IC * plane);
+        const int ih0 = u_w0 / g.W, iw0 = u_w0 - ih0 * g.W;
+        float4 in[4];
+        auto fetch = [&](int ph) {
+            const int cg = ph * CPP + u_cgl;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int ic = cg * 4 + c;
+                const bool ok = u_unit && cg < NCG && img_ok && ic < g.IC;
+                in[c] = bload16(xrs, ok ? u_off + uint32_t(ic) * plane : kOffNone);
+            }
+        };
+        auto stash = [&](int ph) {
+            const int cg = ph * CPP + u_cgl;
+            if (!u_unit || cg >= NCG) return;
+            float4 *dst = lds4f + (ph & 1) * bufsz + u_cgl * gstride + u_img * a.IS;
+            int ih = ih0, iw = iw0;
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+                dst[ih * a.WP + iw] = make_float4(comp(in[0], pp), comp(in[1], pp), comp(in[2], pp),
+                                                  comp(in[3], pp));
+                if (++iw == g.W) { iw = 0; ++ih; }
+            }
+        };
+        fetch(0);
+        stash(0);
+        if (NPH > 1) fetch(1);
+        __syncthreads();
+        for (int ph = 0; ph < NPH; ++ph) {
+            if (ph + 1 < NPH) {
+                stash(ph + 1);
+                if (ph + 2 < NPH) fetch(ph + 2);
+            }
+            __syncthreads();
+        }
+        return;
+    }
+
+    // ---- MFMA waves: one 16-channel block each ----
+    const int nb = blockIdx.y * NWM + wave;
+    // fragment f of this wave's block: byte offset w_vo + f*1024 of the packed
+    // weights (the per-fragment part is a constant, so no address registers)
+    const __amdgpu_buffer_rsrc_t wrs = tensor_rsrc(a.wf, uint32_t(gridDim.y) * NWM * NFRAG * 1024);
+    const uint32_t w_vo = (uint32_t(nb) * NFRAG * 64 + lane) * 16;
+    float4 ring[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+        ring[i] = i < NFRAG ? bload16s(wrs, w_vo, i * 1024) : make_float4(0.f, 0.f, 0.f, 0.f);
+
+    const int rows = gimg * g.P;
+    int rowoff[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int r = mb * 16 + (lane & 15);
+        rowoff[mb] = 0;
+        if (r < rows) {
+            uint32_t img, pp, oh, ow;
+            fdivmod(r, g.fd_P, img, pp);
+            fdivmod(pp, g.fd_OW, oh, ow);
+            rowoff[mb] = int(img) * a.IS + int(oh) * g.S * a.WP + int(ow) * g.S;
+        }
+    }
+    int toff[TS];
+#pragma unroll
+    for (int s = 0; s < TS; ++s) {
+        const int t = 4 * s + (lane >> 4);
+        toff[s] = 0;
+        if (t < g.KK) {
+            uint32_t kh, kw;
+            fdivmod(t, g.fd_KW, kh, kw);
+            toff[s] = int(kh) * a.WP + int(kw);
+        }
+    }
+
+    f32x4 acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    __syncthreads();                                 // phase 0 staged
+#pragma unroll
+    for (int ph = 0; ph < NPH; ++ph) {
+        const float4 *xbuf = lds4f + (ph & 1) * bufsz;
+        // A fragments one tap step ahead of their MFMAs
+        float4 af[2][MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) af[0][mb] = xbuf[rowoff[mb] + toff[0]];
+#pragma unroll
+        for (int cg = ph * CPP; cg < (ph + 1) * CPP && cg < NCG; ++cg) {
+            const float4 *xb = xbuf + (cg - ph * CPP) * gstride;
+#pragma unroll
+            for (int st = 0; st < TS; ++st) {
+                const int f = cg * TS + st;
+                const int cur = ((cg - ph * CPP) * TS + st) & 1;   // step within the phase
+                // the next step's A: same group next tap, or next group's first
+                if (st + 1 < TS) {
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) af[cur ^ 1][mb] = xb[rowoff[mb] + toff[st + 1]];
+                } else if (cg + 1 < (ph + 1) * CPP && cg + 1 < NCG) {
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) af[cur ^ 1][mb] = xb[gstride + rowoff[mb] + toff[0]];
+                }
+                const float4 bv = ring[f % D];
+                if (f + D < NFRAG) ring[f % D] = bload16s(wrs, w_vo, (f + D) * 1024);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(comp(af[cur][mb], j), comp(bv, j),
+                                                                       acc[mb], 0, 0, 0);
+                // keep each step's loads in their place: hoisting later steps'
+                // loads above these MFMAs would only lengthen register lives
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        __syncthreads();                             // phase ph done, ph+1 staged
+    }
+
+    // epilogue: row r = mb*16 + 4*(lane/16) + v, column nb*16 + lane%16
+    const int n = nb * 16 + (lane & 15);
+    if (n < g.OC) {
+        const float bn = a.bias ? a.bias[n] : 0.f;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = mb * 16 + (lane >> 4) * 4 + v;
+                if (r >= rows) continue;
+                uint32_t img, pp;
+                fdivmod(r, g.fd_P, img, pp);
+                float val = acc[mb][v] + bn;
+                if (a.relu && !(val > 0.f)) val = 0.f;
+                a.y[(size_t(b0 + int(img)) * g.OC + n) * g.P + int(pp)] = val;
+            }
+    }
+}
+
+struct FwdWsF32Variant {
+    int NWM, MB, TS, NCG, CPP, GS;
+    void (*fn)(FwdWsF32Args);
+};
+#define WF_V(NWM, MB, TS, NCG, CPP, GS) \
+    {NWM, MB, TS, NCG, CPP, GS, fwd_ws_f32<NWM, MB, TS, NCG, CPP, 8, GS>}
+const FwdWsF32Variant kFwdWsF32Variants[] = {
+    WF_V(8, 3, 7, 15, 3, 960),    // 59 -> 128, 11x15, 5x5, stride 3: 4 images, 48 rows
+    WF_V(8, 1, 7, 15, 12, 240),   // the same layer, one image per workgroup
+    WF_V(4, 1, 3, 32, 10, 128),   // 128 -> 128, 3x4, 3x3: 8 images, 16 rows
+    WF_V(4, 1, 3, 32, 32, 16),    // the same layer, one image per workgroup
+};
+#undef WF_V
+
+const FwdWsF32Variant *pick_fwd_ws_f32(int NWM, int MB, int TS, int NCG, int CPP, int gslots)
+{
+    for (const auto &v : kFwdWsF32Variants)
+        if (v.NWM == NWM && v.MB == MB && v.TS == TS && v.NCG == NCG && v.CPP == CPP && gslots <= v.GS)
+            return &v;
+    return nullptr;
+}
+
+}  // namespace
+
+// G as in fwd_rf_f32 (the most images that still give 256 workgroups, four
+// for 12-row images); 8 MFMA waves (128 channels per workgroup) for
+// layer-1-like shapes, 4 (64 channels, twice the column tiles) where an image
+// has 4 rows or fewer; CPP the channel groups the loader threads stage per
+// phase.
+bool plan_fwd_ws_f32(const Geom &g, FwdWsPlan &p)
+{
+    if (g.P > 64 || g.KK > 36 || g.HW < 4) return false;
+    if (size_t(g.B) * g.IC * g.HW * 4 >= (size_t(1) << 31)) return false;
+    FwdWsPlan q{};
+    q.NWM = g.P <= 4 ? 4 : 8;
+    q.NBW = 1;
+    q.TS = (g.KK + 3) / 4;
+    q.NCG = (g.IC + 3) / 4;
+    q.nblk = (g.HW + 3) / 4;
+    q.ntile = (g.OC + 16 * q.NWM - 1) / (16 * q.NWM);
+    int G = std::max(1, 64 / g.P);
+    while (G > 1 && ((g.B + G - 1) / G) * q.ntile < 256) --G;
+    if (g.P == 12 && G > 4) G = 4;
+    if (G > g.B) G = g.B;
+    q.G = G;
+    q.MB = (G * g.P + 15) / 16;
+    const int loaders = 64 * q.NWM;
+    const int units_per_cg = G * q.nblk;
+    if (units_per_cg > loaders) return false;
+    q.CPP = std::min(q.NCG, loaders / units_per_cg);
+    pick_lds_pitch(g, G, q.MB, q.TS, q.WP, q.IS);
+    const FwdWsF32Variant *v = pick_fwd_ws_f32(q.NWM, q.MB, q.TS, q.NCG, q.CPP, G * q.IS);
+    if (!v) return false;
+    q.lds = sizeof(float4) * 2 * size_t(q.CPP) * v->GS;
+    if (q.lds > 150 * 1024) return false;
+    q.ws_bytes = size_t(q.ntile) * q.NWM * q.NCG * q.TS * 64 * 16;
+    p = q;
+    return true;
+}
+
+hipError_t launch_fwd_ws_f32(const Geom &g, const FwdWsPlan &p, const void *x, const void *w,
+                             const void *bias, void *y, void *ws, int relu, hipStream_t s)
+{
+    const FwdWsF32Variant *v = pick_fwd_ws_f32(p.NWM, p.MB, p.TS, p.NCG, p.CPP, p.G * p.IS);
+    if (!v || p.G * p.nblk * p.CPP > 64 * p.NWM || g.HW < 4 || p.G * g.P > 16 * p.MB ||
+        p.lds < sizeof(float4) * 2 * size_t(p.CPP) * v->GS)
+        return hipErrorInvalidValue;
+    hipError_t e = launch_pack_w_fwd_f32(g, p.NCG, p.TS, p.ntile * p.NWM, w, ws, p.ws_bytes, s);
+    if (e != hipSuccess) return e;
+    FwdWsF32Args a{g, (const float *)x, (const float4 *)ws, (const float *)bias, (float *)y, relu,
+                   p.G, p.WP, p.IS, p.nblk};
+    e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(v->fn, dim3((g.B + p.G - 1) / p.G, p.ntile), dim3(128 * p.NWM), p.lds, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace gc

@@ -97,6 +97,10 @@ bool fwd_f32_rf_plan(const Geom &g, FwdBfPlan &p)
 {
     return use_ig() && cached_plan<FwdBfPlan, plan_fwd_rf_f32>(g, p);
 }
+bool fwd_f32_ws_plan(const Geom &g, FwdWsPlan &p)
+{
+    return use_ig() && cached_plan<FwdWsPlan, plan_fwd_ws_f32>(g, p);
+}
 bool fwd_bf16_ws_plan(const Geom &g, FwdWsPlan &p)
 {
     return use_ig() && cached_plan<FwdWsPlan, plan_fwd_ws_bf16>(g, p);
@@ -194,6 +198,7 @@ size_t gc_conv_workspace_bytes(int op, const gc_conv_desc *d, int dtype)
     case GC_OP_FWD: {
         FwdWsPlan wp;
         if (dtype == GC_BF16 && fwd_bf16_ws_plan(g, wp)) return wp.ws_bytes;
+        if (dtype == GC_F32 && fwd_f32_ws_plan(g, wp)) return wp.ws_bytes;
         FwdBfPlan p;
         if (dtype == GC_BF16 && fwd_bf16_plan(g, p)) return p.ws_bytes;
         if (dtype == GC_F32 && fwd_f32_rf_plan(g, p)) return p.ws_bytes;
@@ -231,6 +236,12 @@ static int conv_fwd(const void *x, const void *w, const void *bias, void *y, voi
         return GC_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == GC_F32) {
+        FwdWsPlan wp;
+        if (fwd_f32_ws_plan(g, wp)) {
+            if (!workspace || ws_bytes < wp.ws_bytes) return GC_ERR_WORKSPACE;
+            if (reinterpret_cast<uintptr_t>(workspace) % 16) return GC_ERR_WORKSPACE;
+            return hip_status(launch_fwd_ws_f32(g, wp, x, w, bias, y, workspace, relu, s));
+        }
         FwdBfPlan rp;
         if (fwd_f32_rf_plan(g, rp)) {
             if (!workspace || ws_bytes < rp.ws_bytes) return GC_ERR_WORKSPACE;

@@ -64,6 +64,14 @@ hipError_t launch_bias_grad(const Geom &g, const void *dy, const void *ym, void 
 // fp32 forward with channels-innermost staging and packed weight fragments
 // (fwd_rf_f32.hip); the plan struct is shared with the bf16 forward.
 bool plan_fwd_rf_f32(const Geom &g, FwdBfPlan &p);
+// packs w into the B-fragment order of the fp32 forward for `nblocks`
+// 16-channel blocks (shared by fwd_rf_f32 and fwd_ws_f32)
+hipError_t launch_pack_w_fwd_f32(const Geom &g, int NCG, int TS, int nblocks, const void *w,
+                                 void *wf, size_t ws_bytes, hipStream_t s);
+// fp32 forward with loader and MFMA waves
+bool plan_fwd_ws_f32(const Geom &g, FwdWsPlan &p);
+hipError_t launch_fwd_ws_f32(const Geom &g, const FwdWsPlan &p, const void *x, const void *w,
+                             const void *bias, void *y, void *ws, int relu, hipStream_t s);
 hipError_t launch_fwd_rf_f32(const Geom &g, const FwdBfPlan &p, const void *x, const void *w,
                              const void *bias, void *y, void *ws, int relu, hipStream_t s);
 bool plan_dgrad_ig_bf16(const Geom &g, DgradBfPlan &p);

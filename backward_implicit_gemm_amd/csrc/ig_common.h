@@ -91,6 +91,23 @@ __device__ __forceinline__ uint4 bload16u(__amdgpu_buffer_rsrc_t r, uint32_t off
     __builtin_memcpy(&u, &v, 16);
     return u;
 }
+// 16 bytes at byte offset voff + soff, soff wave-uniform (a scalar register
+// or a constant, so a sequence of loads from one base costs no vector
+// registers for addresses)
+__device__ __forceinline__ float4 bload16s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    float4 f;
+    __builtin_memcpy(&f, &v, 16);
+    return f;
+}
+__device__ __forceinline__ uint4 bload16us(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    uint4 u;
+    __builtin_memcpy(&u, &v, 16);
+    return u;
+}
 constexpr uint32_t kOffNone = 0xFFFFFFF0u;   // an offset past the end of every tensor
 
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -125,18 +142,19 @@ struct FwdBfPlan {
     size_t ws_bytes;   // packed weights
 };
 
-// bf16 forward with loader and MFMA waves (fwd_ws_bf16.hip).
+// Forward with loader and MFMA waves (fwd_ws_bf16.hip, fwd_ws_f32.hip).
 struct FwdWsPlan {
-    int NBW;      // 16-channel blocks per MFMA wave (4 MFMA waves)
+    int NWM;      // MFMA waves (as many loader waves; fp32 only, bf16 uses 4)
+    int NBW;      // 16-channel blocks per MFMA wave
     int G;        // images per workgroup
     int MB;       // 16-row M blocks
     int TS;       // tap steps: ceil(KH*KW/4)
     int WP, IS;   // LDS pixel slots per image row / per image
-    int nblk;     // 8-pixel blocks per image plane
-    int NCG;      // channel groups of 8
+    int nblk;     // pixel blocks per image plane (8 pixels bf16, 4 fp32)
+    int NCG;      // channel groups (8 channels bf16, 4 fp32)
     int CPP;      // channel groups per staging phase
-    int ntile;    // column tiles of 64*NBW channels
-    size_t lds;       // the whole x tile
+    int ntile;    // column tiles
+    size_t lds;       // the whole x tile (bf16), two phase buffers (fp32)
     size_t ws_bytes;  // packed weights
 };
 
