@@ -3,16 +3,16 @@
 //
 // Same structure as the bf16 d_input kernel: a workgroup owns G whole images
 // (G a multiple of 4) and stages their masked output gradient dz once in LDS
-// as rows m = p*G + img by columns oc; every wave then holds the A fragments
-// of all its rows for the whole reduction over oc in registers (one fp32 per
-// row block and 4-channel step).  Input channels are walked in chunks of CC;
-// for each chunk the column gradient
+// as rows m = p*G + img by columns oc.  Input channels are walked in chunks of
+// CC; for each chunk the column gradient
 //     dcol[m][(icl,kh,kw)] = sum_oc dz[m][oc] * w[oc][c0+icl][kh][kw]
-// is formed by four MFMA waves splitting its 16-column blocks, while the other
-// four waves gather the previous chunk (see the kernel).  The weights are
-// pre-packed into B-fragment order -- [chunk][column block][16-oc step]
-// [lane] x 4 oc, 16 bytes per lane covering four MFMA steps -- and requested
-// one chunk ahead of their use.  dcol goes to LDS column by column and the
+// is formed by eight MFMA waves (two per SIMD), one 16-column block each,
+// while eight gather waves gather the previous chunk (see the kernel).  The
+// reduction over oc runs in blocks of 16 channels, MFMA step j giving lane
+// group q the channel 16*s + 4*q + j, so a lane's A values for four steps are
+// one 16-byte LDS read of its dz row and its B values one 16-byte unit of the
+// weights, pre-packed in that order -- [chunk][column block][16-oc block]
+// [lane] x 4 oc -- and requested one chunk ahead of their use.  dcol goes to LDS column by column and the
 // chunk's input gradient is gathered from it, four images per 16-byte read:
 //     dx[b][ic][ih][iw] = sum over the taps with oh*S+kh = ih, ow*S+kw = iw
 //                         of dcol[(oh,ow,b)][(ic,kh,kw)]
@@ -28,8 +28,10 @@ namespace {
 
 // Packed weights, 16-byte units ((chunk*NBC + nbl)*KS4 + s)*64 + lane: column
 // n = nbl*16 + lane%16 of the chunk is (icl, kk) = (n / KK, n % KK), and the
-// unit holds w[16*s + 4*j + lane/16][chunk*CC + icl][kk] for j = 0..3 (the B
-// value of MFMA step 4*s + j), zero past OC, IC or the chunk's CC*KK columns.
+// unit holds w[16*s + 4*(lane/16) + j][chunk*CC + icl][kk] for j = 0..3 (the
+// B value of MFMA step j of 16-channel block s: lane group q takes channel
+// 16*s + 4*q + j, so its four steps read four consecutive channels), zero
+// past OC, IC or the chunk's CC*KK columns.
 __global__ void __launch_bounds__(256) pack_w_dgrad_f32(const float *__restrict__ w,
                                                         float4 *__restrict__ wp, Geom g, int CC,
                                                         int NBC, int KS4, int total)
@@ -48,7 +50,7 @@ __global__ void __launch_bounds__(256) pack_w_dgrad_f32(const float *__restrict_
         float v[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int oc = 16 * s4 + 4 * j + (lane >> 4);
+            const int oc = 16 * s4 + 4 * (lane >> 4) + j;
             v[j] = (ok && oc < g.OC) ? w[(size_t(oc) * g.IC + ic) * g.KK + kk] : 0.f;
         }
         wp[u] = make_float4(v[0], v[1], v[2], v[3]);
@@ -70,18 +72,19 @@ __device__ __forceinline__ float comp(const float4 &v, int i)
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// KS4 = OC/16 rounded up: 16-channel steps, each 4 MFMA steps of 4 channels.
+// KS4 = OC/16 rounded up: 16-channel blocks, each 4 MFMA steps of 4 channels.
 //
-// Roles: waves 0-3 (one per SIMD) run the MFMAs of chunk c while waves 4-7
-// gather chunk c-1 and store chunk c-2's dx tile, all between the same pair
-// of barriers, so the gather's LDS and VALU work hides under the MFMAs.
+// Roles: waves 0-7 (two per SIMD) run the MFMAs of chunk c while waves 8-15
+// gather chunk c-1 and store its dx, all between the same pair of barriers,
+// so the gather's LDS and VALU work hides under the MFMAs.
 template <int MB, int KS4, int TAPS, int NBW>
-__global__ void __launch_bounds__(512) dgrad_rf_f32(DgradRfArgs a)
+__global__ void __launch_bounds__(1024) dgrad_rf_f32(DgradRfArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint4 lds4[];
     const Geom &g = a.g;
     const DgradBfPlan &p = a.p;
-    constexpr int NT = 512, NMW = 4, NGT = 256;   // threads, MFMA waves, gather threads
+    constexpr int NT = 1024, NMW = 8, NGT = 512;  // threads, MFMA waves, gather threads
+    static_assert(NBW == 1, "one column block per MFMA wave");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool mfma_role = wave < NMW;
     const int G = p.G;
@@ -212,44 +215,48 @@ __global__ void __launch_bounds__(512) dgrad_rf_f32(DgradRfArgs a)
     __syncthreads();
 
     // ---- MFMA role state ---------------------------------------------------
-    // A fragments of every row block and oc step, kept for the whole kernel:
-    // lane holds dz[mb*16 + lane%16][4*ks + lane/16].  Each MFMA wave owns
-    // column blocks nbl = wave and wave + 4 of every chunk; their weight
-    // fragments live in two register sets, bw0 and bw1, each refilled right
-    // after its MFMAs have read it, one block (96 MFMAs) ahead of its use.
-    float af[MB][KS];
-    float4 bw0[KS4], bw1[KS4];
-    auto block_ok = [&](int c, int j) { return wave + NMW * j < nbc_of(c); };
-    auto load_b = [&](float4 (&dst)[KS4], int c, int j) {
-        const float4 *src = a.wp + (uint32_t(c * p.NBC + wave + NMW * j) * KS4 * 64 + lane);
+    // MFMA wave w owns column block w of every chunk.  Its weight fragments
+    // for one chunk (KS4 16-byte units per lane) sit in bcur, the next chunk's
+    // arrive in bnext during this chunk's MFMAs.  A values are read from the
+    // dz tile in LDS one 16-channel block ahead of their MFMAs:
+    // lane (row mb*16 + lane%16, group q) reads dz[row][16*s + 4*q .. +3].
+    float4 bcur[KS4], bnext[KS4];
+    auto block_ok = [&](int c) { return wave < nbc_of(c); };
+    auto load_b = [&](float4 (&dst)[KS4], int c) {
+        const float4 *src = a.wp + (uint32_t(c * p.NBC + wave) * KS4 * 64 + lane);
 #pragma unroll
         for (int s = 0; s < KS4; ++s) dst[s] = src[s * 64];
     };
-    auto mfma_block = [&](const float4 (&bb)[KS4], float *dbuf, int j) {
+    const float *arow = dz + (lane & 15) * p.OCP + 4 * (lane >> 4);
+    auto mfma_block = [&](float *dbuf) {
         f32x4 acc[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float4 av[2][MB];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int mb = 0; mb < MB; ++mb)
+            av[0][mb] = *reinterpret_cast<const float4 *>(arow + mb * 16 * p.OCP);
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[mb][ks], comp(bb[ks >> 2], ks & 3),
-                                                               acc[mb], 0, 0, 0);
-        // lane holds rows mb*16 + 4*(lane/16) + v of column nbl*16 + lane%16
-        const int nbl = wave + NMW * j;
-        float *dst = dbuf + (nbl * 16 + (lane & 15)) * p.RP + (lane >> 4) * 4;
+        for (int s = 0; s < KS4; ++s) {
+            if (s + 1 < KS4) {
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    av[(s + 1) & 1][mb] =
+                        *reinterpret_cast<const float4 *>(arow + mb * 16 * p.OCP + 16 * (s + 1));
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(comp(av[s & 1][mb], j),
+                                                                   comp(bcur[s], j), acc[mb], 0, 0, 0);
+        }
+        // lane holds rows mb*16 + 4*(lane/16) + v of column wave*16 + lane%16
+        float *dst = dbuf + (wave * 16 + (lane & 15)) * p.RP + (lane >> 4) * 4;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) *reinterpret_cast<f32x4 *>(dst + mb * 16) = acc[mb];
     };
-    if (mfma_role) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const float *row = dz + (mb * 16 + (lane & 15)) * p.OCP + (lane >> 4);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) af[mb][ks] = row[4 * ks];
-        }
-        if (c_begin < c_end && block_ok(c_begin, 0)) load_b(bw0, c_begin, 0);
-    }
+    if (mfma_role && c_begin < c_end && block_ok(c_begin)) load_b(bnext, c_begin);
 
     // ---- gather role: sum the taps of 4 images per 16-byte read and store
     // straight to dx; a store instruction covers 64 consecutive pixels of one
@@ -289,13 +296,11 @@ __global__ void __launch_bounds__(512) dgrad_rf_f32(DgradRfArgs a)
     // every dcol buffer changes hands at a barrier -----------------------------
     for (int it = c_begin; it <= c_end; ++it) {
         if (mfma_role) {
-            if (it < c_end) {
-                float *dbuf = dcol + ((it - c_begin) & 1) * dcol_buf;
-                const bool ok0 = block_ok(it, 0), ok1 = NBW > 1 && block_ok(it, 1);
-                if (ok1) load_b(bw1, it, 1);
-                if (ok0) mfma_block(bw0, dbuf, 0);
-                if (it + 1 < c_end && block_ok(it + 1, 0)) load_b(bw0, it + 1, 0);
-                if (ok1) mfma_block(bw1, dbuf, 1);
+            if (it < c_end && block_ok(it)) {
+#pragma unroll
+                for (int s = 0; s < KS4; ++s) bcur[s] = bnext[s];
+                if (it + 1 < c_end && block_ok(it + 1)) load_b(bnext, it + 1);
+                mfma_block(dcol + ((it - c_begin) & 1) * dcol_buf);
             }
         } else if (it > c_begin) {
             gather(it - 1, dcol + ((it - 1 - c_begin) & 1) * dcol_buf);
@@ -309,8 +314,8 @@ struct DgradRfVariant {
     void (*fn)(DgradRfArgs);
 };
 
-#define DR_V(MB, KS4, TAPS, NBW) {8, MB, KS4, TAPS, NBW, dgrad_rf_f32<MB, KS4, TAPS, NBW>}
-#define DR_TAPS(MB, KS4) DR_V(MB, KS4, 2, 2), DR_V(MB, KS4, 4, 2), DR_V(MB, KS4, 9, 2)
+#define DR_V(MB, KS4, TAPS, NBW) {16, MB, KS4, TAPS, NBW, dgrad_rf_f32<MB, KS4, TAPS, NBW>}
+#define DR_TAPS(MB, KS4) DR_V(MB, KS4, 2, 1), DR_V(MB, KS4, 4, 1), DR_V(MB, KS4, 9, 1)
 const DgradRfVariant kDgradRfVariants[] = {
     DR_TAPS(1, 8), DR_TAPS(2, 8), DR_TAPS(3, 8),     // OC 113..128
     DR_TAPS(1, 4), DR_TAPS(2, 4), DR_TAPS(3, 4),     // OC 49..64
@@ -349,12 +354,12 @@ int max_taps_rf(const Geom &g)
 
 }  // namespace
 
-// Four MFMA waves take up to two column blocks each per chunk (NBC <= 8); the
-// chunk time is the longer of their MFMA work and the gather waves' work.
-// MB*KS fragments stay in registers, so MB is capped at 3 for 128 channels.
+// Eight MFMA waves take one column block each per chunk (NBC <= 8); the
+// chunk time is the longer of their MFMA work (two waves per SIMD) and the
+// gather waves' work.  MB is capped at 3.
 bool plan_dgrad_rf_f32(const Geom &g, DgradBfPlan &p)
 {
-    constexpr int NW = 8, NGT = 256;
+    constexpr int NW = 16, NGT = 512;
     if (g.HW > NGT || g.P > 16) return false;
     const int ks4 = (g.OC + 15) / 16;
     const int KS4 = ks4 <= 1 ? 1 : ks4 <= 2 ? 2 : ks4 <= 4 ? 4 : ks4 <= 8 ? 8 : 0;
@@ -376,7 +381,7 @@ bool plan_dgrad_rf_f32(const Geom &g, DgradBfPlan &p)
         for (int CC = 1; CC <= g.IC; ++CC) {
             const int NBC = (CC * g.KK + 15) / 16;
             if (NBC > 8) break;
-            const int NBW = 2;
+            const int NBW = 1;
             const size_t lds = dz_bytes + 2 * size_t(NBC) * 16 * RP * 4;
             if (lds > 160 * 1024) break;
             const int nchunks = (g.IC + CC - 1) / CC;
@@ -384,7 +389,7 @@ bool plan_dgrad_rf_f32(const Geom &g, DgradBfPlan &p)
             while (ngroups * cgroups < 256 && cgroups < nchunks) ++cgroups;
             const int cpg = (nchunks + cgroups - 1) / cgroups;
             cgroups = (nchunks + cpg - 1) / cpg;
-            const double mfma = double((NBC + 3) / 4) * MB * 4 * KS4 * 32;
+            const double mfma = 2.0 * MB * 4 * KS4 * 32;
             const double passes = double((CC * (G / 4) + rpi - 1) / rpi);
             const double gather = passes * 4 * (mt * 16.0 + 40.0) + 600.0;
             const double chunk = std::max(mfma, gather) + 300.0;
@@ -409,7 +414,7 @@ hipError_t launch_dgrad_rf_f32(const Geom &g, const DgradBfPlan &p, const void *
                                const void *ym, void *dx, void *ws, int relu, hipStream_t s)
 {
     const DgradRfVariant *v = pick_dgrad_rf(p.NW, p.MB, p.KS, p.TAPS, p.NBW);
-    if (!v || p.NW != 8 || g.HW > 256 || p.G % 4 || p.G * g.P > 16 * p.MB || p.NBC > 4 * p.NBW ||
+    if (!v || p.NW != 16 || g.HW > 512 || p.G % 4 || p.G * g.P > 16 * p.MB || p.NBC > 8 * p.NBW ||
         p.RP < 16 * p.MB + p.G)
         return hipErrorInvalidValue;
     const int total = p.nchunks * p.NBC * p.KS * 64;
