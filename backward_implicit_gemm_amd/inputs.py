@@ -80,6 +80,8 @@ WORKLOADS = (
              "layer-2 shape, bf16 storage, fp32 accumulation"),
     Workload("chain_bf16_b16384", "bf16", (LAYER1.with_batch(16384), LAYER2.with_batch(16384)),
              (41, 42, 43, 44), "conv1 (ReLU) -> conv2, bf16, B=16384"),
+    Workload("chain_bf16_b32768", "bf16", (LAYER1.with_batch(32768), LAYER2.with_batch(32768)),
+             (51, 52, 53, 54), "conv1 (ReLU) -> conv2, bf16, B=32768, the encoder's batch"),
 )
 
 

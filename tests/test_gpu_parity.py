@@ -2,7 +2,7 @@
 
 Covers the policy-network layer shapes of "Speedups to gemm_conv_forward and
 gemm_conv_backward kernels" (PufferLib pull request #522) at their full
-batch of 1024 in fp32 and bf16, the two-layer chain at B=16384 on sampled
+batch of 1024 in fp32 and bf16, the two-layer chain at B=16384 and 32768 on sampled
 outputs, an odd-shape sweep whose tiles end mid-tile, integer-valued inputs
 that must match bit for bit, and run-to-run determinism of wgrad.
 """
@@ -57,7 +57,7 @@ def test_workload_full_parity(idx, kernel_policy):
 
 
 # ---------------------------------------------------------------------------
-# Two-layer chain at B=16384, stage-wise on sampled outputs
+# Two-layer chain at B=16384 and B=32768, stage-wise on sampled outputs
 # ---------------------------------------------------------------------------
 
 def _sample(shape, n, seed):
@@ -65,8 +65,9 @@ def _sample(shape, n, seed):
     return np.stack([r.integers(0, s, n) for s in shape], axis=1)
 
 
-def test_chain_b16384_sampled():
-    wl = inputs.WORKLOADS[4]
+@pytest.mark.parametrize("idx", [4, 5], ids=[w.name for w in inputs.WORKLOADS[4:6]])
+def test_chain_sampled(idx):
+    wl = inputs.WORKLOADS[idx]
     l1, l2 = (Layer.of(L) for L in wl.layers)
     t = inputs.workload_inputs(wl)
     dev = "cuda"
