@@ -57,13 +57,13 @@ struct FusedVariant {
     int MB, KS, TAPS, NBW, NSTEP;
     void (*fn)(DgradBfArgs, WgradBfArgs, int, int, int);   // both grids in one launch
     void (*fn_d)(DgradBfArgs);                              // d_input alone
-    void (*fn_w)(WgradBfArgs);                              // wgrad alone
+    void (*fn_w)(WgradBfArgs);                              // wgrad alone (16 waves)
 };
 // The (d_input, wgrad) kernel pairs the planners choose for the policy
 // network's layers at B=1024 and B=16384; other shapes use separate calls.
 #define FV(MB, KS, TAPS, NBW, NSTEP)                                                   \
     {MB, KS, TAPS, NBW, NSTEP, bwd_fused_bf16<8, MB, KS, TAPS, NBW, 2, NSTEP>,          \
-     dgrad_ig_bf16<8, MB, KS, TAPS, NBW, 2>, wgrad_ig_bf16<NSTEP>}
+     dgrad_ig_bf16<8, MB, KS, TAPS, NBW, 2>, wgrad_ws_bf16<NSTEP>}
 const FusedVariant kFusedVariants[] = {
     FV(3, 4, 4, 1, 3),    // 59 -> 128, 11x15, 5x5, stride 3
     FV(3, 4, 2, 1, 1),    // 128 -> 128, 3x4, 3x3, B=1024
@@ -161,7 +161,7 @@ hipError_t launch_bwd_fused_bf16(const Geom &g, const BwdFusedBfPlan &p, const v
         if (e != hipSuccess) return e;
         e = allow_max_lds(reinterpret_cast<const void *>(v->fn_w));
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(v->fn_w, dim3(n_wg), dim3(kWgNT), wp.lds, s, wa);
+        hipLaunchKernelGGL(v->fn_w, dim3(n_wg), dim3(2 * kWgNT), wp.lds, s, wa);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;

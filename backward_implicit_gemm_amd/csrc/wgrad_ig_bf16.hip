@@ -25,12 +25,13 @@
 namespace gc {
 namespace {
 
+// The role-split kernel (16 waves) runs the standalone call.
 struct WgradBfVariant {
     int NSTEP;
     void (*fn)(WgradBfArgs);
 };
 const WgradBfVariant kWgradBfVariants[] = {
-    {1, wgrad_ig_bf16<1>}, {2, wgrad_ig_bf16<2>}, {3, wgrad_ig_bf16<3>}, {4, wgrad_ig_bf16<4>},
+    {1, wgrad_ws_bf16<1>}, {2, wgrad_ws_bf16<2>}, {3, wgrad_ws_bf16<3>}, {4, wgrad_ws_bf16<4>},
 };
 
 const WgradBfVariant *pick_wgrad_bf(int nstep)
@@ -108,7 +109,7 @@ hipError_t launch_wgrad_ig_bf16(const Geom &g, const WgradBfPlan &p, const void 
     if (e != hipSuccess) return e;
     WgradBfArgs a{g, (const u16 *)x, dzg, part, p};
     const int slots = (p.splits + 7) / 8 * p.ncol;    // per XCD
-    hipLaunchKernelGGL(v->fn, dim3(8 * slots), dim3(kWgNT), p.lds, s, a);
+    hipLaunchKernelGGL(v->fn, dim3(8 * slots), dim3(2 * kWgNT), p.lds, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_wgrad_reduce<bf16_t>(part, dw, p.splits, g.OC * g.K, s);

@@ -283,10 +283,195 @@ __device__ __forceinline__ void wgrad_ig_bf16_body(const WgradBfArgs &a, int bid
     }
 }
 
+// The same computation with the roles split over 16 waves: waves 0..7 run
+// the MFMAs exactly as above, waves 8..15 run the staging (the same units,
+// indexed by their own thread number).  A wave's vector-memory counter is in
+// order, so in the 8-wave body every wait for a stage also waited for the
+// loads of the stage after it; here the MFMA waves issue no global loads.
+// The loaders store stage i+1 (loaded during stage i-1) into the other LDS
+// buffer and issue the loads of stage i+2 while the MFMAs run stage i; one
+// barrier per stage hands the buffers over.
+template <int NSTEP>
+__device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid)
+{
+    extern __shared__ __attribute__((aligned(16))) uint4 lds4[];
+    const Geom &g = a.g;
+    const WgradBfPlan &p = a.p;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const bool loader = wave >= 8;
+    const int tid = loader ? int(threadIdx.x) - kWgNT : int(threadIdx.x);   // index within the role
+    const int wm = wave & 1;          // output channels 64*wm .. +63
+    const int wn = wave >> 1;         // columns 32*wn .. +31 of the tile
+    const int N = g.K;                // IC*KH*KW columns
+    // Workgroups are dealt to the 8 XCDs round-robin by id; ids are laid out
+    // so that all column tiles of one split (one image range) share an XCD,
+    // whose L2 then serves that range's dz and x to every tile.
+    const int xcd = bid & 7, slot = bid >> 3;
+    const int split = (slot / p.ncol) * 8 + xcd;
+    if (split >= p.splits) return;
+    const int n0 = (slot % p.ncol) * 128;
+    const int c_lo = n0 / g.KK;
+    const int gb = split * p.gps;
+    const int ge = min(gb + p.gps, p.ngroups);
+
+    const int xbuf = p.CCW * p.HWP;               // 16-byte units per x stage
+    const int dbuf = p.PP * 128;                  // 16-byte units per dz stage
+    uint4 *xs = lds4;                             // [2][CCW][HWP]
+    uint4 *ds = lds4 + 2 * xbuf;                  // [2][PP][128]
+
+    // ---- per-lane fragment offsets (16-byte units) -------------------------
+    // B (x): column n = n0 + 32*wn + 16*j + lane%16 -> (ic, kh, kw); position
+    // p = 4*s + lane/16 -> pixel (oh*S, ow*S).  Padded columns and positions
+    // read a valid pixel; their dz is zero or their result is not stored.
+    int xcol[2], xrow[NSTEP], drow[NSTEP];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int n = min(n0 + 32 * wn + 16 * j + (lane & 15), N - 1);
+        uint32_t ic, kk, kh, kw;
+        fdivmod(uint32_t(n), g.fd_KK, ic, kk);
+        fdivmod(kk, g.fd_KW, kh, kw);
+        xcol[j] = (int(ic) - c_lo) * p.HWP + int(kh) * g.W + int(kw);
+    }
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+        const int pp = 4 * s + (lane >> 4);
+        const int pc = min(pp, g.P - 1);
+        uint32_t oh, ow;
+        fdivmod(uint32_t(pc), g.fd_OW, oh, ow);
+        xrow[s] = int(oh) * g.S * g.W + int(ow) * g.S;
+        drow[s] = pp * 128 + 64 * wm + (lane & 15);
+    }
+
+    // ---- staging -----------------------------------------------------------
+    // x unit (icl, blk, half): pixels [pix, pix+8) of channel c_lo + icl for
+    // images 4*half .. 4*half+3 of the group, pix = min(8*blk, HW-8) so every
+    // 16-byte load stays inside its plane (the last block overlaps its
+    // neighbour and rewrites the same values).  Every thread issues the same
+    // loads, from clamped valid addresses where it has no unit, so the wait
+    // for a stage is an exact count of the loads issued after it.  Images
+    // past the batch are zeroed (their dz is zero too; a zero x keeps
+    // non-finite values out of the sums).
+    const bool xon = tid < 2 * p.CCW * p.nblk;
+    const int xunit = xon ? tid >> 1 : 0;
+    const int xhalf = tid & 1;
+    const int xicl = xunit / p.nblk;
+    const int xpix = min(8 * (xunit - xicl * p.nblk), g.HW - 8);
+    const int xic = min(c_lo + xicl, g.IC - 1);
+    auto fetch = [&](int grp, WgStage<NSTEP> &st) {
+        const int b0 = grp * 8 + 4 * xhalf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int b = min(b0 + i, g.B - 1);
+            st.x[i] = ldg16(a.x + (uint32_t(b) * g.IC + xic) * g.HW + xpix);
+        }
+        const uint4 *src = a.dzg + size_t(grp) * dbuf;
+#pragma unroll
+        for (int k = 0; k < NSTEP; ++k) st.d[k] = src[tid + k * kWgNT];
+    };
+    auto stash = [&](int grp, const WgStage<NSTEP> &st, int buf) {
+        if (xon) {
+            const int nb = g.B - grp * 8 - 4 * xhalf;   // images of this half in the batch
+            uint32_t in[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = i < nb;
+                in[i][0] = ok ? st.x[i].x : 0u; in[i][1] = ok ? st.x[i].y : 0u;
+                in[i][2] = ok ? st.x[i].z : 0u; in[i][3] = ok ? st.x[i].w : 0u;
+            }
+            // pixel pp's 16-byte slot holds images 0..7; this thread writes
+            // the 8 bytes of its four: word j = images (2j, 2j+1)
+            uint2 *dst = reinterpret_cast<uint2 *>(xs + buf * xbuf + xicl * p.HWP + xpix) + xhalf;
+#pragma unroll
+            for (int pp = 0; pp < 8; ++pp) {
+                const int wi = pp >> 1;
+                uint32_t o[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const uint32_t lo = in[2 * j][wi], hi = in[2 * j + 1][wi];
+                    o[j] = (pp & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+                }
+                dst[2 * pp] = make_uint2(o[0], o[1]);
+            }
+        }
+        uint4 *dd = ds + buf * dbuf;
+#pragma unroll
+        for (int k = 0; k < NSTEP; ++k) dd[tid + k * kWgNT] = st.d[k];
+    };
+
+    f32x4 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto mfma_stage = [&](int buf) {
+        const uint4 *xb = xs + buf * xbuf;
+        const uint4 *db = ds + buf * dbuf;
+#pragma unroll
+        for (int s = 0; s < NSTEP; ++s) {
+            bf16x8 af[4], bfr[2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] = __builtin_bit_cast(bf16x8, db[drow[s] + 16 * i]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) bfr[j] = __builtin_bit_cast(bf16x8, xb[xcol[j] + xrow[s]]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    const int ng = ge - gb;
+    if (loader) {
+        WgStage<NSTEP> r;
+        if (ng > 0) {
+            fetch(gb, r);
+            stash(gb, r, 0);
+        }
+        if (ng > 1) fetch(gb + 1, r);
+        __syncthreads();
+        for (int i = 0; i < ng; ++i) {
+            if (i + 1 < ng) {
+                stash(gb + i + 1, r, (i + 1) & 1);
+                if (i + 2 < ng) fetch(gb + i + 2, r);
+            }
+            __syncthreads();
+        }
+        return;
+    }
+    __syncthreads();
+    for (int i = 0; i < ng; ++i) {
+        mfma_stage(i & 1);
+        __syncthreads();
+    }
+
+    // ---- partial tile: lane holds rows 4*(lane/16) + v of column lane%16 ----
+    float *part = a.part + size_t(split) * g.OC * N;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int n = n0 + 32 * wn + 16 * j + (lane & 15);
+        if (n >= N) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int oc = 64 * wm + 16 * i + 4 * (lane >> 4) + v;
+                if (oc < g.OC) part[uint32_t(oc) * N + n] = acc[i][j][v];
+            }
+    }
+}
+
 template <int NSTEP>
 __global__ void __launch_bounds__(kWgNT) wgrad_ig_bf16(WgradBfArgs a)
 {
     wgrad_ig_bf16_body<NSTEP>(a, blockIdx.x);
+}
+
+template <int NSTEP>
+__global__ void __launch_bounds__(2 * kWgNT) wgrad_ws_bf16(WgradBfArgs a)
+{
+    wgrad_ws_bf16_body<NSTEP>(a, blockIdx.x);
 }
 
 }  // namespace
