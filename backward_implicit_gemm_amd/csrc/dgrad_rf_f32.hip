@@ -10,10 +10,10 @@
 // while eight gather waves gather the previous chunk (see the kernel).  The
 // reduction over oc runs in blocks of 16 channels, MFMA step j giving lane
 // group q the channel 16*s + 4*q + j, so a lane's A values for four steps are
-// one 16-byte LDS read of its dz row and its B values one 16-byte unit of the
-// weights, pre-packed in that order -- [chunk][column block][16-oc block]
-// [lane] x 4 oc -- and requested one chunk ahead of their use.  dcol goes to LDS column by column and the
-// chunk's input gradient is gathered from it, four images per 16-byte read:
+// one 16-byte LDS read of its dz row; its B values are four floats of w read
+// in place (16 lanes read 16 consecutive floats of one weight row), a few
+// channel blocks ahead of their MFMAs.  dcol goes to LDS column by column and
+// the chunk's input gradient is gathered from it, four images per 16-byte read:
 //     dx[b][ic][ih][iw] = sum over the taps with oh*S+kh = ih, ow*S+kw = iw
 //                         of dcol[(oh,ow,b)][(ic,kh,kw)]
 // in fp32 in a fixed tap order and stored straight to dx (64 consecutive
@@ -26,41 +26,10 @@
 namespace gc {
 namespace {
 
-// Packed weights, 16-byte units ((chunk*NBC + nbl)*KS4 + s)*64 + lane: column
-// n = nbl*16 + lane%16 of the chunk is (icl, kk) = (n / KK, n % KK), and the
-// unit holds w[16*s + 4*(lane/16) + j][chunk*CC + icl][kk] for j = 0..3 (the
-// B value of MFMA step j of 16-channel block s: lane group q takes channel
-// 16*s + 4*q + j, so its four steps read four consecutive channels), zero
-// past OC, IC or the chunk's CC*KK columns.
-__global__ void __launch_bounds__(256) pack_w_dgrad_f32(const float *__restrict__ w,
-                                                        float4 *__restrict__ wp, Geom g, int CC,
-                                                        int NBC, int KS4, int total)
-{
-    for (int u = blockIdx.x * 256 + threadIdx.x; u < total; u += gridDim.x * 256) {
-        const int lane = u & 63;
-        int rest = u >> 6;
-        const int s4 = rest % KS4;
-        rest /= KS4;
-        const int nbl = rest % NBC;
-        const int chunk = rest / NBC;
-        const int n = nbl * 16 + (lane & 15);
-        const int icl = n / g.KK, kk = n - icl * g.KK;
-        const int ic = chunk * CC + icl;
-        const bool ok = icl < CC && ic < g.IC;
-        float v[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int oc = 16 * s4 + 4 * (lane >> 4) + j;
-            v[j] = (ok && oc < g.OC) ? w[(size_t(oc) * g.IC + ic) * g.KK + kk] : 0.f;
-        }
-        wp[u] = make_float4(v[0], v[1], v[2], v[3]);
-    }
-}
-
 struct DgradRfArgs {
     Geom g;
     const float *dy, *ym;
-    const float4 *wp;
+    const float *w;      // OIHW weights, read in place
     float *dx;
     int relu;
     DgradBfPlan p;
@@ -76,7 +45,9 @@ __device__ __forceinline__ float comp(const float4 &v, int i)
 //
 // Roles: waves 0-7 (two per SIMD) run the MFMAs of chunk c while waves 8-15
 // gather chunk c-1 and store its dx, all between the same pair of barriers,
-// so the gather's LDS and VALU work hides under the MFMAs.
+// so the gather's LDS and VALU work hides under the MFMAs.  The roles branch
+// outside the chunk loop (each wave passes the same number of barriers), so
+// each role's registers are live only in its own loop.
 template <int MB, int KS4, int TAPS, int NBW>
 __global__ void __launch_bounds__(1024) dgrad_rf_f32(DgradRfArgs a)
 {
@@ -110,10 +81,35 @@ __global__ void __launch_bounds__(1024) dgrad_rf_f32(DgradRfArgs a)
         }
     }
 
-    auto nbc_of = [&](int c) {
-        const int cc = min(p.CC, g.IC - c * p.CC);
-        return (cc * g.KK + 15) >> 4;
+    // ---- MFMA role: weights ------------------------------------------------
+    // MFMA wave w (w < NBC) owns column block w of every chunk: weight-matrix
+    // columns kc = chunk*CC*KK + 16*w + lane%16 of w[oc][ic*KK + kk].  Its B
+    // values for 16-channel block s are w[16*s + 4*q + j][kc], j = 0..3 (q =
+    // lane/16), four 4-byte loads in which 16 lanes read 16 consecutive floats
+    // of one row.  They run D blocks ahead of their MFMAs through a register
+    // ring that crosses chunk boundaries; the first D are issued here, before
+    // the dz staging.  Loads past the tensor's end read zeros (channels past
+    // OC); columns past a chunk's CC*KK only feed dcol columns the gather never
+    // reads, and the loads for the chunk after the last are never used.
+    constexpr int D = KS4 < 4 ? KS4 : 4;
+    static_assert(KS4 % D == 0, "the ring slot of block s is s % D in every chunk");
+    const bool mfma_on = mfma_role && wave < p.NBC;
+    const uint32_t K4 = uint32_t(g.K) * 4;
+    const uint32_t cbytes = uint32_t(p.CC) * g.KK * 4;                 // one chunk's columns
+    const __amdgpu_buffer_rsrc_t wrs = tensor_rsrc(a.w, uint32_t(g.OC) * K4);
+    uint32_t w_vo = uint32_t(4 * (lane >> 4)) * K4 + (uint32_t(wave) * 16 + (lane & 15)) * 4 +
+                    uint32_t(c_begin) * cbytes;
+    auto load_blk = [&](uint32_t vo, int s) {
+        float4 r;
+        r.x = bload4s(wrs, vo, uint32_t(16 * s + 0) * K4);
+        r.y = bload4s(wrs, vo, uint32_t(16 * s + 1) * K4);
+        r.z = bload4s(wrs, vo, uint32_t(16 * s + 2) * K4);
+        r.w = bload4s(wrs, vo, uint32_t(16 * s + 3) * K4);
+        return r;
     };
+    float4 ring[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) ring[i] = mfma_on ? load_blk(w_vo, i) : make_float4(0.f, 0.f, 0.f, 0.f);
 
     // dz: the group's gimg*OC*P contiguous elements of dy (and y), 4 per
     // 16-byte load, all of a thread's loads in flight together; element
@@ -214,50 +210,6 @@ __global__ void __launch_bounds__(1024) dgrad_rf_f32(DgradRfArgs a)
     }
     __syncthreads();
 
-    // ---- MFMA role state ---------------------------------------------------
-    // MFMA wave w owns column block w of every chunk.  Its weight fragments
-    // for one chunk (KS4 16-byte units per lane) sit in bcur, the next chunk's
-    // arrive in bnext during this chunk's MFMAs.  A values are read from the
-    // dz tile in LDS one 16-channel block ahead of their MFMAs:
-    // lane (row mb*16 + lane%16, group q) reads dz[row][16*s + 4*q .. +3].
-    float4 bcur[KS4], bnext[KS4];
-    auto block_ok = [&](int c) { return wave < nbc_of(c); };
-    auto load_b = [&](float4 (&dst)[KS4], int c) {
-        const float4 *src = a.wp + (uint32_t(c * p.NBC + wave) * KS4 * 64 + lane);
-#pragma unroll
-        for (int s = 0; s < KS4; ++s) dst[s] = src[s * 64];
-    };
-    const float *arow = dz + (lane & 15) * p.OCP + 4 * (lane >> 4);
-    auto mfma_block = [&](float *dbuf) {
-        f32x4 acc[MB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float4 av[2][MB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-            av[0][mb] = *reinterpret_cast<const float4 *>(arow + mb * 16 * p.OCP);
-#pragma unroll
-        for (int s = 0; s < KS4; ++s) {
-            if (s + 1 < KS4) {
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    av[(s + 1) & 1][mb] =
-                        *reinterpret_cast<const float4 *>(arow + mb * 16 * p.OCP + 16 * (s + 1));
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    acc[mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(comp(av[s & 1][mb], j),
-                                                                   comp(bcur[s], j), acc[mb], 0, 0, 0);
-        }
-        // lane holds rows mb*16 + 4*(lane/16) + v of column wave*16 + lane%16
-        float *dst = dbuf + (wave * 16 + (lane & 15)) * p.RP + (lane >> 4) * 4;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) *reinterpret_cast<f32x4 *>(dst + mb * 16) = acc[mb];
-    };
-    if (mfma_role && c_begin < c_end && block_ok(c_begin)) load_b(bnext, c_begin);
-
     // ---- gather role: sum the taps of 4 images per 16-byte read and store
     // straight to dx; a store instruction covers 64 consecutive pixels of one
     // plane, so the 4-byte stores coalesce without staging --------------------
@@ -294,16 +246,56 @@ __global__ void __launch_bounds__(1024) dgrad_rf_f32(DgradRfArgs a)
 
     // ---- pipeline: iteration it computes chunk it and gathers chunk it-1;
     // every dcol buffer changes hands at a barrier -----------------------------
+    if (!mfma_role) {
+        for (int it = c_begin; it <= c_end; ++it) {
+            if (it > c_begin) gather(it - 1, dcol + ((it - 1 - c_begin) & 1) * dcol_buf);
+            __syncthreads();
+        }
+        return;
+    }
+    if (!mfma_on) {             // no column block for this wave
+        for (int it = c_begin; it <= c_end; ++it) __syncthreads();
+        return;
+    }
+    // A values come from the dz tile in LDS one 16-channel block ahead of
+    // their MFMAs: lane (row mb*16 + lane%16, group q) reads dz[row][16*s +
+    // 4*q .. +3].  C: lane holds rows mb*16 + 4*(lane/16) + v of column
+    // wave*16 + lane%16.
+    const float *arow = dz + (lane & 15) * p.OCP + 4 * (lane >> 4);
+    float *dst = dcol + (wave * 16 + (lane & 15)) * p.RP + (lane >> 4) * 4;
     for (int it = c_begin; it <= c_end; ++it) {
-        if (mfma_role) {
-            if (it < c_end && block_ok(it)) {
+        if (it < c_end) {
+            f32x4 acc[MB];
 #pragma unroll
-                for (int s = 0; s < KS4; ++s) bcur[s] = bnext[s];
-                if (it + 1 < c_end && block_ok(it + 1)) load_b(bnext, it + 1);
-                mfma_block(dcol + ((it - c_begin) & 1) * dcol_buf);
+            for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            float4 av[2][MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                av[0][mb] = *reinterpret_cast<const float4 *>(arow + mb * 16 * p.OCP);
+#pragma unroll
+            for (int s = 0; s < KS4; ++s) {
+                if (s + 1 < KS4) {
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        av[(s + 1) & 1][mb] =
+                            *reinterpret_cast<const float4 *>(arow + mb * 16 * p.OCP + 16 * (s + 1));
+                }
+                const float4 bv = ring[s % D];
+                // refill: block s+D of this chunk, else block s+D-KS4 of the next
+                ring[s % D] = s + D < KS4 ? load_blk(w_vo, s + D) : load_blk(w_vo + cbytes, s + D - KS4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(comp(av[s & 1][mb], j), comp(bv, j),
+                                                                       acc[mb], 0, 0, 0);
+                // keep each block's loads and MFMAs in their place
+                __builtin_amdgcn_sched_barrier(0);
             }
-        } else if (it > c_begin) {
-            gather(it - 1, dcol + ((it - 1 - c_begin) & 1) * dcol_buf);
+            float *d = dst + ((it - c_begin) & 1) * dcol_buf;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) *reinterpret_cast<f32x4 *>(d + mb * 16) = acc[mb];
+            w_vo += cbytes;
         }
         __syncthreads();
     }
@@ -402,7 +394,7 @@ bool plan_dgrad_rf_f32(const Geom &g, DgradBfPlan &p)
                 p.CC = CC; p.NBC = NBC; p.nchunks = nchunks; p.cgroups = cgroups; p.cpg = cpg;
                 p.RP = RP; p.OCP = OCP; p.dz_bytes = int(dz_bytes); p.ORUN = 0;
                 p.lds = lds;
-                p.ws_bytes = size_t(nchunks) * NBC * KS4 * 64 * 16;
+                p.ws_bytes = 0;
                 found = true;
             }
         }
@@ -411,21 +403,17 @@ bool plan_dgrad_rf_f32(const Geom &g, DgradBfPlan &p)
 }
 
 hipError_t launch_dgrad_rf_f32(const Geom &g, const DgradBfPlan &p, const void *dy, const void *w,
-                               const void *ym, void *dx, void *ws, int relu, hipStream_t s)
+                               const void *ym, void *dx, int relu, hipStream_t s)
 {
     const DgradRfVariant *v = pick_dgrad_rf(p.NW, p.MB, p.KS, p.TAPS, p.NBW);
     if (!v || p.NW != 16 || g.HW > 512 || p.G % 4 || p.G * g.P > 16 * p.MB || p.NBC > 8 * p.NBW ||
         p.RP < 16 * p.MB + p.G)
         return hipErrorInvalidValue;
-    const int total = p.nchunks * p.NBC * p.KS * 64;
-    if (size_t(total) * 16 > p.ws_bytes) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(pack_w_dgrad_f32, dim3(std::min((total + 255) / 256, 2048)), dim3(256), 0, s,
-                       (const float *)w, (float4 *)ws, g, p.CC, p.NBC, p.KS, total);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    DgradRfArgs a{g, (const float *)dy, (const float *)ym, (const float4 *)ws, (float *)dx, relu, p,
+    // weight offsets are 32-bit byte offsets inside the tensor
+    if (size_t(g.OC) * g.K * 4 >= (size_t(1) << 31)) return hipErrorInvalidValue;
+    DgradRfArgs a{g, (const float *)dy, (const float *)ym, (const float *)w, (float *)dx, relu, p,
                   make_fastdiv(g.OC * g.P)};
-    e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
+    hipError_t e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
     if (e != hipSuccess) return e;
     dim3 grid((g.B + p.G - 1) / p.G, p.cgroups);
     hipLaunchKernelGGL(v->fn, grid, dim3(64 * p.NW), p.lds, s, a);

@@ -318,12 +318,12 @@ int gc_conv_bwd_data(const void *dy, const void *w, const void *y_mask, void *dx
         DgradBfPlan bp;
         const bool bf = dtype == GC_BF16 && dgrad_bf16_plan(g, bp);
         const bool rf = !bf && dtype == GC_F32 && dgrad_f32_rf_plan(g, bp);
-        if (bf || rf) {
+        if (bf) {
             if (!workspace || ws_bytes < bp.ws_bytes) return GC_ERR_WORKSPACE;
             if (reinterpret_cast<uintptr_t>(workspace) % 16) return GC_ERR_WORKSPACE;
-            return hip_status(bf ? launch_dgrad_ig_bf16(g, bp, dy, w, y_mask, dx, workspace, relu, s)
-                                 : launch_dgrad_rf_f32(g, bp, dy, w, y_mask, dx, workspace, relu, s));
+            return hip_status(launch_dgrad_ig_bf16(g, bp, dy, w, y_mask, dx, workspace, relu, s));
         }
+        if (rf) return hip_status(launch_dgrad_rf_f32(g, bp, dy, w, y_mask, dx, relu, s));
     }
     DgradIgPlan p;
     const bool ig = dgrad_plan(g, p);

@@ -75,11 +75,12 @@ hipError_t launch_fwd_ws_f32(const Geom &g, const FwdWsPlan &p, const void *x, c
 hipError_t launch_fwd_rf_f32(const Geom &g, const FwdBfPlan &p, const void *x, const void *w,
                              const void *bias, void *y, void *ws, int relu, hipStream_t s);
 bool plan_dgrad_ig_bf16(const Geom &g, DgradBfPlan &p);
-// fp32 d_input with register-held dz fragments (dgrad_rf_f32.hip); the plan
-// struct is shared with the bf16 kernel, KS holding the 16-channel steps.
+// fp32 d_input on fp32 MFMA, weights read in place (dgrad_rf_f32.hip); the
+// plan struct is shared with the bf16 kernel, KS holding the 16-channel
+// blocks, and needs no workspace.
 bool plan_dgrad_rf_f32(const Geom &g, DgradBfPlan &p);
 hipError_t launch_dgrad_rf_f32(const Geom &g, const DgradBfPlan &p, const void *dy, const void *w,
-                               const void *ym, void *dx, void *ws, int relu, hipStream_t s);
+                               const void *ym, void *dx, int relu, hipStream_t s);
 // fp32 wgrad with image-quad staging: partial tiles then the fixed-order
 // reduction into dw (fp32 storage only)
 bool plan_wgrad_rf_f32(const Geom &g, WgradRfPlan &p);

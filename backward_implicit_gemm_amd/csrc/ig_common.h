@@ -63,10 +63,6 @@ __device__ __forceinline__ float4 ldg4_any(const float *p)
 
 constexpr int IG_NT = 256;   // threads per workgroup (4 waves)
 
-// s_waitcnt vmcnt(0): every vector memory operation this wave has issued has
-// completed.  Placed where only loads issued long ago are outstanding, it
-// retires them before later stores are issued, so a later use of the loaded
-// registers does not wait for those stores as well.
 // Buffer resource over a whole tensor of `bytes` bytes (< 2^31): a load
 // whose offset is at or past the end returns zeros, so staging loads need no
 // branches for images past the batch or channels past the tensor.  Word 3
@@ -108,8 +104,17 @@ __device__ __forceinline__ uint4 bload16us(__amdgpu_buffer_rsrc_t r, uint32_t vo
     __builtin_memcpy(&u, &v, 16);
     return u;
 }
+// 4 bytes at byte offset voff + soff, soff wave-uniform (zeros past the end)
+__device__ __forceinline__ float bload4s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
 constexpr uint32_t kOffNone = 0xFFFFFFF0u;   // an offset past the end of every tensor
 
+// s_waitcnt vmcnt(0): every vector memory operation this wave has issued has
+// completed.  Placed where only loads issued long ago are outstanding, it
+// retires them before later stores are issued, so a later use of the loaded
+// registers does not wait for those stores as well.
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ---------------------------------------------------------------- forward --

@@ -345,7 +345,7 @@ def cpu_baseline(wl, budget_s):
 # Kernels behind each call, as named in rocprofv3 summaries.
 CALL_KERNELS = {
     "fwd": {"f32": ["pack_w_fwd_f32", "fwd_ws_f32"], "bf16": ["pack_w_fwd_bf16", "fwd_ws_bf16"]},
-    "dgrad": {"f32": ["pack_w_dgrad_f32", "dgrad_rf_f32"], "bf16": ["pack_w_dgrad_bf16", "dgrad_ig_bf16"]},
+    "dgrad": {"f32": ["dgrad_rf_f32"], "bf16": ["pack_w_dgrad_bf16", "dgrad_ig_bf16"]},
     "wgrad": {"f32": ["wgrad_rf_f32", "wgrad_reduce"],
               "bf16": ["dz_groups_bf16", "wgrad_ws_bf16", "wgrad_reduce"]},
 }
