@@ -48,7 +48,7 @@ __device__ __forceinline__ float comp(const float4 &v, int i)
 // so the gather's LDS and VALU work hides under the MFMAs.  The roles branch
 // outside the chunk loop (each wave passes the same number of barriers), so
 // each role's registers are live only in its own loop.
-template <int MB, int KS4, int TAPS, int NBW>
+template <int MB, int KS4, int TAPS, int NBW, bool EXACT>
 __global__ void __launch_bounds__(1024) dgrad_rf_f32(DgradRfArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint4 lds4[];
@@ -88,28 +88,40 @@ __global__ void __launch_bounds__(1024) dgrad_rf_f32(DgradRfArgs a)
     // lane/16), four 4-byte loads in which 16 lanes read 16 consecutive floats
     // of one row.  They run D blocks ahead of their MFMAs through a register
     // ring that crosses chunk boundaries; the first D are issued here, before
-    // the dz staging.  Loads past the tensor's end read zeros (channels past
-    // OC); columns past a chunk's CC*KK only feed dcol columns the gather never
-    // reads, and the loads for the chunk after the last are never used.
+    // the dz staging.  Every load stays inside the tensor: the column is
+    // clamped to K-1 (columns past a chunk's CC*KK only feed dcol columns the
+    // gather never reads, and the loads for the chunk after the last are
+    // never used), and with OC < 16*KS4 (EXACT false) the rows past OC take
+    // an offset past the end of the tensor, which reads zeros.
     constexpr int D = KS4 < 4 ? KS4 : 4;
     static_assert(KS4 % D == 0, "the ring slot of block s is s % D in every chunk");
     const bool mfma_on = mfma_role && wave < p.NBC;
     const uint32_t K4 = uint32_t(g.K) * 4;
-    const uint32_t cbytes = uint32_t(p.CC) * g.KK * 4;                 // one chunk's columns
+    const int ckk = p.CC * g.KK;                                         // columns per chunk
     const __amdgpu_buffer_rsrc_t wrs = tensor_rsrc(a.w, uint32_t(g.OC) * K4);
-    uint32_t w_vo = uint32_t(4 * (lane >> 4)) * K4 + (uint32_t(wave) * 16 + (lane & 15)) * 4 +
-                    uint32_t(c_begin) * cbytes;
+    const uint32_t w_q = uint32_t(4 * (lane >> 4)) * K4;                // row 4*q
+    int w_col = c_begin * ckk + wave * 16 + (lane & 15);                 // kc of the current chunk
+    auto chunk_vo = [&](int col) { return w_q + uint32_t(min(col, g.K - 1)) * 4; };
     auto load_blk = [&](uint32_t vo, int s) {
         float4 r;
-        r.x = bload4s(wrs, vo, uint32_t(16 * s + 0) * K4);
-        r.y = bload4s(wrs, vo, uint32_t(16 * s + 1) * K4);
-        r.z = bload4s(wrs, vo, uint32_t(16 * s + 2) * K4);
-        r.w = bload4s(wrs, vo, uint32_t(16 * s + 3) * K4);
+        if constexpr (EXACT) {
+            r.x = bload4s(wrs, vo, uint32_t(16 * s + 0) * K4);
+            r.y = bload4s(wrs, vo, uint32_t(16 * s + 1) * K4);
+            r.z = bload4s(wrs, vo, uint32_t(16 * s + 2) * K4);
+            r.w = bload4s(wrs, vo, uint32_t(16 * s + 3) * K4);
+        } else {
+            const int row = 16 * s + 4 * (lane >> 4);
+            auto at = [&](int j) { return row + j < g.OC ? vo + uint32_t(16 * s + j) * K4 : kOffNone; };
+            r.x = bload4s(wrs, at(0), 0);
+            r.y = bload4s(wrs, at(1), 0);
+            r.z = bload4s(wrs, at(2), 0);
+            r.w = bload4s(wrs, at(3), 0);
+        }
         return r;
     };
     float4 ring[D];
 #pragma unroll
-    for (int i = 0; i < D; ++i) ring[i] = mfma_on ? load_blk(w_vo, i) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = 0; i < D; ++i) ring[i] = mfma_on ? load_blk(chunk_vo(w_col), i) : make_float4(0.f, 0.f, 0.f, 0.f);
 
     // dz: the group's gimg*OC*P contiguous elements of dy (and y), 4 per
     // 16-byte load, all of a thread's loads in flight together; element
@@ -210,45 +222,51 @@ __global__ void __launch_bounds__(1024) dgrad_rf_f32(DgradRfArgs a)
     }
     __syncthreads();
 
-    // ---- gather role: sum the taps of 4 images per 16-byte read and store
-    // straight to dx; a store instruction covers 64 consecutive pixels of one
-    // plane, so the 4-byte stores coalesce without staging --------------------
-    const uint32_t plane = uint32_t(g.IC) * g.HW;     // dx elements per image
-    auto gather = [&](int c, const float *dbuf) {
-        if (!gthr) return;
-        const int c0 = c * p.CC;
-        const int cc = min(p.CC, g.IC - c0);
-        const int nplanes = cc * ((gimg + 3) >> 2);
-        int quad = 0, icl = r0;
-        while (icl >= cc) { icl -= cc; ++quad; }
-        for (int pl = r0; pl < nplanes; pl += rpi) {
-            const float *src = dbuf + icl * g.KK * p.RP + quad * 4;
-            f32x4 v[TAPS];
-#pragma unroll
-            for (int j = 0; j < TAPS; ++j) v[j] = *reinterpret_cast<const f32x4 *>(src + toff[j]);
-            f32x4 sum = v[0];
-#pragma unroll
-            for (int j = 1; j < TAPS; ++j) sum += v[j];
-            const int img0 = quad * 4;
-            float *o = a.dx + ((uint32_t(b0 + img0) * g.IC + uint32_t(c0 + icl)) * g.HW + q);
-            if (img0 + 4 <= gimg) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) o[i * plane] = sum[i];
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (img0 + i < gimg) o[i * plane] = sum[i];
-            }
-            icl += rpi;
-            while (icl >= cc) { icl -= cc; ++quad; }
-        }
-    };
-
     // ---- pipeline: iteration it computes chunk it and gathers chunk it-1;
     // every dcol buffer changes hands at a barrier -----------------------------
     if (!mfma_role) {
+        // Gather role: sum the taps of 4 images per 16-byte read and store
+        // straight to dx; a store instruction covers 64 consecutive pixels of
+        // one plane, so the 4-byte stores coalesce without staging.  A chunk's
+        // (channel, image quad) planes are numbered pl = icl*nq + quad; thread
+        // (r0, q) takes planes r0, r0 + rpi, ... (at most NPL), whose LDS and
+        // dx offsets are the same in every chunk up to the dcol buffer and the
+        // chunk's first channel.  Images past the batch have dx offsets past
+        // the end of the tensor, so their stores are dropped.
+        constexpr int NPL = 4;
+        const uint32_t plane4 = uint32_t(g.IC) * g.HW * 4;          // dx bytes per image
+        const __amdgpu_buffer_rsrc_t dxrs = tensor_rsrc(a.dx, uint32_t(g.B) * plane4);
+        const int nq = (gimg + 3) >> 2;
+        int loff[NPL];
+        uint32_t goff[NPL];
+#pragma unroll
+        for (int k = 0; k < NPL; ++k) {
+            const int pl = r0 + k * rpi;
+            const int icl = pl / nq, quad = pl - icl * nq;
+            loff[k] = icl * g.KK * p.RP + quad * 4;
+            goff[k] = ((uint32_t(b0 + 4 * quad) * g.IC + uint32_t(icl)) * g.HW + uint32_t(q)) * 4;
+        }
         for (int it = c_begin; it <= c_end; ++it) {
-            if (it > c_begin) gather(it - 1, dcol + ((it - 1 - c_begin) & 1) * dcol_buf);
+            if (it > c_begin && gthr) {
+                const int c0 = (it - 1) * p.CC;
+                const int nplanes = min(p.CC, g.IC - c0) * nq;
+                const float *dbuf = dcol + ((it - 1 - c_begin) & 1) * dcol_buf;
+                const uint32_t cbase = uint32_t(c0) * g.HW * 4;
+#pragma unroll
+                for (int k = 0; k < NPL; ++k) {
+                    if (r0 + k * rpi < nplanes) {
+                        const float *src = dbuf + loff[k];
+                        f32x4 v[TAPS];
+#pragma unroll
+                        for (int j = 0; j < TAPS; ++j) v[j] = *reinterpret_cast<const f32x4 *>(src + toff[j]);
+                        f32x4 sum = v[0];
+#pragma unroll
+                        for (int j = 1; j < TAPS; ++j) sum += v[j];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) bstore4s(dxrs, sum[i], goff[k] + i * plane4, cbase);
+                    }
+                }
+            }
             __syncthreads();
         }
         return;
@@ -272,6 +290,7 @@ __global__ void __launch_bounds__(1024) dgrad_rf_f32(DgradRfArgs a)
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
                 av[0][mb] = *reinterpret_cast<const float4 *>(arow + mb * 16 * p.OCP);
+            const uint32_t vo = chunk_vo(w_col), vo_next = chunk_vo(w_col + ckk);
 #pragma unroll
             for (int s = 0; s < KS4; ++s) {
                 if (s + 1 < KS4) {
@@ -282,7 +301,7 @@ __global__ void __launch_bounds__(1024) dgrad_rf_f32(DgradRfArgs a)
                 }
                 const float4 bv = ring[s % D];
                 // refill: block s+D of this chunk, else block s+D-KS4 of the next
-                ring[s % D] = s + D < KS4 ? load_blk(w_vo, s + D) : load_blk(w_vo + cbytes, s + D - KS4);
+                ring[s % D] = s + D < KS4 ? load_blk(vo, s + D) : load_blk(vo_next, s + D - KS4);
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -295,7 +314,7 @@ __global__ void __launch_bounds__(1024) dgrad_rf_f32(DgradRfArgs a)
             float *d = dst + ((it - c_begin) & 1) * dcol_buf;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) *reinterpret_cast<f32x4 *>(d + mb * 16) = acc[mb];
-            w_vo += cbytes;
+            w_col += ckk;
         }
         __syncthreads();
     }
@@ -303,24 +322,26 @@ __global__ void __launch_bounds__(1024) dgrad_rf_f32(DgradRfArgs a)
 
 struct DgradRfVariant {
     int NW, MB, KS4, TAPS, NBW;
+    bool exact;          // OC == 16*KS4
     void (*fn)(DgradRfArgs);
 };
 
-#define DR_V(MB, KS4, TAPS, NBW) {16, MB, KS4, TAPS, NBW, dgrad_rf_f32<MB, KS4, TAPS, NBW>}
-#define DR_TAPS(MB, KS4) DR_V(MB, KS4, 2, 1), DR_V(MB, KS4, 4, 1), DR_V(MB, KS4, 9, 1)
+#define DR_V(MB, KS4, TAPS, EX) {16, MB, KS4, TAPS, 1, EX, dgrad_rf_f32<MB, KS4, TAPS, 1, EX>}
+#define DR_TAPS(MB, KS4, EX) DR_V(MB, KS4, 2, EX), DR_V(MB, KS4, 4, EX), DR_V(MB, KS4, 9, EX)
+#define DR_MB(KS4, EX) DR_TAPS(1, KS4, EX), DR_TAPS(2, KS4, EX), DR_TAPS(3, KS4, EX)
 const DgradRfVariant kDgradRfVariants[] = {
-    DR_TAPS(1, 8), DR_TAPS(2, 8), DR_TAPS(3, 8),     // OC 113..128
-    DR_TAPS(1, 4), DR_TAPS(2, 4), DR_TAPS(3, 4),     // OC 49..64
-    DR_TAPS(1, 2), DR_TAPS(2, 2), DR_TAPS(3, 2),     // OC 17..32
-    DR_TAPS(1, 1), DR_TAPS(2, 1), DR_TAPS(3, 1),     // OC 1..16
+    DR_MB(8, true), DR_MB(4, true), DR_MB(2, true), DR_MB(1, true),        // OC 128, 64, 32, 16
+    DR_MB(8, false), DR_MB(4, false), DR_MB(2, false), DR_MB(1, false),    // OC below those
 };
+#undef DR_MB
 #undef DR_TAPS
 #undef DR_V
 
-const DgradRfVariant *pick_dgrad_rf(int NW, int MB, int KS4, int TAPS, int NBW)
+const DgradRfVariant *pick_dgrad_rf(int NW, int MB, int KS4, int TAPS, int NBW, bool exact)
 {
     for (const auto &v : kDgradRfVariants)
-        if (v.NW == NW && v.MB == MB && v.KS4 == KS4 && v.TAPS == TAPS && v.NBW == NBW) return &v;
+        if (v.NW == NW && v.MB == MB && v.KS4 == KS4 && v.TAPS == TAPS && v.NBW == NBW && v.exact == exact)
+            return &v;
     return nullptr;
 }
 
@@ -353,6 +374,9 @@ bool plan_dgrad_rf_f32(const Geom &g, DgradBfPlan &p)
 {
     constexpr int NW = 16, NGT = 512;
     if (g.HW > NGT || g.P > 16) return false;
+    // dx and w byte offsets are 32-bit offsets inside their tensors
+    if (size_t(g.B) * g.IC * g.HW * 4 >= (size_t(1) << 31) || size_t(g.OC) * g.K * 4 >= (size_t(1) << 31))
+        return false;
     const int ks4 = (g.OC + 15) / 16;
     const int KS4 = ks4 <= 1 ? 1 : ks4 <= 2 ? 2 : ks4 <= 4 ? 4 : ks4 <= 8 ? 8 : 0;
     if (!KS4) return false;
@@ -373,6 +397,7 @@ bool plan_dgrad_rf_f32(const Geom &g, DgradBfPlan &p)
         for (int CC = 1; CC <= g.IC; ++CC) {
             const int NBC = (CC * g.KK + 15) / 16;
             if (NBC > 8) break;
+            if ((CC * (G / 4) + rpi - 1) / rpi > 4) break;   // planes per gather thread
             const int NBW = 1;
             const size_t lds = dz_bytes + 2 * size_t(NBC) * 16 * RP * 4;
             if (lds > 160 * 1024) break;
@@ -388,7 +413,7 @@ bool plan_dgrad_rf_f32(const Geom &g, DgradBfPlan &p)
             const double per_wg = cpg * chunk + 2500.0;
             const double t = std::ceil(double(ngroups) * cgroups / 256.0) * per_wg;
             if (t < best - 1e-9) {
-                if (!pick_dgrad_rf(NW, MB, KS4, TAPS, NBW)) continue;
+                if (!pick_dgrad_rf(NW, MB, KS4, TAPS, NBW, g.OC == 16 * KS4)) continue;
                 best = t;
                 p.NW = NW; p.G = G; p.MB = MB; p.KS = KS4; p.TAPS = TAPS; p.NBW = NBW; p.GP = 0;
                 p.CC = CC; p.NBC = NBC; p.nchunks = nchunks; p.cgroups = cgroups; p.cpg = cpg;
@@ -405,12 +430,16 @@ bool plan_dgrad_rf_f32(const Geom &g, DgradBfPlan &p)
 hipError_t launch_dgrad_rf_f32(const Geom &g, const DgradBfPlan &p, const void *dy, const void *w,
                                const void *ym, void *dx, int relu, hipStream_t s)
 {
-    const DgradRfVariant *v = pick_dgrad_rf(p.NW, p.MB, p.KS, p.TAPS, p.NBW);
+    const DgradRfVariant *v = pick_dgrad_rf(p.NW, p.MB, p.KS, p.TAPS, p.NBW, g.OC == 16 * p.KS);
     if (!v || p.NW != 16 || g.HW > 512 || p.G % 4 || p.G * g.P > 16 * p.MB || p.NBC > 8 * p.NBW ||
         p.RP < 16 * p.MB + p.G)
         return hipErrorInvalidValue;
-    // weight offsets are 32-bit byte offsets inside the tensor
-    if (size_t(g.OC) * g.K * 4 >= (size_t(1) << 31)) return hipErrorInvalidValue;
+    // at most four planes per gather thread and chunk; dx and w byte offsets
+    // are 32-bit offsets inside their tensors
+    const int rpi = 512 / g.HW;
+    if ((p.CC * (p.G / 4) + rpi - 1) / rpi > 4 || size_t(g.OC) * g.K * 4 >= (size_t(1) << 31) ||
+        size_t(g.B) * g.IC * g.HW * 4 >= (size_t(1) << 31))
+        return hipErrorInvalidValue;
     DgradRfArgs a{g, (const float *)dy, (const float *)ym, (const float *)w, (float *)dx, relu, p,
                   make_fastdiv(g.OC * g.P)};
     hipError_t e = allow_max_lds(reinterpret_cast<const void *>(v->fn));

@@ -109,6 +109,12 @@ __device__ __forceinline__ float bload4s(__amdgpu_buffer_rsrc_t r, uint32_t voff
 {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
+// store 4 bytes at byte offset voff + soff; a store whose voff alone is at
+// or past the end of the tensor is dropped
+__device__ __forceinline__ void bstore4s(__amdgpu_buffer_rsrc_t r, float v, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+}
 constexpr uint32_t kOffNone = 0xFFFFFFF0u;   // an offset past the end of every tensor
 
 // s_waitcnt vmcnt(0): every vector memory operation this wave has issued has
