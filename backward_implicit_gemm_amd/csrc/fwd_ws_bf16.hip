@@ -22,6 +22,16 @@
 //     weight fragments, and start on phase ph as soon as its barrier passes.
 // With NBW = 2 each A fragment read from LDS feeds two MFMAs.  The whole x
 // tile has its own LDS, so no phase waits for a buffer to drain.
+//
+// A workgroup walks image groups grp = blockIdx.x, + gridDim.x, ... (one per
+// workgroup when the batch gives no more groups than the grid has slots).
+// Only one workgroup fits on a CU (the x tile fills most of its LDS), so the
+// next group is pipelined inside the workgroup instead: as soon as a loader
+// thread has stored phase ph of the current group, it issues the loads of
+// phase ph of its next group into the same registers, and stores them once
+// the MFMA waves have finished phase ph of the current group (one barrier per
+// phase, at least two phases per group).  The weight ring runs on from one
+// group into the next without a break (its slot pattern repeats per group).
 #include "gc_kernels.h"
 #include "ig_common.h"
 
@@ -57,9 +67,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
     const Geom &g = a.g;
     constexpr int NPH = (NCG + CPP - 1) / CPP;
     constexpr int NFRAG = NCG * TS;
+    static_assert(NFRAG % D == 0, "the ring's slot pattern must repeat per image group");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int b0 = blockIdx.x * a.G;
-    const int gimg = min(a.G, g.B - b0);
+    const int ngroups = (g.B + a.G - 1) / a.G;
+    const int nmine = (ngroups - int(blockIdx.x) + int(gridDim.x) - 1) / int(gridDim.x);
     const int gstride = a.G * a.IS;                  // 16-byte slots per channel group
 
     if (wave >= kMfmaWaves) {
@@ -69,13 +80,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
         const int u_blk = lt % a.nblk, u_img = (lt / a.nblk) % a.G, u_cgl = lt / units_per_cg;
         const bool u_unit = u_cgl < CPP;
         const int u_w0 = min(8 * u_blk, g.HW - 8);
-        const bool img_ok = u_img < gimg;
         const uint32_t plane = uint32_t(g.HW) * 2;
-        const uint32_t u_off = (uint32_t(b0 + u_img) * g.IC * g.HW + u_w0) * 2;
         const __amdgpu_buffer_rsrc_t xrs = tensor_rsrc(a.x, uint32_t(g.B) * g.IC * plane);
         uint32_t in[NPH][8][4];
-#pragma unroll
-        for (int ph = 0; ph < NPH; ++ph) {
+        // loads of phase ph of image group grp (zeros past the batch)
+        auto fetch = [&](int grp, int ph) {
+            const int b0 = grp * a.G;
+            const bool img_ok = u_img < min(a.G, g.B - b0);
+            const uint32_t u_off = (uint32_t(b0 + u_img) * g.IC * g.HW + u_w0) * 2;
             const int cg = ph * CPP + u_cgl;
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
@@ -84,8 +96,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
                 const uint4 v = bload16u(xrs, ok ? u_off + uint32_t(ic) * plane : kOffNone);
                 in[ph][c][0] = v.x; in[ph][c][1] = v.y; in[ph][c][2] = v.z; in[ph][c][3] = v.w;
             }
-        }
+        };
+#pragma unroll
+        for (int ph = 0; ph < NPH; ++ph) fetch(blockIdx.x, ph);
         const int ih0 = u_w0 / g.W, iw0 = u_w0 - ih0 * g.W;
+        for (int i = 0; i < nmine; ++i) {
 #pragma unroll
         for (int ph = 0; ph < NPH; ++ph) {
             const int cg = ph * CPP + u_cgl;
@@ -107,29 +122,36 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
                     if (++iw == g.W) { iw = 0; ++ih; }
                 }
             }
+            // phase ph of the next group; the last group loads group 0 again
+            // (in bounds, never stored) so that no branch guards the loads
+            fetch(i + 1 < nmine ? int(blockIdx.x) + (i + 1) * int(gridDim.x) : 0, ph);
             __syncthreads();                         // phase ph is in LDS
+        }
         }
         return;
     }
 
     // ---- MFMA waves: NBW 16-channel blocks each ----
     const int nb0 = (blockIdx.y * kMfmaWaves + wave) * NBW;
-    const uint4 *wf_wave = a.wf + size_t(nb0) * NFRAG * 64 + lane;
-    // fragment f of block j streams through ring[j][f % D], D fragments ahead
+    // fragment f of block j streams through ring[j][f % D], D fragments
+    // ahead: a buffer load at lane offset w_vo plus the constant (j*NFRAG +
+    // f)*1024, so no per-fragment address is held in registers
+    const __amdgpu_buffer_rsrc_t wrs = tensor_rsrc(a.wf, uint32_t(gridDim.y) * kMfmaWaves * NBW * NFRAG * 1024);
+    const uint32_t w_vo = (uint32_t(nb0) * NFRAG * 64 + lane) * 16;
     uint4 ring[NBW][D];
 #pragma unroll
     for (int j = 0; j < NBW; ++j)
 #pragma unroll
-        for (int i = 0; i < D; ++i)
-            ring[j][i] = i < NFRAG ? wf_wave[(size_t(j) * NFRAG + i) * 64] : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < D; ++i) ring[j][i] = bload16us(wrs, w_vo, (j * NFRAG + i) * 1024);
 
-    const int rows = gimg * g.P;
+    // rows past a group's images read image slots the loaders filled with
+    // zeros (or nothing the epilogue stores)
     int rowoff[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
         const int r = mb * 16 + (lane & 15);
         rowoff[mb] = 0;
-        if (r < rows) {
+        if (r < a.G * g.P) {
             uint32_t img, pp, oh, ow;
             fdivmod(r, g.fd_P, img, pp);
             fdivmod(pp, g.fd_OW, oh, ow);
@@ -148,6 +170,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
         }
     }
 
+    for (int i = 0; i < nmine; ++i) {
+    const int b0 = (int(blockIdx.x) + i * int(gridDim.x)) * a.G;
+    const int rows = min(a.G, g.B - b0) * g.P;
+    // The LDS read addresses are the same for every group; re-defining the
+    // group stride opaquely in each iteration keeps the compiler from
+    // computing all of them before the loop and holding them in registers.
+    int gs = gstride;
+    asm volatile("" : "+s"(gs));
     f32x4 acc[NBW][MB];
 #pragma unroll
     for (int j = 0; j < NBW; ++j)
@@ -159,7 +189,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
         __syncthreads();                             // wait for phase ph
 #pragma unroll
         for (int cg = ph * CPP; cg < (ph + 1) * CPP && cg < NCG; ++cg) {
-            const uint4 *xb = lds4 + cg * gstride;
+            const uint4 *xb = lds4 + cg * gs;
             uint4 af[TS][MB];
 #pragma unroll
             for (int st = 0; st < TS; ++st)
@@ -172,7 +202,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
 #pragma unroll
                 for (int j = 0; j < NBW; ++j) {
                     bv[j] = __builtin_bit_cast(bf16x8, ring[j][f % D]);
-                    if (f + D < NFRAG) ring[j][f % D] = wf_wave[(size_t(j) * NFRAG + f + D) * 64];
+                    // the fragment D ahead, into the next group's first ones
+                    // (after the last group they are loaded and not used)
+                    ring[j][f % D] = bload16us(wrs, w_vo, (j * NFRAG + (f + D) % NFRAG) * 1024);
                 }
 #pragma unroll
                 for (int j = 0; j < NBW; ++j)
@@ -203,6 +235,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
                 a.y[(size_t(b0 + int(img)) * g.OC + n) * g.P + int(pp)] = from_f32<bf16_t>(val);
             }
     }
+    }
 }
 
 struct FwdWsVariant {
@@ -211,8 +244,8 @@ struct FwdWsVariant {
 };
 #define WS_V(NBW, MB, TS, NCG, CPP, D) {NBW, MB, TS, NCG, CPP, fwd_ws_bf16<NBW, MB, TS, NCG, CPP, D>}
 const FwdWsVariant kFwdWsVariants[] = {
-    WS_V(2, 3, 7, 8, 3, 12),    // 59 -> 128, 11x15, 5x5, stride 3: 4 images, 48 rows
-    WS_V(2, 1, 7, 8, 8, 12),    // the same layer, one image per workgroup
+    WS_V(2, 3, 7, 8, 3, 14),    // 59 -> 128, 11x15, 5x5, stride 3: 4 images, 48 rows
+    WS_V(2, 1, 7, 8, 8, 14),    // the same layer, one image per workgroup
     WS_V(1, 1, 3, 16, 16, 16),  // 128 -> 128, 3x4, 3x3: 8 images, 16 rows
     WS_V(1, 4, 3, 16, 4, 16),   // the same layer at large batch: 32 images
 };
@@ -279,7 +312,15 @@ hipError_t launch_fwd_ws_bf16(const Geom &g, const FwdWsPlan &p, const void *x, 
                 p.G, p.WP, p.IS, p.nblk};
     e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(v->fn, dim3((g.B + p.G - 1) / p.G, p.ntile), dim3(kThreads), p.lds, s, a);
+    // one workgroup per CU (the x tile takes most of its LDS): at most one
+    // round of workgroups, each walking its share of the image groups.  The
+    // next group's phase ph overwrites this group's phase ph only two
+    // barriers later if there are at least two phases; with one, every
+    // workgroup takes a single group.
+    const int ngroups = (g.B + p.G - 1) / p.G;
+    const int nph = (p.NCG + p.CPP - 1) / p.CPP;
+    const int gx = nph >= 2 ? std::min(ngroups, std::max(1, 256 / p.ntile)) : ngroups;
+    hipLaunchKernelGGL(v->fn, dim3(gx, p.ntile), dim3(kThreads), p.lds, s, a);
     return hipGetLastError();
 }
 
