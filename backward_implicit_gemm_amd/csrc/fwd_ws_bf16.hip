@@ -190,13 +190,17 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
 #pragma unroll
         for (int cg = ph * CPP; cg < (ph + 1) * CPP && cg < NCG; ++cg) {
             const uint4 *xb = lds4 + cg * gs;
-            uint4 af[TS][MB];
+            // A fragments one tap step ahead of their MFMAs (two register
+            // sets), which leaves the registers for a deep weight ring
+            uint4 af[2][MB];
 #pragma unroll
-            for (int st = 0; st < TS; ++st)
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb) af[st][mb] = xb[rowoff[mb] + toff[st]];
+            for (int mb = 0; mb < MB; ++mb) af[0][mb] = xb[rowoff[mb] + toff[0]];
 #pragma unroll
             for (int st = 0; st < TS; ++st) {
+                if (st + 1 < TS) {
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) af[(st + 1) & 1][mb] = xb[rowoff[mb] + toff[st + 1]];
+                }
                 const int f = cg * TS + st;
                 bf16x8 bv[NBW];
 #pragma unroll
@@ -206,12 +210,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
                     // (after the last group they are loaded and not used)
                     ring[j][f % D] = bload16us(wrs, w_vo, (j * NFRAG + (f + D) % NFRAG) * 1024);
                 }
+                // Without this the scheduler sinks each refill load down to
+                // just before its use, D steps later, and waits for it there:
+                // the ring would then hide no latency at all.
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int j = 0; j < NBW; ++j)
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb)
                         acc[j][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, af[st][mb]), bv[j], acc[j][mb], 0, 0, 0);
+                            __builtin_bit_cast(bf16x8, af[st & 1][mb]), bv[j], acc[j][mb], 0, 0, 0);
             }
         }
     }
@@ -244,8 +252,8 @@ struct FwdWsVariant {
 };
 #define WS_V(NBW, MB, TS, NCG, CPP, D) {NBW, MB, TS, NCG, CPP, fwd_ws_bf16<NBW, MB, TS, NCG, CPP, D>}
 const FwdWsVariant kFwdWsVariants[] = {
-    WS_V(2, 3, 7, 8, 3, 14),    // 59 -> 128, 11x15, 5x5, stride 3: 4 images, 48 rows
-    WS_V(2, 1, 7, 8, 8, 14),    // the same layer, one image per workgroup
+    WS_V(2, 3, 7, 8, 3, 7),    // 59 -> 128, 11x15, 5x5, stride 3: 4 images, 48 rows
+    WS_V(2, 1, 7, 8, 8, 7),    // the same layer, one image per workgroup
     WS_V(1, 1, 3, 16, 16, 16),  // 128 -> 128, 3x4, 3x3: 8 images, 16 rows
     WS_V(1, 4, 3, 16, 4, 16),   // the same layer at large batch: 32 images
 };
