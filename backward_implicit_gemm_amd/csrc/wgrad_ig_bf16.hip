@@ -64,7 +64,7 @@ bool plan_wgrad_ig_bf16(const Geom &g, WgradBfPlan &p)
     if (g.HW < 8) return false;
     const int nblk = (g.HW + 7) / 8;
     if (2 * CCW * nblk > kWgNT) return false;
-    const int HWP = nblk * 8;
+    const int HWP = nblk * 9;        // 8-pixel blocks of 9 LDS slots (see xslot)
     const size_t lds = 2 * (size_t(CCW) * HWP + size_t(PP) * 128) * 16;
     if (lds > 160 * 1024) return false;
     const int ngroups = (g.B + 7) / 8;

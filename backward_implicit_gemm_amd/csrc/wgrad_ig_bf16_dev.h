@@ -20,6 +20,12 @@ __device__ __forceinline__ uint4 ldg16(const u16 *p)
     return v;
 }
 
+// LDS slot of pixel p in a staged x plane: every 8-pixel block takes 9
+// slots.  The loader threads that store one pixel step together hold
+// consecutive 8-pixel blocks; without the skip their 16-byte slots are 128
+// bytes apart and every second one falls on the same four banks.
+__device__ __forceinline__ int xslot(int p) { return p + (p >> 3); }
+
 // dzg unit ((bg*PP + p)*128 + oc) = the 8 images of group bg at (oc, p),
 // masked; zero for positions >= P, channels >= OC and images >= B.  One
 // workgroup per group: the group's images are contiguous in dy and y
@@ -144,14 +150,15 @@ __device__ __forceinline__ void wgrad_ig_bf16_body(const WgradBfArgs &a, int bid
     // B (x): column n = n0 + 32*wn + 16*j + lane%16 -> (ic, kh, kw); position
     // p = 4*s + lane/16 -> pixel (oh*S, ow*S).  Padded columns and positions
     // read a valid pixel; their dz is zero or their result is not stored.
-    int xcol[2], xrow[NSTEP], drow[NSTEP];
+    int xcol[2], xpl[2], xrow[NSTEP], drow[NSTEP];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int n = min(n0 + 32 * wn + 16 * j + (lane & 15), N - 1);
         uint32_t ic, kk, kh, kw;
         fdivmod(uint32_t(n), g.fd_KK, ic, kk);
         fdivmod(kk, g.fd_KW, kh, kw);
-        xcol[j] = (int(ic) - c_lo) * p.HWP + int(kh) * g.W + int(kw);
+        xpl[j] = (int(ic) - c_lo) * p.HWP;
+        xcol[j] = int(kh) * g.W + int(kw);
     }
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
@@ -162,6 +169,11 @@ __device__ __forceinline__ void wgrad_ig_bf16_body(const WgradBfArgs &a, int bid
         xrow[s] = int(oh) * g.S * g.W + int(ow) * g.S;
         drow[s] = pp * 128 + 64 * wm + (lane & 15);
     }
+    int xoff[2][NSTEP];      // LDS slot of this lane's B value per column block and step
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int s = 0; s < NSTEP; ++s) xoff[j][s] = xpl[j] + xslot(xcol[j] + xrow[s]);
 
     // ---- staging -----------------------------------------------------------
     // x unit (icl, blk, half): pixels [pix, pix+8) of channel c_lo + icl for
@@ -201,7 +213,7 @@ __device__ __forceinline__ void wgrad_ig_bf16_body(const WgradBfArgs &a, int bid
             }
             // pixel pp's 16-byte slot holds images 0..7; this thread writes
             // the 8 bytes of its four: word j = images (2j, 2j+1)
-            uint2 *dst = reinterpret_cast<uint2 *>(xs + buf * xbuf + xicl * p.HWP + xpix) + xhalf;
+            uint4 *plane = xs + buf * xbuf + xicl * p.HWP;
 #pragma unroll
             for (int pp = 0; pp < 8; ++pp) {
                 const int wi = pp >> 1;
@@ -211,7 +223,7 @@ __device__ __forceinline__ void wgrad_ig_bf16_body(const WgradBfArgs &a, int bid
                     const uint32_t lo = in[2 * j][wi], hi = in[2 * j + 1][wi];
                     o[j] = (pp & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
                 }
-                dst[2 * pp] = make_uint2(o[0], o[1]);
+                reinterpret_cast<uint2 *>(plane + xslot(xpix + pp))[xhalf] = make_uint2(o[0], o[1]);
             }
         }
         uint4 *dd = ds + buf * dbuf;
@@ -234,7 +246,7 @@ __device__ __forceinline__ void wgrad_ig_bf16_body(const WgradBfArgs &a, int bid
 #pragma unroll
             for (int i = 0; i < 4; ++i) af[i] = __builtin_bit_cast(bf16x8, db[drow[s] + 16 * i]);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) bfr[j] = __builtin_bit_cast(bf16x8, xb[xcol[j] + xrow[s]]);
+            for (int j = 0; j < 2; ++j) bfr[j] = __builtin_bit_cast(bf16x8, xb[xoff[j][s]]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -323,14 +335,15 @@ __device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid
     // B (x): column n = n0 + 32*wn + 16*j + lane%16 -> (ic, kh, kw); position
     // p = 4*s + lane/16 -> pixel (oh*S, ow*S).  Padded columns and positions
     // read a valid pixel; their dz is zero or their result is not stored.
-    int xcol[2], xrow[NSTEP], drow[NSTEP];
+    int xcol[2], xpl[2], xrow[NSTEP], drow[NSTEP];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int n = min(n0 + 32 * wn + 16 * j + (lane & 15), N - 1);
         uint32_t ic, kk, kh, kw;
         fdivmod(uint32_t(n), g.fd_KK, ic, kk);
         fdivmod(kk, g.fd_KW, kh, kw);
-        xcol[j] = (int(ic) - c_lo) * p.HWP + int(kh) * g.W + int(kw);
+        xpl[j] = (int(ic) - c_lo) * p.HWP;
+        xcol[j] = int(kh) * g.W + int(kw);
     }
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
@@ -341,6 +354,11 @@ __device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid
         xrow[s] = int(oh) * g.S * g.W + int(ow) * g.S;
         drow[s] = pp * 128 + 64 * wm + (lane & 15);
     }
+    int xoff[2][NSTEP];      // LDS slot of this lane's B value per column block and step
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int s = 0; s < NSTEP; ++s) xoff[j][s] = xpl[j] + xslot(xcol[j] + xrow[s]);
 
     // ---- staging -----------------------------------------------------------
     // x unit (icl, blk, half): pixels [pix, pix+8) of channel c_lo + icl for
@@ -380,7 +398,7 @@ __device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid
             }
             // pixel pp's 16-byte slot holds images 0..7; this thread writes
             // the 8 bytes of its four: word j = images (2j, 2j+1)
-            uint2 *dst = reinterpret_cast<uint2 *>(xs + buf * xbuf + xicl * p.HWP + xpix) + xhalf;
+            uint4 *plane = xs + buf * xbuf + xicl * p.HWP;
 #pragma unroll
             for (int pp = 0; pp < 8; ++pp) {
                 const int wi = pp >> 1;
@@ -390,7 +408,7 @@ __device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid
                     const uint32_t lo = in[2 * j][wi], hi = in[2 * j + 1][wi];
                     o[j] = (pp & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
                 }
-                dst[2 * pp] = make_uint2(o[0], o[1]);
+                reinterpret_cast<uint2 *>(plane + xslot(xpix + pp))[xhalf] = make_uint2(o[0], o[1]);
             }
         }
         uint4 *dd = ds + buf * dbuf;
@@ -413,7 +431,7 @@ __device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid
 #pragma unroll
             for (int i = 0; i < 4; ++i) af[i] = __builtin_bit_cast(bf16x8, db[drow[s] + 16 * i]);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) bfr[j] = __builtin_bit_cast(bf16x8, xb[xcol[j] + xrow[s]]);
+            for (int j = 0; j < 2; ++j) bfr[j] = __builtin_bit_cast(bf16x8, xb[xoff[j][s]]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
