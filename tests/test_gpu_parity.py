@@ -223,3 +223,19 @@ def test_bf16_rounding_is_nearest_even():
     _, y, _, _ = gpu_layer(layer, x, w, dy, "bf16")
     want = (x.float() * w.float()).to(torch.bfloat16)
     assert torch.equal(y.cpu(), want)
+
+
+# ---------------------------------------------------------------------------
+# Batches with more image groups than the bf16 forward's single round of
+# workgroups: each workgroup walks two or three groups, the last one ragged
+# (2054 = 513*4 + 2 images of layer 1; 8300 = 259*32 + 12 of layer 2)
+# ---------------------------------------------------------------------------
+
+SEVERAL_GROUPS = [(2054, 59, 11, 15, 128, 5, 5, 3, 1), (8300, 128, 3, 4, 128, 3, 3, 1, 0)]
+
+
+@pytest.mark.parametrize("shape", SEVERAL_GROUPS, ids=["layer1_b2054", "layer2_b8300"])
+def test_bf16_several_groups_per_workgroup(shape):
+    layer = Layer(*shape)
+    errs, _, _ = check_layer(layer, "bf16", seeds=(5, 6, 7))
+    print(f"{shape}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
