@@ -58,6 +58,8 @@ struct FwdWsArgs {
     int WP;       // LDS pixel slots per image row (>= W)
     int IS;       // LDS pixel slots per image (>= H*WP)
     int nblk;     // 8-pixel blocks per image plane
+    int ystage;   // stage the output through LDS (every channel of every wave real, P*NBW*16 % 8 == 0)
+    int ybase;    // 16-byte LDS slot where the waves' output staging regions start
 };
 
 template <int NBW, int MB, int TS, int NCG, int CPP, int D>
@@ -224,7 +226,42 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
         }
     }
 
-    // epilogue: row r = mb*16 + 4*(lane/16) + v, column (nb0 + j)*16 + lane%16
+    // epilogue: row r = mb*16 + 4*(lane/16) + v, column (nb0 + j)*16 + lane%16.
+    // Staged: the wave's NBW*16 channels of each image are one contiguous run
+    // of y (NBW*16*P elements), so they go through the wave's own LDS region
+    // ([img][channel][position], bf16) and leave in 16-byte stores instead of
+    // 2-byte ones.  Only this wave touches the region, and its LDS accesses
+    // are in order, so no barrier is needed.
+    if (a.ystage) {
+        const int run = NBW * 16 * g.P;                          // elements per image
+        u16 *st = reinterpret_cast<u16 *>(lds4 + a.ybase) + wave * a.G * run;
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+            const int nl = j * 16 + (lane & 15);
+            const float bn = a.bias ? __uint_as_float(uint32_t(a.bias[nb0 * 16 + nl]) << 16) : 0.f;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = mb * 16 + (lane >> 4) * 4 + v;
+                    if (r >= rows) continue;
+                    uint32_t img, pp;
+                    fdivmod(r, g.fd_P, img, pp);
+                    float val = acc[j][mb][v] + bn;
+                    if (a.relu && !(val > 0.f)) val = 0.f;
+                    st[(int(img) * NBW * 16 + nl) * g.P + int(pp)] = from_f32<bf16_t>(val);
+                }
+        }
+        __builtin_amdgcn_wave_barrier();
+        const int units = run / 8, gimg = rows / g.P;
+        for (int u = lane; u < gimg * units; u += 64) {
+            const int img = u / units, k = u - img * units;
+            const uint4 v = *reinterpret_cast<const uint4 *>(st + img * run + 8 * k);
+            __builtin_memcpy(a.y + (size_t(b0 + img) * g.OC + nb0 * 16) * g.P + 8 * k, &v, 16);
+        }
+        __builtin_amdgcn_wave_barrier();     // the region is rewritten for the next group
+        continue;
+    }
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
         const int n = (nb0 + j) * 16 + (lane & 15);
@@ -296,6 +333,9 @@ bool plan_fwd_ws_bf16(const Geom &g, FwdWsPlan &p)
         if (!pick_fwd_ws(NBW, q.MB, TS, NCG, q.CPP)) continue;
         pick_lds_pitch(g, G, q.MB, TS, q.WP, q.IS);
         q.lds = sizeof(uint4) * size_t(NCG) * G * q.IS;
+        // output staging: one region per MFMA wave, G images x NBW*16 channels x P
+        q.ystage = g.OC % (64 * NBW) == 0 && (g.P * NBW * 16) % 8 == 0;
+        if (q.ystage) q.lds += size_t(kMfmaWaves) * G * NBW * 16 * g.P * 2;
         if (q.lds > 150 * 1024) continue;
         q.ws_bytes = size_t(q.ntile) * kMfmaWaves * NBW * NCG * TS * 64 * 16;
         const double fill = double(G * g.P) / (16.0 * q.MB);
@@ -316,8 +356,10 @@ hipError_t launch_fwd_ws_bf16(const Geom &g, const FwdWsPlan &p, const void *x, 
     hipError_t e = launch_pack_w_fwd_bf16(g, p.NCG, p.TS, p.ntile * kMfmaWaves * p.NBW, w, ws,
                                           p.ws_bytes, s);
     if (e != hipSuccess) return e;
+    if (p.ystage && (g.OC % (64 * p.NBW) || (reinterpret_cast<uintptr_t>(y) & 15)))
+        return hipErrorInvalidValue;
     FwdWsArgs a{g, (const u16 *)x, (const uint4 *)ws, (const u16 *)bias, (u16 *)y, relu,
-                p.G, p.WP, p.IS, p.nblk};
+                p.G, p.WP, p.IS, p.nblk, p.ystage, p.NCG * p.G * p.IS};
     e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
     if (e != hipSuccess) return e;
     // one workgroup per CU (the x tile takes most of its LDS): at most one

@@ -165,6 +165,7 @@ struct FwdWsPlan {
     int NCG;      // channel groups (8 channels bf16, 4 fp32)
     int CPP;      // channel groups per staging phase
     int ntile;    // column tiles
+    int ystage;   // bf16: output staged through LDS for 16-byte stores
     size_t lds;       // the whole x tile (bf16), two phase buffers (fp32)
     size_t ws_bytes;  // packed weights
 };
