@@ -119,3 +119,15 @@ def test_bias_grad_deterministic():
         conv.bwd_bias(dyd, y, db2)
         torch.cuda.synchronize()
         assert torch.equal(db2.view(torch.int32), db.view(torch.int32))
+
+
+@pytest.mark.parametrize("shape", [(2054, 59, 11, 15, 128, 5, 5, 3, 1), (8300, 128, 3, 4, 128, 3, 3, 1, 0)],
+                         ids=["layer1_b2054", "layer2_b8300"])
+def test_bias_bf16_several_groups_per_workgroup(shape):
+    # batches whose bf16 forward workgroups each walk two or three image
+    # groups, the last one ragged, with the bias added in the staged epilogue
+    layer = Layer(*shape)
+    x, w, dy = draw(layer, (9, 10, 11), "bf16")
+    b = _bias(layer, 78, "bf16")
+    ey, eb, _, _ = _check(layer, "bf16", x, w, b, dy)
+    print(f"{shape}: y(bias)={ey:.2e} db={eb:.2e}", flush=True)
