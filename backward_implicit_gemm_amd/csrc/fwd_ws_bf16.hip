@@ -32,6 +32,9 @@
 // the MFMA waves have finished phase ph of the current group (one barrier per
 // phase, at least two phases per group).  The weight ring runs on from one
 // group into the next without a break (its slot pattern repeats per group).
+// Each MFMA wave writes a group's output through a private LDS region as
+// contiguous 16-byte stores: scattered 2-byte stores would sit in its
+// in-order memory counter ahead of the next group's ring loads.
 #include "gc_kernels.h"
 #include "ig_common.h"
 
