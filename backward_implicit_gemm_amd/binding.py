@@ -21,6 +21,7 @@ EXPORTED = (
     "gc_conv_out_dims", "gc_conv_workspace_bytes", "gc_conv_fwd", "gc_conv_bwd_data",
     "gc_conv_bwd_weight", "gc_status_string", "gc_fastdiv_selfcheck", "gc_version",
     "gc_set_kernel_policy", "gc_conv_fwd_bias", "gc_conv_bwd_bias", "gc_conv_bwd",
+    "gc_conv_plan_name",
 )
 GC_POLICY_AUTO, GC_POLICY_GENERIC = 0, 1
 
@@ -68,6 +69,8 @@ def lib():
     L.gc_status_string.restype = ctypes.c_char_p
     L.gc_fastdiv_selfcheck.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
     L.gc_fastdiv_selfcheck.restype = ctypes.c_int64
+    L.gc_conv_plan_name.argtypes = [i, dp, i, ctypes.c_char_p, sz]
+    L.gc_conv_plan_name.restype = i
     L.gc_version.argtypes = []
     L.gc_version.restype = i
     L.gc_set_kernel_policy.argtypes = [i]
@@ -113,12 +116,35 @@ def gc_conv_workspace_bytes(op, desc, dtype):
     return int(lib().gc_conv_workspace_bytes(int(op), ctypes.byref(desc), int(dtype)))
 
 
+def gc_conv_plan_name(op, desc, dtype):
+    """The kernels `op` would run for this problem (host only, enqueues nothing)."""
+    buf = ctypes.create_string_buffer(256)
+    st = lib().gc_conv_plan_name(int(op), ctypes.byref(desc), int(dtype), buf, len(buf))
+    _check("gc_conv_plan_name", st)
+    return buf.value.decode()
+
+
 def _dtype_code(t):
     if t.dtype == torch.float32:
         return GC_F32
     if t.dtype == torch.bfloat16:
         return GC_BF16
     raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
+
+
+def _expect(t, name, shape):
+    """Raises ValueError unless tensor t (if given) has exactly this shape;
+    checked before anything touches the device, so a wrongly sized buffer
+    never reaches the kernels."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(int(v) for v in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _y_shape(desc):
+    oh, ow = gc_conv_out_dims(desc)
+    return (desc.B, desc.OC, oh, ow)
 
 
 def _dev(t, name, dtype):
@@ -164,6 +190,7 @@ def gc_conv_fwd(x, w, y, relu, stride, workspace=None, stream=None):
     """y = relu?(conv(x, w)) via the C entry point gc_conv_fwd."""
     dt = _dtype_code(x)
     desc = desc_from(x.shape, w.shape, stride)
+    _expect(y, "y", _y_shape(desc))
     wp, wn = _ws(workspace)
     st = lib().gc_conv_fwd(_dev(x, "x", dt), _dev(w, "w", dt), _dev(y, "y", dt), wp, wn,
                            ctypes.byref(desc), int(relu), dt, _stream(stream))
@@ -175,6 +202,8 @@ def gc_conv_fwd_bias(x, w, bias, y, relu, stride, workspace=None, stream=None):
     """y = relu?(conv(x, w) + bias) via the C entry point gc_conv_fwd_bias."""
     dt = _dtype_code(x)
     desc = desc_from(x.shape, w.shape, stride)
+    _expect(y, "y", _y_shape(desc))
+    _expect(bias, "bias", (desc.OC,))
     wp, wn = _ws(workspace)
     st = lib().gc_conv_fwd_bias(_dev(x, "x", dt), _dev(w, "w", dt), _dev(bias, "bias", dt),
                                 _dev(y, "y", dt), wp, wn, ctypes.byref(desc), int(relu), dt,
@@ -187,6 +216,10 @@ def gc_conv_bwd_bias(dy, y_mask, db, relu, x_shape, w_shape, stride, workspace, 
     """db[oc] = sum of dy (masked by y_mask > 0 when relu) via gc_conv_bwd_bias."""
     dt = _dtype_code(dy)
     desc = desc_from(x_shape, w_shape, stride)
+    ys = _y_shape(desc)
+    _expect(dy, "dy", ys)
+    _expect(y_mask, "y_mask", ys)
+    _expect(db, "db", (desc.OC,))
     wp, wn = _ws(workspace)
     st = lib().gc_conv_bwd_bias(_dev(dy, "dy", dt), _dev(y_mask, "y_mask", dt), _dev(db, "db", dt),
                                 wp, wn, ctypes.byref(desc), int(relu), dt, _stream(stream))
@@ -198,6 +231,9 @@ def gc_conv_bwd_data(dy, w, y_mask, dx, relu, stride, workspace=None, stream=Non
     """dx from dy (masked by y_mask > 0 when relu) via gc_conv_bwd_data."""
     dt = _dtype_code(dy)
     desc = desc_from(dx.shape, w.shape, stride)
+    ys = _y_shape(desc)
+    _expect(dy, "dy", ys)
+    _expect(y_mask, "y_mask", ys)
     wp, wn = _ws(workspace)
     st = lib().gc_conv_bwd_data(_dev(dy, "dy", dt), _dev(w, "w", dt), _dev(y_mask, "y_mask", dt),
                                 _dev(dx, "dx", dt), wp, wn, ctypes.byref(desc), int(relu), dt,
@@ -210,6 +246,9 @@ def gc_conv_bwd_weight(x, dy, y_mask, dw, relu, stride, workspace, stream=None):
     """dw from x and dy (masked by y_mask > 0 when relu) via gc_conv_bwd_weight."""
     dt = _dtype_code(x)
     desc = desc_from(x.shape, dw.shape, stride)
+    ys = _y_shape(desc)
+    _expect(dy, "dy", ys)
+    _expect(y_mask, "y_mask", ys)
     wp, wn = _ws(workspace)
     st = lib().gc_conv_bwd_weight(_dev(x, "x", dt), _dev(dy, "dy", dt), _dev(y_mask, "y_mask", dt),
                                   _dev(dw, "dw", dt), wp, wn, ctypes.byref(desc), int(relu), dt,
@@ -222,6 +261,11 @@ def gc_conv_bwd(x, w, dy, y_mask, dx, dw, relu, stride, workspace, stream=None):
     """dx and dw together (dy masked by y_mask > 0 when relu) via gc_conv_bwd."""
     dt = _dtype_code(x)
     desc = desc_from(x.shape, w.shape, stride)
+    ys = _y_shape(desc)
+    _expect(dy, "dy", ys)
+    _expect(y_mask, "y_mask", ys)
+    _expect(dx, "dx", x.shape)
+    _expect(dw, "dw", w.shape)
     wp, wn = _ws(workspace)
     st = lib().gc_conv_bwd(_dev(x, "x", dt), _dev(w, "w", dt), _dev(dy, "dy", dt),
                            _dev(y_mask, "y_mask", dt), _dev(dx, "dx", dt), _dev(dw, "dw", dt),

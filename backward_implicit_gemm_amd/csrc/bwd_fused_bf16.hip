@@ -39,9 +39,9 @@ __global__ void __launch_bounds__(kDzNT) bwd_prep_bf16(const u16 *__restrict__ d
 }
 
 // d_input workgroups first (n_dg of them, an (image group, channel group)
-// grid of nx_dg columns, padded to a multiple of 8), then the wgrad
+// grid of nx_dg columns, padded to a multiple of the XCD count), then the wgrad
 // workgroups; the padding keeps each wgrad workgroup on the XCD its own
-// decode expects (workgroup ids go round-robin over the 8 XCDs).
+// decode expects (workgroup ids go round-robin over the XCDs).
 template <int NW, int MB, int KS, int TAPS, int NBW, int GP, int NSTEP>
 __global__ void __launch_bounds__(64 * NW) bwd_fused_bf16(DgradBfArgs da, WgradBfArgs wa, int n_dg,
                                                           int nx_dg, int n_dg_pad)
@@ -100,7 +100,7 @@ bool plan_bwd_fused_bf16(const Geom &g, BwdFusedBfPlan &p)
     const size_t lds = std::max(q.d.lds, q.w.lds);
     const int per_cu = lds ? int((160 * 1024) / lds) : 8;
     const int n_dg = (g.B + q.d.G - 1) / q.d.G * q.d.cgroups;
-    q.fuse_main = n_dg <= 256 * std::max(per_cu, 1);
+    q.fuse_main = n_dg <= g.ncu * std::max(per_cu, 1);
     p = q;
     return true;
 }
@@ -133,6 +133,9 @@ hipError_t launch_bwd_fused_bf16(const Geom &g, const BwdFusedBfPlan &p, const v
     const int npack = std::min((total + 255) / 256, 2048);
     const size_t dz_lds = size_t(2) * 8 * g.OC * g.P * sizeof(u16);
     hipError_t e = allow_max_lds(reinterpret_cast<const void *>(&bwd_prep_bf16));
+    if (e == hipSuccess) e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
+    if (e == hipSuccess) e = allow_max_lds(reinterpret_cast<const void *>(v->fn_d));
+    if (e == hipSuccess) e = allow_max_lds(reinterpret_cast<const void *>(v->fn_w));
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_prep_bf16, dim3(wp.ngroups + npack), dim3(kDzNT), dz_lds, s,
                        (const u16 *)dy, (const u16 *)ym, dzg, g, relu, wp.PP, wp.ngroups,
@@ -146,20 +149,14 @@ hipError_t launch_bwd_fused_bf16(const Geom &g, const BwdFusedBfPlan &p, const v
     WgradBfArgs wa{g, (const u16 *)x, dzg, part, wp};
     const int nx_dg = (g.B + d.G - 1) / d.G;
     const int n_dg = nx_dg * d.cgroups;
-    const int n_wg = 8 * ((wp.splits + 7) / 8) * wp.ncol;
+    const int n_wg = g.nxcd * ((wp.splits + g.nxcd - 1) / g.nxcd) * wp.ncol;
     if (p.fuse_main) {
-        const int n_dg_pad = (n_dg + 7) / 8 * 8;
-        e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
-        if (e != hipSuccess) return e;
+        const int n_dg_pad = (n_dg + g.nxcd - 1) / g.nxcd * g.nxcd;
         hipLaunchKernelGGL(v->fn, dim3(n_dg_pad + n_wg), dim3(kWgNT), std::max(d.lds, wp.lds), s, da,
                            wa, n_dg, nx_dg, n_dg_pad);
     } else {
-        e = allow_max_lds(reinterpret_cast<const void *>(v->fn_d));
-        if (e != hipSuccess) return e;
         hipLaunchKernelGGL(v->fn_d, dim3(nx_dg, d.cgroups), dim3(64 * d.NW), d.lds, s, da);
         e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        e = allow_max_lds(reinterpret_cast<const void *>(v->fn_w));
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(v->fn_w, dim3(n_wg), dim3(2 * kWgNT), wp.lds, s, wa);
     }

@@ -113,7 +113,7 @@ bool plan_dgrad_ig_bf16(const Geom &g, DgradBfPlan &p)
             const int nchunks = (g.IC + CC - 1) / CC;
             const int occ = lds <= 80 * 1024 ? 2 : 1;
             int cgroups = 1;
-            while (ngroups * cgroups < 256 * occ && cgroups < nchunks) ++cgroups;
+            while (ngroups * cgroups < g.ncu * occ && cgroups < nchunks) ++cgroups;
             const int cpg = (nchunks + cgroups - 1) / cgroups;
             cgroups = (nchunks + cpg - 1) / cpg;
             // cycles per chunk on one CU
@@ -122,7 +122,7 @@ bool plan_dgrad_ig_bf16(const Geom &g, DgradBfPlan &p)
             const double gather = passes * NW * (mt * 8.0 + 16.0);
             const double chunk = mfma + gather + 400.0;
             const double per_wg = cpg * chunk + 2500.0;
-            const double waves_of_wgs = std::ceil(double(ngroups) * cgroups / (256.0 * occ));
+            const double waves_of_wgs = std::ceil(double(ngroups) * cgroups / (double(g.ncu) * occ));
             const double t = waves_of_wgs * per_wg * (occ == 2 ? 1.4 : 1.0);
             if (t < best - 1e-9) {
                 if (!pick_dgrad_bf(NW, MB, KS, TAPS, NBW, GP)) continue;
@@ -148,14 +148,14 @@ hipError_t launch_dgrad_ig_bf16(const Geom &g, const DgradBfPlan &p, const void 
         return hipErrorInvalidValue;
     const int total = p.nchunks * p.NBC * p.KS * 64;
     if (size_t(total) * 16 > p.ws_bytes) return hipErrorInvalidValue;
+    hipError_t e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(pack_w_dgrad_bf16, dim3(std::min((total + 255) / 256, 2048)), dim3(256), 0, s,
                        (const u16 *)w, (uint4 *)ws, g, p.CC, p.NBC, p.KS, total);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     DgradBfArgs a{g, (const u16 *)dy, (const u16 *)ym, (const uint4 *)ws, (u16 *)dx, relu, p,
                   make_fastdiv(g.OC * g.P)};
-    e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
-    if (e != hipSuccess) return e;
     dim3 grid((g.B + p.G - 1) / p.G, p.cgroups);
     hipLaunchKernelGGL(v->fn, grid, dim3(64 * p.NW), p.lds, s, a);
     return hipGetLastError();

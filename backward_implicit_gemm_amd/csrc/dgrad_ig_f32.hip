@@ -304,7 +304,7 @@ bool plan_dgrad_ig_f32(const Geom &g, DgradIgPlan &p)
             q.TH = TH; q.TW = TW;
             q.nchunks = (g.IC + CC - 1) / CC;
             q.cgroups = 1;
-            while (ngroups * q.cgroups < 256 && q.cgroups * 2 <= q.nchunks) q.cgroups *= 2;
+            while (ngroups * q.cgroups < g.ncu && q.cgroups * 2 <= q.nchunks) q.cgroups *= 2;
             q.cpg = (q.nchunks + q.cgroups - 1) / q.cgroups;
             q.cgroups = (q.nchunks + q.cpg - 1) / q.cpg;
             q.WV = (OCS * ((q.NCH + 3) / 4) + 64 * NW - 1) / (64 * NW);

@@ -403,7 +403,7 @@ bool plan_dgrad_rf_f32(const Geom &g, DgradBfPlan &p)
             if (lds > 160 * 1024) break;
             const int nchunks = (g.IC + CC - 1) / CC;
             int cgroups = 1;
-            while (ngroups * cgroups < 256 && cgroups < nchunks) ++cgroups;
+            while (ngroups * cgroups < g.ncu && cgroups < nchunks) ++cgroups;
             const int cpg = (nchunks + cgroups - 1) / cgroups;
             cgroups = (nchunks + cpg - 1) / cpg;
             const double mfma = 2.0 * MB * 4 * KS4 * 32;
@@ -411,7 +411,7 @@ bool plan_dgrad_rf_f32(const Geom &g, DgradBfPlan &p)
             const double gather = passes * 4 * (mt * 16.0 + 40.0) + 600.0;
             const double chunk = std::max(mfma, gather) + 300.0;
             const double per_wg = cpg * chunk + 2500.0;
-            const double t = std::ceil(double(ngroups) * cgroups / 256.0) * per_wg;
+            const double t = std::ceil(double(ngroups) * cgroups / double(g.ncu)) * per_wg;
             if (t < best - 1e-9) {
                 if (!pick_dgrad_rf(NW, MB, KS4, TAPS, NBW, g.OC == 16 * KS4)) continue;
                 best = t;

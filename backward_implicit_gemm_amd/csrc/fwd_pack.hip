@@ -1,0 +1,153 @@
+// fwd_pack.hip -- pieces shared by the two forward kernels (fwd_ws_bf16.hip,
+// fwd_ws_f32.hip): the per-call weight packing into MFMA B-fragment order and
+// the LDS pitch choice of the channels-innermost x tile.
+//
+// Both forwards order the reduction index (channel group, tap, channel in the
+// group), so that a lane's MFMA operand is a run of consecutive channels at one
+// tap: 8 channels (16 bytes) for v_mfma_f32_16x16x32_bf16, 4 channels (16
+// bytes) for v_mfma_f32_16x16x4_f32.  OIHW weights hold a tap's channels KH*KW
+// elements apart, so a small pass per call gathers them into fragment order,
+// padding channels and taps with zeros; each wave then streams its fragments
+// as contiguous 1 KB reads.
+#include "gc_kernels.h"
+#include "ig_common.h"
+
+namespace gc {
+namespace {
+
+typedef unsigned short u16;
+
+// Packed weight layout, 16-byte units: ((nb*NCG + cg)*TS + s)*64 + lane,
+// lane = (n%16) + 16*q, holding w[n][8*cg + i][4*s + q] for i = 0..7 (zero
+// past OC, IC or KH*KW).
+__global__ void __launch_bounds__(256) pack_w_fwd_bf16(const u16 *__restrict__ w,
+                                                       uint4 *__restrict__ wf, Geom g, int NCG,
+                                                       int TS, int total)
+{
+    for (int u = blockIdx.x * 256 + threadIdx.x; u < total; u += gridDim.x * 256) {
+        const int lane = u & 63;
+        int rest = u >> 6;
+        const int s = rest % TS;
+        rest /= TS;
+        const int cg = rest % NCG;
+        const int nb = rest / NCG;
+        const int n = nb * 16 + (lane & 15);
+        const int t = 4 * s + (lane >> 4);
+        u16 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int ic = 8 * cg + i;
+            v[i] = (n < g.OC && ic < g.IC && t < g.KK) ? w[(size_t(n) * g.IC + ic) * g.KK + t] : u16(0);
+        }
+        uint4 o;
+        o.x = v[0] | (uint32_t(v[1]) << 16);
+        o.y = v[2] | (uint32_t(v[3]) << 16);
+        o.z = v[4] | (uint32_t(v[5]) << 16);
+        o.w = v[6] | (uint32_t(v[7]) << 16);
+        wf[u] = o;
+    }
+}
+
+// Packed weights, 16-byte units ((nb*NCG + cg)*TS + s)*64 + lane holding
+// w[16*nb + lane%16][4*cg + j][4*s + lane/16] for j = 0..3 (zero past OC, IC
+// or KH*KW).
+__global__ void __launch_bounds__(256) pack_w_fwd_f32(const float *__restrict__ w,
+                                                      float4 *__restrict__ wf, Geom g, int NCG,
+                                                      int TS, int total)
+{
+    for (int u = blockIdx.x * 256 + threadIdx.x; u < total; u += gridDim.x * 256) {
+        const int lane = u & 63;
+        int rest = u >> 6;
+        const int s = rest % TS;
+        rest /= TS;
+        const int cg = rest % NCG;
+        const int nb = rest / NCG;
+        const int n = nb * 16 + (lane & 15);
+        const int t = 4 * s + (lane >> 4);
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int ic = 4 * cg + j;
+            v[j] = (n < g.OC && ic < g.IC && t < g.KK) ? w[(size_t(n) * g.IC + ic) * g.KK + t] : 0.f;
+        }
+        wf[u] = make_float4(v[0], v[1], v[2], v[3]);
+    }
+}
+
+}  // namespace
+
+// LDS pitch of the channels-innermost x tile.  A 16-lane group of an A
+// fragment read fetches the 16-byte pixel slots of 16 output rows at one
+// tap; the LDS serves it in one pass only if the 16 slots fall in distinct
+// 16-byte bank groups (slot mod 16).  Pad the row pitch WP and the image
+// stride IS (each by less than 16 slots) to minimise the worst-case
+// multiplicity summed over every row block and tap.
+static void search_lds_pitch(const Geom &g, int G, int MB, int TS, int &WP_out, int &IS_out)
+{
+    int best = 1 << 30;
+    WP_out = g.W;
+    IS_out = g.H * g.W;
+    const int rows = G * g.P;
+    for (int WP = g.W; WP < g.W + 16; ++WP)
+        for (int IS = g.H * WP; IS < g.H * WP + 16; ++IS) {
+            int cost = 0;
+            for (int mb = 0; mb < MB; ++mb)
+                for (int t = 0; t < std::min(4 * TS, g.KK); ++t) {
+                    int cnt[16] = {0}, worst = 0;
+                    for (int l = 0; l < 16; ++l) {
+                        const int r = mb * 16 + l;
+                        int slot = 0;
+                        if (r < rows) {
+                            const int img = r / g.P, pp = r % g.P;
+                            slot = img * IS + (pp / g.OW) * g.S * WP + (pp % g.OW) * g.S;
+                        }
+                        slot += (t / g.KW) * WP + t % g.KW;
+                        worst = std::max(worst, ++cnt[slot & 15]);
+                    }
+                    cost += worst;
+                }
+            // fewer conflicts first, then the smaller tile
+            if (cost < best) {
+                best = cost;
+                WP_out = WP;
+                IS_out = IS;
+            }
+        }
+}
+
+// The search does not depend on the batch size beyond the rows G*P the
+// images fill, so it runs once per layer shape and G.
+void pick_lds_pitch(const Geom &g, int G, int MB, int TS, int &WP_out, int &IS_out)
+{
+    static SearchMemo<std::pair<int, int>> memo;
+    const int key[12] = {g.IC, g.H, g.W, g.OC, g.KH, g.KW, g.S, G, MB, TS, 0, 0};
+    const std::pair<int, int> r = memo.get(key, [&] {
+        int wp = 0, is = 0;
+        search_lds_pitch(g, G, MB, TS, wp, is);
+        return std::make_pair(wp, is);
+    });
+    WP_out = r.first;
+    IS_out = r.second;
+}
+
+hipError_t launch_pack_w_fwd_bf16(const Geom &g, int NCG, int TS, int nblocks, const void *w,
+                                  void *wf, size_t ws_bytes, hipStream_t s)
+{
+    const int total = nblocks * NCG * TS * 64;
+    if (size_t(total) * 16 > ws_bytes) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pack_w_fwd_bf16, dim3(std::min((total + 255) / 256, 1024)), dim3(256), 0, s,
+                       (const u16 *)w, (uint4 *)wf, g, NCG, TS, total);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_w_fwd_f32(const Geom &g, int NCG, int TS, int nblocks, const void *w,
+                                 void *wf, size_t ws_bytes, hipStream_t s)
+{
+    const int total = nblocks * NCG * TS * 64;
+    if (size_t(total) * 16 > ws_bytes) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pack_w_fwd_f32, dim3(std::min((total + 255) / 256, 1024)), dim3(256), 0, s,
+                       (const float *)w, (float4 *)wf, g, NCG, TS, total);
+    return hipGetLastError();
+}
+
+}  // namespace gc

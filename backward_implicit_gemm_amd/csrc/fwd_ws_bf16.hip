@@ -1,14 +1,20 @@
 // fwd_ws_bf16.hip -- forward convolution, bf16 storage, fp32 accumulation,
 // with loader waves and MFMA waves.
 //
-// Same contraction and operand layout as fwd_ig_bf16.hip: y = x * w as an
-// implicit GEMM on v_mfma_f32_16x16x32_bf16, the reduction ordered (channel
-// group of 8, tap, channel) so that both operands are single 16-byte reads;
-// x staged channels-innermost [group][image][pixel][8] through 8x8 register
-// transposes; weights pre-packed into fragment order and streamed from L2
-// through register rings.
+// y = x * w as an implicit GEMM y[m][n] = sum_k A[m][k] * w[n][k], m =
+// (b,oh,ow), n = oc, on v_mfma_f32_16x16x32_bf16, whose operands carry 8
+// consecutive reduction elements per lane.  The reduction index is ordered
+// (channel group of 8, tap, channel) so that both operands are single
+// 16-byte reads: a workgroup owns G whole images, each channel group of them
+// staged in LDS channels-innermost [group][image][pixel][8], so the A
+// fragment of output row (b,oh,ow) and tap (kh,kw) is the 16 bytes at pixel
+// (oh*S+kh, ow*S+kw) (the transposition from NCHW happens in registers, 8
+// pixels x 8 channels per loader thread); the weights are packed per call into
+// fragment order (fwd_pack.hip) and streamed from L2 through register rings.
+// Channels are padded to a multiple of 8 and taps to a multiple of 4 with
+// zero weights.
 //
-// What differs is who waits for what.  A wave's vector-memory counter is in
+// Roles.  A wave's vector-memory counter is in
 // order: when one wave issues both the x staging loads (from HBM) and the
 // weight-ring loads (from L2), every ring wait after an x load also waits for
 // that x load, and the MFMAs stall on HBM latency.  Here the two never share
@@ -39,9 +45,6 @@
 #include "ig_common.h"
 
 namespace gc {
-
-void pick_lds_pitch(const Geom &g, int G, int MB, int TS, int &WP_out, int &IS_out);
-
 namespace {
 
 typedef unsigned short u16;
@@ -292,10 +295,14 @@ struct FwdWsVariant {
 };
 #define WS_V(NBW, MB, TS, NCG, CPP, D) {NBW, MB, TS, NCG, CPP, fwd_ws_bf16<NBW, MB, TS, NCG, CPP, D>}
 const FwdWsVariant kFwdWsVariants[] = {
-    WS_V(2, 3, 7, 8, 3, 7),    // 59 -> 128, 11x15, 5x5, stride 3: 4 images, 48 rows
-    WS_V(2, 1, 7, 8, 8, 7),    // the same layer, one image per workgroup
-    WS_V(1, 1, 3, 16, 16, 16),  // 128 -> 128, 3x4, 3x3: 8 images, 16 rows
-    WS_V(1, 4, 3, 16, 4, 16),   // the same layer at large batch: 32 images
+    // 59 -> 128, 11x15, 5x5, stride 3 (12 rows per image)
+    WS_V(2, 3, 7, 8, 3, 7),     // 4 images, 128 channels per workgroup
+    WS_V(1, 3, 7, 8, 3, 14),    // 4 images, 64 channels (two column tiles)
+    WS_V(2, 1, 7, 8, 8, 7),     // one image
+    // 128 -> 128, 3x4, 3x3 (2 rows per image), 64 channels per workgroup
+    WS_V(1, 1, 3, 16, 16, 16),  // up to 8 images
+    WS_V(1, 2, 3, 16, 8, 16),   // 16 images
+    WS_V(1, 4, 3, 16, 4, 16),   // 32 images
 };
 #undef WS_V
 
@@ -308,10 +315,14 @@ const FwdWsVariant *pick_fwd_ws(int NBW, int MB, int TS, int NCG, int CPP)
 
 }  // namespace
 
-// G as in fwd_ig_bf16 (the most images that still give 256 workgroups, four
-// for 12-row images); NBW 2 where 64 rows or fewer fill the M blocks, else 1
-// with twice the column tiles; CPP the channel groups the 256 loader threads
-// stage per phase.
+// Enumerates the tilings that have an instantiation -- NBW 16-channel blocks
+// per MFMA wave (2: 128 channels per workgroup, 1: 64 channels and twice the
+// column tiles), G images per workgroup, MB = ceil(G*P/16) row blocks, CPP
+// channel groups per staging phase for the 256 loader threads -- and keeps
+// the one that (1) puts the most workgroups on the chip at once, up to one
+// per CU, then (2) wastes the fewest MFMA rows, then (3) has the wider NBW
+// (each A read feeds more MFMAs), then (4) the larger G (fewer passes of the
+// weight stream per image).
 bool plan_fwd_ws_bf16(const Geom &g, FwdWsPlan &p)
 {
     if (g.P > 64 || g.KK > 36 || g.HW < 8) return false;
@@ -319,52 +330,64 @@ bool plan_fwd_ws_bf16(const Geom &g, FwdWsPlan &p)
     const int TS = (g.KK + 3) / 4;
     const int NCG = (g.IC + 7) / 8;
     const int nblk = (g.HW + 7) / 8;
-    double best_fill = -1.0;
+    bool found = false;
+    int best_wgs = 0, best_nbw = 0, best_g = 0;
+    double best_fill = 0.0;
     for (int NBW : {2, 1}) {
-        FwdWsPlan q{};
-        q.NBW = NBW; q.TS = TS; q.NCG = NCG; q.nblk = nblk;
-        q.ntile = (g.OC + 64 * NBW - 1) / (64 * NBW);
-        int G = std::max(1, 64 / g.P);
-        while (G > 1 && ((g.B + G - 1) / G) * q.ntile < 256) --G;
-        if (g.P == 12 && G > 4) G = 4;
-        if (G > g.B) G = g.B;
-        q.G = G;
-        q.MB = (G * g.P + 15) / 16;
-        const int units_per_cg = G * nblk;
-        if (units_per_cg > kLoaders) continue;
-        q.CPP = std::min(NCG, kLoaders / units_per_cg);
-        if (!pick_fwd_ws(NBW, q.MB, TS, NCG, q.CPP)) continue;
-        pick_lds_pitch(g, G, q.MB, TS, q.WP, q.IS);
-        q.lds = sizeof(uint4) * size_t(NCG) * G * q.IS;
-        // output staging: one region per MFMA wave, G images x NBW*16 channels x P
-        q.ystage = g.OC % (64 * NBW) == 0 && (g.P * NBW * 16) % 8 == 0;
-        if (q.ystage) q.lds += size_t(kMfmaWaves) * G * NBW * 16 * g.P * 2;
-        if (q.lds > 150 * 1024) continue;
-        q.ws_bytes = size_t(q.ntile) * kMfmaWaves * NBW * NCG * TS * 64 * 16;
-        const double fill = double(G * g.P) / (16.0 * q.MB);
-        if (fill > best_fill) {
-            best_fill = fill;
+        const int ntile = (g.OC + 64 * NBW - 1) / (64 * NBW);
+        for (int G = std::min(g.B, std::max(1, 64 / g.P)); G >= 1; --G) {
+            FwdWsPlan q{};
+            q.NBW = NBW; q.TS = TS; q.NCG = NCG; q.nblk = nblk; q.ntile = ntile; q.G = G;
+            q.MB = (G * g.P + 15) / 16;
+            const int units_per_cg = G * nblk;
+            if (units_per_cg > kLoaders) continue;
+            // as many channel groups per phase as the loaders can stage, or
+            // fewer where only that has an instantiation
+            q.CPP = std::min(NCG, kLoaders / units_per_cg);
+            while (q.CPP >= 1 && !pick_fwd_ws(NBW, q.MB, TS, NCG, q.CPP)) --q.CPP;
+            if (q.CPP < 1) continue;
+            const long long groups = (g.B + G - 1) / G;
+            const int wgs = int(std::min<long long>(groups * ntile, g.ncu));
+            const double fill = double(G * g.P) / (16.0 * q.MB);
+            const bool better =
+                !found || wgs > best_wgs ||
+                (wgs == best_wgs && (fill > best_fill + 1e-9 ||
+                                     (fill > best_fill - 1e-9 &&
+                                      (NBW > best_nbw || (NBW == best_nbw && G > best_g)))));
+            if (!better) continue;
+            pick_lds_pitch(g, G, q.MB, TS, q.WP, q.IS);
+            q.lds = sizeof(uint4) * size_t(NCG) * G * q.IS;
+            // output staging: one region per MFMA wave, G images x NBW*16
+            // channels x P; used when y is 16-byte aligned (checked per call)
+            q.ystage = g.OC % (64 * NBW) == 0 && (g.P * NBW * 16) % 8 == 0;
+            if (q.ystage) q.lds += size_t(kMfmaWaves) * G * NBW * 16 * g.P * 2;
+            if (q.lds > 150 * 1024) continue;
+            q.ws_bytes = size_t(ntile) * kMfmaWaves * NBW * NCG * TS * 64 * 16;
             p = q;
+            found = true;
+            best_wgs = wgs; best_fill = fill; best_nbw = NBW; best_g = G;
         }
     }
-    return best_fill >= 0.0;
+    return found;
 }
 
 hipError_t launch_fwd_ws_bf16(const Geom &g, const FwdWsPlan &p, const void *x, const void *w,
                               const void *bias, void *y, void *ws, int relu, hipStream_t s)
 {
+    // every precondition is checked before the first launch
     const FwdWsVariant *v = pick_fwd_ws(p.NBW, p.MB, p.TS, p.NCG, p.CPP);
     if (!v || p.G * p.nblk * p.CPP > kLoaders || g.HW < 8 || p.G * g.P > 16 * p.MB)
         return hipErrorInvalidValue;
-    hipError_t e = launch_pack_w_fwd_bf16(g, p.NCG, p.TS, p.ntile * kMfmaWaves * p.NBW, w, ws,
-                                          p.ws_bytes, s);
+    if (p.ystage && g.OC % (64 * p.NBW)) return hipErrorInvalidValue;
+    // 16-byte output stores need a 16-byte-aligned y (every run starts at a
+    // multiple of 8 elements from it); any other y takes the 2-byte stores
+    const int ystage = p.ystage && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
+    hipError_t e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
     if (e != hipSuccess) return e;
-    if (p.ystage && (g.OC % (64 * p.NBW) || (reinterpret_cast<uintptr_t>(y) & 15)))
-        return hipErrorInvalidValue;
+    e = launch_pack_w_fwd_bf16(g, p.NCG, p.TS, p.ntile * kMfmaWaves * p.NBW, w, ws, p.ws_bytes, s);
+    if (e != hipSuccess) return e;
     FwdWsArgs a{g, (const u16 *)x, (const uint4 *)ws, (const u16 *)bias, (u16 *)y, relu,
-                p.G, p.WP, p.IS, p.nblk, p.ystage, p.NCG * p.G * p.IS};
-    e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
-    if (e != hipSuccess) return e;
+                p.G, p.WP, p.IS, p.nblk, ystage, p.NCG * p.G * p.IS};
     // one workgroup per CU (the x tile takes most of its LDS): at most one
     // round of workgroups, each walking its share of the image groups.  The
     // next group's phase ph overwrites this group's phase ph only two
@@ -372,7 +395,7 @@ hipError_t launch_fwd_ws_bf16(const Geom &g, const FwdWsPlan &p, const void *x, 
     // workgroup takes a single group.
     const int ngroups = (g.B + p.G - 1) / p.G;
     const int nph = (p.NCG + p.CPP - 1) / p.CPP;
-    const int gx = nph >= 2 ? std::min(ngroups, std::max(1, 256 / p.ntile)) : ngroups;
+    const int gx = nph >= 2 ? std::min(ngroups, std::max(1, g.ncu / p.ntile)) : ngroups;
     hipLaunchKernelGGL(v->fn, dim3(gx, p.ntile), dim3(kThreads), p.lds, s, a);
     return hipGetLastError();
 }

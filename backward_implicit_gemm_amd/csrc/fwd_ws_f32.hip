@@ -1,8 +1,7 @@
 // fwd_ws_f32.hip -- forward convolution, fp32 storage, fp32 MFMA
 // (v_mfma_f32_16x16x4_f32), with loader waves and MFMA waves.
 //
-// Same contraction and operand layout as fwd_rf_f32.hip: the reduction in
-// blocks of 16 k = 4 channels x 4 taps, so a lane's four MFMA steps read four
+// The reduction runs in blocks of 16 k = 4 channels x 4 taps, so a lane's four MFMA steps read four
 // consecutive channels at one tap: x staged channels-innermost
 // [group][image][pixel][4] through 4x4 register transposes, weights
 // pre-packed into float4 fragments and streamed from L2 through a register
@@ -23,9 +22,6 @@
 #include "ig_common.h"
 
 namespace gc {
-
-void pick_lds_pitch(const Geom &g, int G, int MB, int TS, int &WP_out, int &IS_out);
-
 namespace {
 
 struct FwdWsF32Args {
@@ -215,10 +211,16 @@ struct FwdWsF32Variant {
 #define WF_V(NWM, MB, TS, NCG, CPP, GS) \
     {NWM, MB, TS, NCG, CPP, GS, fwd_ws_f32<NWM, MB, TS, NCG, CPP, 8, GS>}
 const FwdWsF32Variant kFwdWsF32Variants[] = {
-    WF_V(8, 3, 7, 15, 3, 960),    // 59 -> 128, 11x15, 5x5, stride 3: 4 images, 48 rows
-    WF_V(8, 1, 7, 15, 12, 240),   // the same layer, one image per workgroup
-    WF_V(4, 1, 3, 32, 10, 128),   // 128 -> 128, 3x4, 3x3: 8 images, 16 rows
-    WF_V(4, 1, 3, 32, 32, 16),    // the same layer, one image per workgroup
+    // 59 -> 128, 11x15, 5x5, stride 3 (12 rows per image), 128 channels per workgroup
+    WF_V(8, 3, 7, 15, 3, 960),    // 3 or 4 images, 36 or 48 rows
+    WF_V(8, 2, 7, 15, 6, 480),    // 2 images
+    WF_V(8, 1, 7, 15, 12, 240),   // one image
+    // 128 -> 128, 3x4, 3x3 (2 rows per image), 64 channels per workgroup
+    WF_V(4, 4, 3, 32, 2, 512),    // 32 images
+    WF_V(4, 2, 3, 32, 5, 256),    // 16 images
+    WF_V(4, 1, 3, 32, 10, 128),   // 8 images
+    WF_V(4, 1, 3, 32, 21, 64),    // 4 images
+    WF_V(4, 1, 3, 32, 32, 32),    // one or two images
 };
 #undef WF_V
 
@@ -232,40 +234,53 @@ const FwdWsF32Variant *pick_fwd_ws_f32(int NWM, int MB, int TS, int NCG, int CPP
 
 }  // namespace
 
-// G as in fwd_rf_f32 (the most images that still give 256 workgroups, four
-// for 12-row images); 8 MFMA waves (128 channels per workgroup) for
-// layer-1-like shapes, 4 (64 channels, twice the column tiles) where an image
-// has 4 rows or fewer; CPP the channel groups the loader threads stage per
+// NWM = 8 MFMA waves (128 channels per workgroup) for layer-1-like shapes, 4
+// (64 channels, twice the column tiles) where an image has 4 rows or fewer;
+// then, over the G (images per workgroup) that have an instantiation, the one
+// that (1) puts the most workgroups on the chip at once, up to one per CU,
+// (2) wastes the fewest MFMA rows, (3) is larger (fewer passes of the weight
+// stream per image).  CPP: the channel groups the loader threads stage per
 // phase.
 bool plan_fwd_ws_f32(const Geom &g, FwdWsPlan &p)
 {
     if (g.P > 64 || g.KK > 36 || g.HW < 4) return false;
     if (size_t(g.B) * g.IC * g.HW * 4 >= (size_t(1) << 31)) return false;
-    FwdWsPlan q{};
-    q.NWM = g.P <= 4 ? 4 : 8;
-    q.NBW = 1;
-    q.TS = (g.KK + 3) / 4;
-    q.NCG = (g.IC + 3) / 4;
-    q.nblk = (g.HW + 3) / 4;
-    q.ntile = (g.OC + 16 * q.NWM - 1) / (16 * q.NWM);
-    int G = std::max(1, 64 / g.P);
-    while (G > 1 && ((g.B + G - 1) / G) * q.ntile < 256) --G;
-    if (g.P == 12 && G > 4) G = 4;
-    if (G > g.B) G = g.B;
-    q.G = G;
-    q.MB = (G * g.P + 15) / 16;
-    const int loaders = 64 * q.NWM;
-    const int units_per_cg = G * q.nblk;
-    if (units_per_cg > loaders) return false;
-    q.CPP = std::min(q.NCG, loaders / units_per_cg);
-    pick_lds_pitch(g, G, q.MB, q.TS, q.WP, q.IS);
-    const FwdWsF32Variant *v = pick_fwd_ws_f32(q.NWM, q.MB, q.TS, q.NCG, q.CPP, G * q.IS);
-    if (!v) return false;
-    q.lds = sizeof(float4) * 2 * size_t(q.CPP) * v->GS;
-    if (q.lds > 150 * 1024) return false;
-    q.ws_bytes = size_t(q.ntile) * q.NWM * q.NCG * q.TS * 64 * 16;
-    p = q;
-    return true;
+    const int NWM = g.P <= 4 ? 4 : 8;
+    const int TS = (g.KK + 3) / 4, NCG = (g.IC + 3) / 4, nblk = (g.HW + 3) / 4;
+    const int ntile = (g.OC + 16 * NWM - 1) / (16 * NWM);
+    const int loaders = 64 * NWM;
+    bool found = false;
+    int best_wgs = 0, best_g = 0;
+    double best_fill = 0.0;
+    for (int G = std::min(g.B, std::max(1, 64 / g.P)); G >= 1; --G) {
+        FwdWsPlan q{};
+        q.NWM = NWM; q.NBW = 1; q.TS = TS; q.NCG = NCG; q.nblk = nblk; q.ntile = ntile; q.G = G;
+        q.MB = (G * g.P + 15) / 16;
+        const int units_per_cg = G * nblk;
+        if (units_per_cg > loaders) continue;
+        const long long groups = (g.B + G - 1) / G;
+        const int wgs = int(std::min<long long>(groups * ntile, g.ncu));
+        const double fill = double(G * g.P) / (16.0 * q.MB);
+        const bool better = !found || wgs > best_wgs ||
+                            (wgs == best_wgs && (fill > best_fill + 1e-9 ||
+                                                 (fill > best_fill - 1e-9 && G > best_g)));
+        if (!better) continue;
+        pick_lds_pitch(g, G, q.MB, TS, q.WP, q.IS);
+        // as many channel groups per phase as the loaders can stage, or
+        // fewer where only that has an instantiation
+        const FwdWsF32Variant *v = nullptr;
+        for (q.CPP = std::min(NCG, loaders / units_per_cg); q.CPP >= 1 && !v; --q.CPP)
+            v = pick_fwd_ws_f32(NWM, q.MB, TS, NCG, q.CPP, G * q.IS);
+        ++q.CPP;
+        if (!v) continue;
+        q.lds = sizeof(float4) * 2 * size_t(q.CPP) * v->GS;
+        if (q.lds > 150 * 1024) continue;
+        q.ws_bytes = size_t(ntile) * NWM * NCG * TS * 64 * 16;
+        p = q;
+        found = true;
+        best_wgs = wgs; best_fill = fill; best_g = G;
+    }
+    return found;
 }
 
 hipError_t launch_fwd_ws_f32(const Geom &g, const FwdWsPlan &p, const void *x, const void *w,
@@ -275,12 +290,12 @@ hipError_t launch_fwd_ws_f32(const Geom &g, const FwdWsPlan &p, const void *x, c
     if (!v || p.G * p.nblk * p.CPP > 64 * p.NWM || g.HW < 4 || p.G * g.P > 16 * p.MB ||
         p.lds < sizeof(float4) * 2 * size_t(p.CPP) * v->GS)
         return hipErrorInvalidValue;
-    hipError_t e = launch_pack_w_fwd_f32(g, p.NCG, p.TS, p.ntile * p.NWM, w, ws, p.ws_bytes, s);
+    hipError_t e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
+    if (e != hipSuccess) return e;
+    e = launch_pack_w_fwd_f32(g, p.NCG, p.TS, p.ntile * p.NWM, w, ws, p.ws_bytes, s);
     if (e != hipSuccess) return e;
     FwdWsF32Args a{g, (const float *)x, (const float4 *)ws, (const float *)bias, (float *)y, relu,
                    p.G, p.WP, p.IS, p.nblk};
-    e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
-    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(v->fn, dim3((g.B + p.G - 1) / p.G, p.ntile), dim3(128 * p.NWM), p.lds, s, a);
     return hipGetLastError();
 }

@@ -3,6 +3,8 @@
 // validation happens before the first HIP call, so the error paths are
 // testable on a machine without a GPU.
 #include <limits.h>
+#include <stdarg.h>
+#include <stdio.h>
 
 #include <atomic>
 #include <mutex>
@@ -20,6 +22,40 @@ constexpr int kVersion = 100;  // 0.1.0
 
 bool valid_dtype(int dtype) { return dtype == GC_F32 || dtype == GC_BF16; }
 
+// Compute units and XCDs of the current device, queried once per device.
+// Without a usable device (a host-only process asking for workspace sizes or
+// plan names) the MI355X values are used: 256 CUs in 8 XCDs.
+void set_device(Geom &g)
+{
+    constexpr int kMaxDev = 64;
+    static std::mutex m;
+    static int known[kMaxDev][2];
+    static bool have[kMaxDev];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
+        (void)hipGetLastError();   // leave no error behind for the next call
+        g.ncu = 256;
+        g.nxcd = 8;
+        return;
+    }
+    std::lock_guard<std::mutex> lk(m);
+    if (!have[dev]) {
+        int ncu = 0, nxcd = 0;
+        if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            ncu < 1)
+            ncu = 256;
+        if (hipDeviceGetAttribute(&nxcd, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess ||
+            nxcd < 1 || ncu % nxcd)
+            nxcd = 1;
+        (void)hipGetLastError();
+        known[dev][0] = ncu;
+        known[dev][1] = nxcd;
+        have[dev] = true;
+    }
+    g.ncu = known[dev][0];
+    g.nxcd = known[dev][1];
+}
+
 // Checks the descriptor and fills the geometry.  OH = (H-KH)/S + 1 and
 // OW = (W-KW)/S + 1 with integer division (no padding; the floor drops the
 // input rows/columns no window reaches).
@@ -36,7 +72,10 @@ int check_desc(const gc_conv_desc *d, Geom *g)
     const long long ny = (long long)d->B * d->OC * OH * OW;
     const long long nw = (long long)d->OC * d->IC * d->KH * d->KW;
     if (nx > INT_MAX || ny > INT_MAX || nw > INT_MAX) return GC_ERR_INVALID_ARG;
-    if (g) *g = make_geom(d->B, d->IC, d->H, d->W, d->OC, d->KH, d->KW, d->stride);
+    if (g) {
+        *g = make_geom(d->B, d->IC, d->H, d->W, d->OC, d->KH, d->KW, d->stride);
+        set_device(*g);
+    }
     return GC_OK;
 }
 
@@ -52,16 +91,16 @@ std::atomic<int> g_policy{GC_POLICY_AUTO};
 
 bool use_ig() { return g_policy.load(std::memory_order_relaxed) == GC_POLICY_AUTO; }
 
-// Plans depend only on the geometry, and some take a search (the bf16
-// forward's LDS pitch) that costs far more host time than a launch, so each
-// planner's answers are kept per geometry, one table per planner (two
-// planners may share a plan type).  Thread-safe; a full table overwrites its
-// entries round-robin.
+// Plans depend only on the geometry and the device's CU and XCD counts, and
+// some take a search (the forward's LDS pitch) that costs far more host time
+// than a launch, so each planner's answers are kept per (geometry, device
+// shape), one table per planner (two planners may share a plan type).
+// Thread-safe; a full table overwrites its entries round-robin.
 template <typename P, bool (*Planner)(const Geom &, P &)>
 bool cached_plan(const Geom &g, P &out)
 {
     struct Entry {
-        int key[8];
+        int key[10];
         bool ok;
         P plan;
     };
@@ -69,11 +108,11 @@ bool cached_plan(const Geom &g, P &out)
     static std::mutex m;
     static Entry table[kSlots];
     static int used = 0, next = 0;
-    const int key[8] = {g.B, g.IC, g.H, g.W, g.OC, g.KH, g.KW, g.S};
+    const int key[10] = {g.B, g.IC, g.H, g.W, g.OC, g.KH, g.KW, g.S, g.ncu, g.nxcd};
     {
         std::lock_guard<std::mutex> lk(m);
         for (int i = 0; i < used; ++i)
-            if (std::equal(key, key + 8, table[i].key)) {
+            if (std::equal(key, key + 10, table[i].key)) {
                 if (table[i].ok) out = table[i].plan;
                 return table[i].ok;
             }
@@ -82,21 +121,13 @@ bool cached_plan(const Geom &g, P &out)
     const bool ok = Planner(g, p);
     std::lock_guard<std::mutex> lk(m);
     Entry &e = table[used < kSlots ? used++ : (next++ % kSlots)];
-    std::copy(key, key + 8, e.key);
+    std::copy(key, key + 10, e.key);
     e.ok = ok;
     e.plan = p;
     if (ok) out = p;
     return ok;
 }
 
-bool fwd_f32_plan(const Geom &g, FwdIgPlan &p)
-{
-    return use_ig() && cached_plan<std::remove_reference_t<decltype(p)>, plan_fwd_ig_f32>(g, p);
-}
-bool fwd_f32_rf_plan(const Geom &g, FwdBfPlan &p)
-{
-    return use_ig() && cached_plan<FwdBfPlan, plan_fwd_rf_f32>(g, p);
-}
 bool fwd_f32_ws_plan(const Geom &g, FwdWsPlan &p)
 {
     return use_ig() && cached_plan<FwdWsPlan, plan_fwd_ws_f32>(g, p);
@@ -104,10 +135,6 @@ bool fwd_f32_ws_plan(const Geom &g, FwdWsPlan &p)
 bool fwd_bf16_ws_plan(const Geom &g, FwdWsPlan &p)
 {
     return use_ig() && cached_plan<FwdWsPlan, plan_fwd_ws_bf16>(g, p);
-}
-bool fwd_bf16_plan(const Geom &g, FwdBfPlan &p)
-{
-    return use_ig() && cached_plan<std::remove_reference_t<decltype(p)>, plan_fwd_ig_bf16>(g, p);
 }
 bool dgrad_bf16_plan(const Geom &g, DgradBfPlan &p)
 {
@@ -139,29 +166,133 @@ bool wgrad_plan(const Geom &g, WgradIgPlan &p)
     return use_ig() && cached_plan<std::remove_reference_t<decltype(p)>, plan_wgrad_ig_f32>(g, p);
 }
 
-// Number of fp32 partial tiles wgrad writes for this problem, and the plan
-// of the image-group kernel when it runs.
-int wgrad_splits(const Geom &g, int dtype, WgradIgPlan *ig, bool *use)
+// ---------------------------------------------------------------------------
+// Kernel selection.  Each entry point asks select_* which kernel family runs
+// a problem, in a fixed order of preference, and gc_conv_plan_name() reports
+// the same choice, so tests can pin which kernel every tested shape runs.
+// ---------------------------------------------------------------------------
+enum class FwdKind { WsF32, WsBf16, Generic };
+struct FwdSel {
+    FwdKind k;
+    FwdWsPlan ws;
+};
+FwdSel select_fwd(const Geom &g, int dtype)
 {
-    WgradIgPlan p;
-    if (wgrad_plan(g, p)) {
-        if (ig) *ig = p;
-        if (use) *use = true;
-        return p.splits;
+    FwdSel s{};
+    if (dtype == GC_F32)
+        s.k = fwd_f32_ws_plan(g, s.ws) ? FwdKind::WsF32 : FwdKind::Generic;
+    else
+        s.k = fwd_bf16_ws_plan(g, s.ws) ? FwdKind::WsBf16 : FwdKind::Generic;
+    return s;
+}
+
+enum class DgradKind { IgBf16, RfF32, IgF32Mfma, Generic };
+struct DgradSel {
+    DgradKind k;
+    DgradBfPlan bf;
+    DgradIgPlan ig;
+};
+DgradSel select_dgrad(const Geom &g, int dtype)
+{
+    DgradSel s{};
+    if (dtype == GC_BF16 && dgrad_bf16_plan(g, s.bf)) s.k = DgradKind::IgBf16;
+    else if (dtype == GC_F32 && dgrad_f32_rf_plan(g, s.bf)) s.k = DgradKind::RfF32;
+    else if (dgrad_plan(g, s.ig)) s.k = DgradKind::IgF32Mfma;
+    else s.k = DgradKind::Generic;
+    return s;
+}
+
+enum class WgradKind { IgBf16, RfF32, IgF32Mfma, Generic };
+struct WgradSel {
+    WgradKind k;
+    WgradBfPlan bf;
+    WgradRfPlan rf;
+    WgradIgPlan ig;
+    int splits;   // partial tiles of the IgF32Mfma and Generic kinds
+};
+WgradSel select_wgrad(const Geom &g, int dtype)
+{
+    WgradSel s{};
+    if (dtype == GC_BF16 && wgrad_bf16_plan(g, s.bf)) s.k = WgradKind::IgBf16;
+    else if (dtype == GC_F32 && wgrad_f32_rf_plan(g, s.rf)) s.k = WgradKind::RfF32;
+    else if (wgrad_plan(g, s.ig)) {
+        s.k = WgradKind::IgF32Mfma;
+        s.splits = s.ig.splits;
+    } else {
+        s.k = WgradKind::Generic;
+        s.splits = wgrad_generic_splits(g);
     }
-    if (use) *use = false;
-    return wgrad_generic_splits(g);
+    return s;
 }
 
-size_t wgrad_ws_bytes(const Geom &g, int dtype)
+// Appends printf-style text to buf (bounded by n, always NUL-terminated).
+void append(char *buf, size_t n, size_t &at, const char *fmt, ...)
+    __attribute__((format(printf, 4, 5)));
+void append(char *buf, size_t n, size_t &at, const char *fmt, ...)
 {
-    WgradBfPlan bp;
-    if (dtype == GC_BF16 && wgrad_bf16_plan(g, bp)) return bp.ws_bytes;
-    WgradRfPlan rp;
-    if (dtype == GC_F32 && wgrad_f32_rf_plan(g, rp)) return rp.ws_bytes;
-    return size_t(wgrad_splits(g, dtype, nullptr, nullptr)) * g.OC * g.K * sizeof(float);
+    if (at >= n) return;
+    va_list ap;
+    va_start(ap, fmt);
+    const int k = vsnprintf(buf + at, n - at, fmt, ap);
+    va_end(ap);
+    if (k > 0) at = std::min(n - 1, at + size_t(k));
 }
 
+// Names: the kernel family and its compile-time instance in <>, then the
+// launch parameters of the plan.
+void name_fwd(const FwdSel &s, char *buf, size_t n, size_t &at)
+{
+    switch (s.k) {
+    case FwdKind::WsF32:
+        append(buf, n, at, "fwd_ws_f32<NWM=%d,MB=%d,TS=%d,NCG=%d,CPP=%d> G=%d ntile=%d", s.ws.NWM,
+               s.ws.MB, s.ws.TS, s.ws.NCG, s.ws.CPP, s.ws.G, s.ws.ntile);
+        break;
+    case FwdKind::WsBf16:
+        append(buf, n, at, "fwd_ws_bf16<NBW=%d,MB=%d,TS=%d,NCG=%d,CPP=%d> G=%d ntile=%d", s.ws.NBW,
+               s.ws.MB, s.ws.TS, s.ws.NCG, s.ws.CPP, s.ws.G, s.ws.ntile);
+        break;
+    case FwdKind::Generic: append(buf, n, at, "igemm_generic_fwd"); break;
+    }
+}
+
+void name_dgrad_bf(const DgradBfPlan &p, char *buf, size_t n, size_t &at)
+{
+    append(buf, n, at, "dgrad_ig_bf16<MB=%d,KS=%d,TAPS=%d,NBW=%d> G=%d CC=%d", p.MB, p.KS, p.TAPS,
+           p.NBW, p.G, p.CC);
+}
+
+void name_dgrad(const DgradSel &s, char *buf, size_t n, size_t &at)
+{
+    switch (s.k) {
+    case DgradKind::IgBf16: name_dgrad_bf(s.bf, buf, n, at); break;
+    case DgradKind::RfF32:
+        append(buf, n, at, "dgrad_rf_f32<MB=%d,KS4=%d,TAPS=%d> G=%d CC=%d", s.bf.MB, s.bf.KS,
+               s.bf.TAPS, s.bf.G, s.bf.CC);
+        break;
+    case DgradKind::IgF32Mfma:
+        append(buf, n, at, "dgrad_ig_f32<MB=%d> G=%d CC=%d", s.ig.MB, s.ig.G, s.ig.CC);
+        break;
+    case DgradKind::Generic: append(buf, n, at, "igemm_generic_dgrad"); break;
+    }
+}
+
+void name_wgrad(const WgradSel &s, char *buf, size_t n, size_t &at)
+{
+    switch (s.k) {
+    case WgradKind::IgBf16:
+        append(buf, n, at, "wgrad_ws_bf16<NSTEP=%d> ncol=%d splits=%d", s.bf.NSTEP, s.bf.ncol,
+               s.bf.splits);
+        break;
+    case WgradKind::RfF32:
+        append(buf, n, at, "wgrad_rf_f32<NBWV=%d> chunks=%d splits=%d", s.rf.NBWV, s.rf.chunks,
+               s.rf.splits);
+        break;
+    case WgradKind::IgF32Mfma:
+        append(buf, n, at, "wgrad_ig_f32<MBW=%d> G=%d splits=%d", s.ig.MBW, s.ig.G, s.splits);
+        break;
+    case WgradKind::Generic: append(buf, n, at, "igemm_generic_wgrad splits=%d", s.splits); break;
+    }
+}
 }  // namespace
 
 extern "C" {
@@ -196,21 +327,19 @@ size_t gc_conv_workspace_bytes(int op, const gc_conv_desc *d, int dtype)
     if (check_desc(d, &g) != GC_OK || !valid_dtype(dtype)) return 0;
     switch (op) {
     case GC_OP_FWD: {
-        FwdWsPlan wp;
-        if (dtype == GC_BF16 && fwd_bf16_ws_plan(g, wp)) return wp.ws_bytes;
-        if (dtype == GC_F32 && fwd_f32_ws_plan(g, wp)) return wp.ws_bytes;
-        FwdBfPlan p;
-        if (dtype == GC_BF16 && fwd_bf16_plan(g, p)) return p.ws_bytes;
-        if (dtype == GC_F32 && fwd_f32_rf_plan(g, p)) return p.ws_bytes;
-        return 0;
+        const FwdSel s = select_fwd(g, dtype);
+        return s.k == FwdKind::Generic ? 0 : s.ws.ws_bytes;
     }
     case GC_OP_BWD_DATA: {
-        DgradBfPlan p;
-        if (dtype == GC_BF16 && dgrad_bf16_plan(g, p)) return p.ws_bytes;
-        if (dtype == GC_F32 && dgrad_f32_rf_plan(g, p)) return p.ws_bytes;
-        return 0;
+        const DgradSel s = select_dgrad(g, dtype);
+        return s.k == DgradKind::IgBf16 ? s.bf.ws_bytes : 0;
     }
-    case GC_OP_BWD_WEIGHT: return wgrad_ws_bytes(g, dtype);
+    case GC_OP_BWD_WEIGHT: {
+        const WgradSel s = select_wgrad(g, dtype);
+        if (s.k == WgradKind::IgBf16) return s.bf.ws_bytes;
+        if (s.k == WgradKind::RfF32) return s.rf.ws_bytes;
+        return size_t(s.splits) * g.OC * g.K * sizeof(float);
+    }
     case GC_OP_BWD_BIAS: return bias_grad_ws_bytes(g);
     case GC_OP_BWD: {
         BwdFusedBfPlan p;
@@ -235,37 +364,20 @@ static int conv_fwd(const void *x, const void *w, const void *bias, void *y, voi
         (bias && !aligned(bias, dtype)))
         return GC_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (dtype == GC_F32) {
-        FwdWsPlan wp;
-        if (fwd_f32_ws_plan(g, wp)) {
-            if (!workspace || ws_bytes < wp.ws_bytes) return GC_ERR_WORKSPACE;
-            if (reinterpret_cast<uintptr_t>(workspace) % 16) return GC_ERR_WORKSPACE;
-            return hip_status(launch_fwd_ws_f32(g, wp, x, w, bias, y, workspace, relu, s));
-        }
-        FwdBfPlan rp;
-        if (fwd_f32_rf_plan(g, rp)) {
-            if (!workspace || ws_bytes < rp.ws_bytes) return GC_ERR_WORKSPACE;
-            if (reinterpret_cast<uintptr_t>(workspace) % 16) return GC_ERR_WORKSPACE;
-            return hip_status(launch_fwd_rf_f32(g, rp, x, w, bias, y, workspace, relu, s));
-        }
-        FwdIgPlan p;
-        if (fwd_f32_plan(g, p))
-            return hip_status(launch_fwd_ig_f32(g, p, x, w, bias, y, relu, s));
-        return hip_status(launch_fwd_generic<float>(g, x, w, bias, y, relu, s));
-    }
-    FwdWsPlan wp;
-    if (fwd_bf16_ws_plan(g, wp)) {
-        if (!workspace || ws_bytes < wp.ws_bytes) return GC_ERR_WORKSPACE;
+    const FwdSel sel = select_fwd(g, dtype);
+    if (sel.k != FwdKind::Generic) {
+        if (!workspace || ws_bytes < sel.ws.ws_bytes) return GC_ERR_WORKSPACE;
         if (reinterpret_cast<uintptr_t>(workspace) % 16) return GC_ERR_WORKSPACE;
-        return hip_status(launch_fwd_ws_bf16(g, wp, x, w, bias, y, workspace, relu, s));
     }
-    FwdBfPlan p;
-    if (fwd_bf16_plan(g, p)) {
-        if (!workspace || ws_bytes < p.ws_bytes) return GC_ERR_WORKSPACE;
-        if (reinterpret_cast<uintptr_t>(workspace) % 16) return GC_ERR_WORKSPACE;
-        return hip_status(launch_fwd_ig_bf16(g, p, x, w, bias, y, workspace, relu, s));
+    switch (sel.k) {
+    case FwdKind::WsF32:
+        return hip_status(launch_fwd_ws_f32(g, sel.ws, x, w, bias, y, workspace, relu, s));
+    case FwdKind::WsBf16:
+        return hip_status(launch_fwd_ws_bf16(g, sel.ws, x, w, bias, y, workspace, relu, s));
+    case FwdKind::Generic: break;
     }
-    return hip_status(launch_fwd_generic<bf16_t>(g, x, w, bias, y, relu, s));
+    return hip_status(dtype == GC_F32 ? launch_fwd_generic<float>(g, x, w, bias, y, relu, s)
+                                      : launch_fwd_generic<bf16_t>(g, x, w, bias, y, relu, s));
 }
 
 int gc_conv_fwd(const void *x, const void *w, void *y, void *workspace, size_t ws_bytes,
@@ -314,24 +426,23 @@ int gc_conv_bwd_data(const void *dy, const void *w, const void *y_mask, void *dx
         (y_mask && !aligned(y_mask, dtype)))
         return GC_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    {
-        DgradBfPlan bp;
-        const bool bf = dtype == GC_BF16 && dgrad_bf16_plan(g, bp);
-        const bool rf = !bf && dtype == GC_F32 && dgrad_f32_rf_plan(g, bp);
-        if (bf) {
-            if (!workspace || ws_bytes < bp.ws_bytes) return GC_ERR_WORKSPACE;
-            if (reinterpret_cast<uintptr_t>(workspace) % 16) return GC_ERR_WORKSPACE;
-            return hip_status(launch_dgrad_ig_bf16(g, bp, dy, w, y_mask, dx, workspace, relu, s));
-        }
-        if (rf) return hip_status(launch_dgrad_rf_f32(g, bp, dy, w, y_mask, dx, relu, s));
+    const DgradSel sel = select_dgrad(g, dtype);
+    switch (sel.k) {
+    case DgradKind::IgBf16:
+        if (!workspace || ws_bytes < sel.bf.ws_bytes) return GC_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(workspace) % 16) return GC_ERR_WORKSPACE;
+        return hip_status(launch_dgrad_ig_bf16(g, sel.bf, dy, w, y_mask, dx, workspace, relu, s));
+    case DgradKind::RfF32:
+        return hip_status(launch_dgrad_rf_f32(g, sel.bf, dy, w, y_mask, dx, relu, s));
+    case DgradKind::IgF32Mfma:
+        return hip_status(dtype == GC_F32
+                              ? launch_dgrad_ig<float>(g, sel.ig, dy, w, y_mask, dx, relu, s)
+                              : launch_dgrad_ig<bf16_t>(g, sel.ig, dy, w, y_mask, dx, relu, s));
+    case DgradKind::Generic: break;
     }
-    DgradIgPlan p;
-    const bool ig = dgrad_plan(g, p);
-    if (dtype == GC_F32)
-        return hip_status(ig ? launch_dgrad_ig<float>(g, p, dy, w, y_mask, dx, relu, s)
-                             : launch_dgrad_generic<float>(g, dy, w, y_mask, dx, relu, s));
-    return hip_status(ig ? launch_dgrad_ig<bf16_t>(g, p, dy, w, y_mask, dx, relu, s)
-                         : launch_dgrad_generic<bf16_t>(g, dy, w, y_mask, dx, relu, s));
+    return hip_status(dtype == GC_F32
+                          ? launch_dgrad_generic<float>(g, dy, w, y_mask, dx, relu, s)
+                          : launch_dgrad_generic<bf16_t>(g, dy, w, y_mask, dx, relu, s));
 }
 
 int gc_conv_bwd_weight(const void *x, const void *dy, const void *y_mask, void *dw,
@@ -348,41 +459,31 @@ int gc_conv_bwd_weight(const void *x, const void *dy, const void *y_mask, void *
         (y_mask && !aligned(y_mask, dtype)))
         return GC_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (dtype == GC_BF16) {
-        WgradBfPlan bp;
-        if (wgrad_bf16_plan(g, bp)) {
-            if (!workspace || ws_bytes < bp.ws_bytes) return GC_ERR_WORKSPACE;
-            if (reinterpret_cast<uintptr_t>(workspace) % 256) return GC_ERR_WORKSPACE;
-            return hip_status(launch_wgrad_ig_bf16(g, bp, x, dy, y_mask, dw, workspace, relu, s));
-        }
+    const WgradSel sel = select_wgrad(g, dtype);
+    if (sel.k == WgradKind::IgBf16) {
+        if (!workspace || ws_bytes < sel.bf.ws_bytes) return GC_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(workspace) % 256) return GC_ERR_WORKSPACE;
+        return hip_status(launch_wgrad_ig_bf16(g, sel.bf, x, dy, y_mask, dw, workspace, relu, s));
     }
-    if (dtype == GC_F32) {
-        WgradRfPlan rp;
-        if (wgrad_f32_rf_plan(g, rp)) {
-            if (!workspace || ws_bytes < rp.ws_bytes) return GC_ERR_WORKSPACE;
-            if (reinterpret_cast<uintptr_t>(workspace) % 16) return GC_ERR_WORKSPACE;
-            return hip_status(launch_wgrad_rf_f32(g, rp, x, dy, y_mask, dw, workspace, relu, s));
-        }
+    if (sel.k == WgradKind::RfF32) {
+        if (!workspace || ws_bytes < sel.rf.ws_bytes) return GC_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(workspace) % 16) return GC_ERR_WORKSPACE;
+        return hip_status(launch_wgrad_rf_f32(g, sel.rf, x, dy, y_mask, dw, workspace, relu, s));
     }
-    WgradIgPlan ig;
-    bool use_ig_path = false;
-    const int splits = wgrad_splits(g, dtype, &ig, &use_ig_path);
+    const int splits = sel.splits;
     const size_t need = size_t(splits) * g.OC * g.K * sizeof(float);
     if (need && (!workspace || ws_bytes < need)) return GC_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % 16) return GC_ERR_WORKSPACE;
     float *part = static_cast<float *>(workspace);
+    const bool ig = sel.k == WgradKind::IgF32Mfma;
     hipError_t e;
     if (dtype == GC_F32) {
-        if (use_ig_path)
-            e = launch_wgrad_ig<float>(g, ig, x, dy, y_mask, part, relu, s);
-        else
-            e = launch_wgrad_generic<float>(g, x, dy, y_mask, part, splits, relu, s);
+        e = ig ? launch_wgrad_ig<float>(g, sel.ig, x, dy, y_mask, part, relu, s)
+               : launch_wgrad_generic<float>(g, x, dy, y_mask, part, splits, relu, s);
         if (e == hipSuccess) e = launch_wgrad_reduce<float>(part, dw, splits, g.OC * g.K, s);
     } else {
-        if (use_ig_path)
-            e = launch_wgrad_ig<bf16_t>(g, ig, x, dy, y_mask, part, relu, s);
-        else
-            e = launch_wgrad_generic<bf16_t>(g, x, dy, y_mask, part, splits, relu, s);
+        e = ig ? launch_wgrad_ig<bf16_t>(g, sel.ig, x, dy, y_mask, part, relu, s)
+               : launch_wgrad_generic<bf16_t>(g, x, dy, y_mask, part, splits, relu, s);
         if (e == hipSuccess) e = launch_wgrad_reduce<bf16_t>(part, dw, splits, g.OC * g.K, s);
     }
     return hip_status(e);
@@ -418,6 +519,41 @@ int gc_conv_bwd(const void *x, const void *w, const void *dy, const void *y_mask
     if (st != GC_OK) return st;
     void *wsw = ww ? static_cast<char *>(workspace) + off : nullptr;
     return gc_conv_bwd_weight(x, dy, y_mask, dw, wsw, ww, d, relu, dtype, stream);
+}
+
+int gc_conv_plan_name(int op, const gc_conv_desc *d, int dtype, char *buf, size_t buf_bytes)
+{
+    Geom g;
+    const int st = check_desc(d, &g);
+    if (st != GC_OK) return st;
+    if (!valid_dtype(dtype) || !buf || buf_bytes == 0) return GC_ERR_INVALID_ARG;
+    size_t at = 0;
+    buf[0] = '\0';
+    switch (op) {
+    case GC_OP_FWD: name_fwd(select_fwd(g, dtype), buf, buf_bytes, at); break;
+    case GC_OP_BWD_DATA: name_dgrad(select_dgrad(g, dtype), buf, buf_bytes, at); break;
+    case GC_OP_BWD_WEIGHT: name_wgrad(select_wgrad(g, dtype), buf, buf_bytes, at); break;
+    case GC_OP_BWD_BIAS: append(buf, buf_bytes, at, "bias_partials+bias_final"); break;
+    case GC_OP_BWD: {
+        BwdFusedBfPlan fp;
+        if (dtype == GC_BF16 && bwd_fused_plan(g, fp)) {
+            append(buf, buf_bytes, at, "bwd_fused_bf16 fuse_main=%d: ", fp.fuse_main);
+            name_dgrad_bf(fp.d, buf, buf_bytes, at);
+            append(buf, buf_bytes, at, " + ");
+            WgradSel w{};
+            w.k = WgradKind::IgBf16;
+            w.bf = fp.w;
+            name_wgrad(w, buf, buf_bytes, at);
+        } else {
+            name_dgrad(select_dgrad(g, dtype), buf, buf_bytes, at);
+            append(buf, buf_bytes, at, " + ");
+            name_wgrad(select_wgrad(g, dtype), buf, buf_bytes, at);
+        }
+        break;
+    }
+    default: return GC_ERR_INVALID_ARG;
+    }
+    return GC_OK;
 }
 
 int gc_set_kernel_policy(int policy)

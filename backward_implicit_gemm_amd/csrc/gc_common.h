@@ -67,6 +67,11 @@ struct Geom {
     int HW;   // H*W, pixels per channel plane
     int K;    // IC*KK, reduction length of the forward GEMM
     FastDiv fd_P, fd_OW, fd_KK, fd_KW, fd_HW, fd_W, fd_S, fd_OC;
+    // the device the call runs on: compute units, and the XCDs (each with its
+    // own L2) that workgroup ids are dealt to round-robin.  Plans size their
+    // grids from these; kernels use nxcd only to place related workgroups on
+    // one XCD, never for coverage.
+    int ncu, nxcd;
 };
 
 inline Geom make_geom(int B, int IC, int H, int W, int OC, int KH, int KW, int S)
@@ -87,6 +92,8 @@ inline Geom make_geom(int B, int IC, int H, int W, int OC, int KH, int KW, int S
     g.fd_W = make_fastdiv(W);
     g.fd_S = make_fastdiv(S);
     g.fd_OC = make_fastdiv(OC);
+    g.ncu = 256;     // MI355X; the C ABI layer sets the current device's values
+    g.nxcd = 8;
     return g;
 }
 

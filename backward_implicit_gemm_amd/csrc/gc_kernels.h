@@ -17,18 +17,15 @@ hipError_t launch_wgrad_generic(const Geom &g, const void *x, const void *dy, co
                                 float *part, int splits, int relu, hipStream_t s);
 int wgrad_generic_splits(const Geom &g);
 
-// Image-group kernels, fp32 storage (fwd_ig_f32.hip, dgrad_ig_f32.hip,
-// wgrad_ig_f32.hip).  plan_* returns false when a shape does not fit them.
-struct FwdIgPlan;
+// Image-group kernels on fp32 MFMA for shapes the kernels below do not plan
+// (dgrad_ig_f32.hip, wgrad_ig_f32.hip).  plan_* returns false when a shape
+// does not fit them.
 struct DgradIgPlan;
 struct WgradIgPlan;
 struct DgradBfPlan;
 struct WgradBfPlan;
 struct WgradRfPlan;
 struct BwdFusedBfPlan;
-bool plan_fwd_ig_f32(const Geom &g, FwdIgPlan &p);
-hipError_t launch_fwd_ig_f32(const Geom &g, const FwdIgPlan &p, const void *x, const void *w,
-                             const void *bias, void *y, int relu, hipStream_t s);
 // d_input and wgrad run on fp32 MFMA for both storage types (T = float or
 // bf16_t; bf16 is widened exactly while staging).
 bool plan_dgrad_ig_f32(const Geom &g, DgradIgPlan &p);
@@ -40,12 +37,10 @@ template <typename T>
 hipError_t launch_wgrad_ig(const Geom &g, const WgradIgPlan &p, const void *x, const void *dy,
                            const void *ym, float *part, int relu, hipStream_t s);
 
-// Image-group kernels, bf16 storage.
-struct FwdBfPlan;
+// Forward kernels with loader and MFMA waves.
 struct FwdWsPlan;
-bool plan_fwd_ig_bf16(const Geom &g, FwdBfPlan &p);
 // packs w into the B-fragment order of the bf16 forward for `nblocks`
-// 16-channel blocks (shared by fwd_ig_bf16 and fwd_ws_bf16)
+// 16-channel blocks (fwd_pack.hip)
 hipError_t launch_pack_w_fwd_bf16(const Geom &g, int NCG, int TS, int nblocks, const void *w,
                                   void *wf, size_t ws_bytes, hipStream_t s);
 // bf16 forward with loader and MFMA waves; plan_* returns false when a shape
@@ -53,27 +48,22 @@ hipError_t launch_pack_w_fwd_bf16(const Geom &g, int NCG, int TS, int nblocks, c
 bool plan_fwd_ws_bf16(const Geom &g, FwdWsPlan &p);
 hipError_t launch_fwd_ws_bf16(const Geom &g, const FwdWsPlan &p, const void *x, const void *w,
                               const void *bias, void *y, void *ws, int relu, hipStream_t s);
-hipError_t launch_fwd_ig_bf16(const Geom &g, const FwdBfPlan &p, const void *x, const void *w,
-                              const void *bias, void *y, void *ws, int relu, hipStream_t s);
 // Bias gradient db[oc] = sum over (b, oh, ow) of dz (bias_grad.hip): fp32
 // partials per image chunk in `part`, then the fixed-order reduction.
 size_t bias_grad_ws_bytes(const Geom &g);
 template <typename T>
 hipError_t launch_bias_grad(const Geom &g, const void *dy, const void *ym, void *db, float *part,
                             int relu, hipStream_t s);
-// fp32 forward with channels-innermost staging and packed weight fragments
-// (fwd_rf_f32.hip); the plan struct is shared with the bf16 forward.
-bool plan_fwd_rf_f32(const Geom &g, FwdBfPlan &p);
 // packs w into the B-fragment order of the fp32 forward for `nblocks`
-// 16-channel blocks (shared by fwd_rf_f32 and fwd_ws_f32)
+// 16-channel blocks (fwd_pack.hip)
 hipError_t launch_pack_w_fwd_f32(const Geom &g, int NCG, int TS, int nblocks, const void *w,
                                  void *wf, size_t ws_bytes, hipStream_t s);
 // fp32 forward with loader and MFMA waves
 bool plan_fwd_ws_f32(const Geom &g, FwdWsPlan &p);
 hipError_t launch_fwd_ws_f32(const Geom &g, const FwdWsPlan &p, const void *x, const void *w,
                              const void *bias, void *y, void *ws, int relu, hipStream_t s);
-hipError_t launch_fwd_rf_f32(const Geom &g, const FwdBfPlan &p, const void *x, const void *w,
-                             const void *bias, void *y, void *ws, int relu, hipStream_t s);
+// LDS pitch of the forwards' channels-innermost x tile (fwd_pack.hip)
+void pick_lds_pitch(const Geom &g, int G, int MB, int TS, int &WP_out, int &IS_out);
 bool plan_dgrad_ig_bf16(const Geom &g, DgradBfPlan &p);
 // fp32 d_input on fp32 MFMA, weights read in place (dgrad_rf_f32.hip); the
 // plan struct is shared with the bf16 kernel, KS holding the 16-channel

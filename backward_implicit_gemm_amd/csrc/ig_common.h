@@ -34,6 +34,38 @@ inline hipError_t allow_max_lds(const void *fn)
     return e;
 }
 
+// A small thread-safe memo for planner searches whose answer does not depend
+// on the batch size (LDS pitch choices), keyed by up to 12 ints.  A full
+// table overwrites its entries round-robin.
+template <typename V, int N = 64>
+class SearchMemo {
+  public:
+    template <typename F>
+    V get(const int (&key)[12], F compute)
+    {
+        {
+            std::lock_guard<std::mutex> lk(m_);
+            for (int i = 0; i < used_; ++i)
+                if (std::equal(key, key + 12, e_[i].key)) return e_[i].v;
+        }
+        const V v = compute();
+        std::lock_guard<std::mutex> lk(m_);
+        Entry &e = e_[used_ < N ? used_++ : (next_++ % N)];
+        std::copy(key, key + 12, e.key);
+        e.v = v;
+        return v;
+    }
+
+  private:
+    struct Entry {
+        int key[12];
+        V v;
+    };
+    std::mutex m_;
+    Entry e_[N];
+    int used_ = 0, next_ = 0;
+};
+
 // Four consecutive elements as fp32 from an element-aligned global address:
 // one 16-byte load for fp32 storage, one 8-byte load widened exactly for
 // bf16 storage.
@@ -124,35 +156,6 @@ constexpr uint32_t kOffNone = 0xFFFFFFF0u;   // an offset past the end of every 
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ---------------------------------------------------------------- forward --
-struct FwdIgPlan {
-    int NW;       // waves per workgroup (they split the output channels)
-    int G;        // images per workgroup
-    int MB;       // 16-row M blocks (G*P <= 16*MB)
-    int NB;       // 16-column N blocks per wave (tile width NW*16*NB)
-    int CC;       // input channels per chunk
-    int KCH;      // CC*KK, multiple of 4 (one fp32 MFMA step)
-    int KS;       // MFMA k steps per chunk (4*KS >= KCH; slots past KCH read zeros)
-    int KCHP;     // LDS row stride of the weight chunk
-    int XCS;      // LDS floats per image in the x chunk (CC*HW rounded up to 4)
-    int nchunks;  // ceil(IC/CC)
-    int XV, WV;   // float4 staging loads per thread (x, w)
-    size_t lds;   // dynamic LDS bytes
-};
-
-// -------------------------------------------------------- forward, bf16 ----
-struct FwdBfPlan {
-    int NW;       // waves per workgroup, 16 output channels each
-    int G;        // images per workgroup
-    int MB;       // 16-row M blocks
-    int TS;       // tap steps: ceil(KH*KW/4)
-    int WP;       // LDS pixel slots per image row (>= W, padded against bank conflicts)
-    int IS;       // LDS pixel slots per image (>= H*WP)
-    int nblk;     // 8-pixel blocks per image
-    int NCG;      // channel groups of 8
-    size_t lds;
-    size_t ws_bytes;   // packed weights
-};
-
 // Forward with loader and MFMA waves (fwd_ws_bf16.hip, fwd_ws_f32.hip).
 struct FwdWsPlan {
     int NWM;      // MFMA waves (as many loader waves; fp32 only, bf16 uses 4)

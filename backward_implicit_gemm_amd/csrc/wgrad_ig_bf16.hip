@@ -71,8 +71,8 @@ bool plan_wgrad_ig_bf16(const Geom &g, WgradBfPlan &p)
     // splits: enough workgroups to cover the CUs, in multiples of 8 so the
     // XCDs get equal shares, few enough that the partial traffic stays small
     // against the operand traffic
-    int splits = std::max(1, std::min(ngroups, (256 + ncol - 1) / ncol));
-    if (splits > 8) splits = splits / 8 * 8;
+    int splits = std::max(1, std::min(ngroups, (g.ncu + ncol - 1) / ncol));
+    if (splits > g.nxcd) splits = splits / g.nxcd * g.nxcd;
     const double part_bytes = double(g.OC) * N * 4;
     const double in_bytes = double(g.B) * g.IC * g.HW * 2;
     const double budget = std::max(0.75 * in_bytes, 12.0 * 1024 * 1024);
@@ -101,15 +101,15 @@ hipError_t launch_wgrad_ig_bf16(const Geom &g, const WgradBfPlan &p, const void 
     if (g.OC * g.P * 8 > kDzChunks * kDzNT * 8) return hipErrorInvalidValue;
     e = allow_max_lds(reinterpret_cast<const void *>(&dz_groups_bf16));
     if (e != hipSuccess) return e;
+    e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(dz_groups_bf16, dim3(p.ngroups), dim3(kDzNT), dz_lds, s,
                        (const u16 *)dy, (const u16 *)ym, dzg, g, relu, p.PP);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
-    if (e != hipSuccess) return e;
     WgradBfArgs a{g, (const u16 *)x, dzg, part, p};
-    const int slots = (p.splits + 7) / 8 * p.ncol;    // per XCD
-    hipLaunchKernelGGL(v->fn, dim3(8 * slots), dim3(2 * kWgNT), p.lds, s, a);
+    const int slots = (p.splits + g.nxcd - 1) / g.nxcd * p.ncol;    // per XCD
+    hipLaunchKernelGGL(v->fn, dim3(g.nxcd * slots), dim3(2 * kWgNT), p.lds, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_wgrad_reduce<bf16_t>(part, dw, p.splits, g.OC * g.K, s);

@@ -130,11 +130,11 @@ __device__ __forceinline__ void wgrad_ig_bf16_body(const WgradBfArgs &a, int bid
     const int wm = wave & 1;          // output channels 64*wm .. +63
     const int wn = wave >> 1;         // columns 32*wn .. +31 of the tile
     const int N = g.K;                // IC*KH*KW columns
-    // Workgroups are dealt to the 8 XCDs round-robin by id; ids are laid out
-    // so that all column tiles of one split (one image range) share an XCD,
+    // Workgroups are dealt to the XCDs round-robin by id; ids are laid out so
+    // that all column tiles of one split (one image range) share an XCD,
     // whose L2 then serves that range's dz and x to every tile.
-    const int xcd = bid & 7, slot = bid >> 3;
-    const int split = (slot / p.ncol) * 8 + xcd;
+    const int xcd = bid % g.nxcd, slot = bid / g.nxcd;
+    const int split = (slot / p.ncol) * g.nxcd + xcd;
     if (split >= p.splits) return;
     const int n0 = (slot % p.ncol) * 128;
     const int c_lo = n0 / g.KK;
@@ -315,11 +315,11 @@ __device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid
     const int wm = wave & 1;          // output channels 64*wm .. +63
     const int wn = wave >> 1;         // columns 32*wn .. +31 of the tile
     const int N = g.K;                // IC*KH*KW columns
-    // Workgroups are dealt to the 8 XCDs round-robin by id; ids are laid out
-    // so that all column tiles of one split (one image range) share an XCD,
+    // Workgroups are dealt to the XCDs round-robin by id; ids are laid out so
+    // that all column tiles of one split (one image range) share an XCD,
     // whose L2 then serves that range's dz and x to every tile.
-    const int xcd = bid & 7, slot = bid >> 3;
-    const int split = (slot / p.ncol) * 8 + xcd;
+    const int xcd = bid % g.nxcd, slot = bid / g.nxcd;
+    const int split = (slot / p.ncol) * g.nxcd + xcd;
     if (split >= p.splits) return;
     const int n0 = (slot % p.ncol) * 128;
     const int c_lo = n0 / g.KK;

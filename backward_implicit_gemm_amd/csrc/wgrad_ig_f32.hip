@@ -44,11 +44,11 @@ __global__ void __launch_bounds__(64 * NW) wgrad_ig_f32(WgradIgArgs<T> a)
     const int wm = wave & 3, wn = wave >> 2;   // oc group, k group of this wave
     constexpr int OCR = MBW * 64;   // oc rows covered by the four oc groups
 
-    // Workgroups are dealt to the 8 XCDs round-robin by id; ids are laid out
-    // so that all column tiles of one split share an XCD and its L2, which
-    // then serves that split's images of x and dy to every tile.
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int split = (slot / p.nkt) * 8 + xcd;
+    // Workgroups are dealt to the XCDs round-robin by id; ids are laid out so
+    // that all column tiles of one split share an XCD and its L2, which then
+    // serves that split's images of x and dy to every tile.
+    const int xcd = int(blockIdx.x) % g.nxcd, slot = int(blockIdx.x) / g.nxcd;
+    const int split = (slot / p.nkt) * g.nxcd + xcd;
     if (split >= p.splits) return;
     const int k0 = (slot % p.nkt) * p.BNK;
     const int bs = split * p.GS;
@@ -265,8 +265,8 @@ bool plan_wgrad_ig_f32(const Geom &g, WgradIgPlan &p)
             q.NW = 8;
             q.DV = (q.G * g.OC * g.P + 64 * q.NW - 1) / (64 * q.NW);
             q.XV = (q.G * q.XSS / 4 + 64 * q.NW - 1) / (64 * q.NW);
-            // split the batch so that tiles x splits covers the 256 CUs once
-            int splits = std::max(1, (256 + q.nkt - 1) / q.nkt);
+            // split the batch so that tiles x splits covers the CUs once
+            int splits = std::max(1, (g.ncu + q.nkt - 1) / q.nkt);
             const int max_splits = (g.B + q.G - 1) / q.G;
             splits = std::min(splits, max_splits);
             q.GS = ((g.B + splits - 1) / splits + q.G - 1) / q.G * q.G;
@@ -289,7 +289,7 @@ hipError_t launch_wgrad_ig(const Geom &g, const WgradIgPlan &p, const void *x, c
     if (!v || 4 * v->RS != p.R4 || p.G * g.P > p.R4) return hipErrorInvalidValue;
     WgradIgArgs<T> a{g, (const T *)x, (const T *)dy, (const T *)ym, part, relu, p,
                      make_fastdiv(g.OC * g.P)};
-    dim3 grid(8 * ((p.splits + 7) / 8) * p.nkt);
+    dim3 grid(g.nxcd * ((p.splits + g.nxcd - 1) / g.nxcd) * p.nkt);
     hipError_t e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(v->fn, grid, dim3(64 * p.NW), p.lds, s, a);

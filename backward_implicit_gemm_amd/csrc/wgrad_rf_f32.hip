@@ -54,11 +54,12 @@ __global__ void __launch_bounds__(1024) wgrad_rf_f32(WgradRfArgs a)
     const bool loader = wave >= 8;
     const int ltid = tid - 512;                     // loader thread index
 
-    // Workgroups are dealt to the 8 XCDs round-robin by id; all column
-    // chunks of one split share an XCD, whose L2 then serves that split's dz
-    // to every chunk.
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int split = (slot / p.chunks) * 8 + xcd;
+    // Workgroups are dealt to the XCDs round-robin by id; all column chunks
+    // of one split share an XCD, whose L2 then serves that split's dz to
+    // every chunk.
+    const int nx = a.g.nxcd;
+    const int xcd = int(blockIdx.x) % nx, slot = int(blockIdx.x) / nx;
+    const int split = (slot / p.chunks) * nx + xcd;
     if (split >= p.splits) return;
     const int chunk = slot % p.chunks;
     const int qs = split * p.QPS;
@@ -327,27 +328,37 @@ bool plan_wgrad_rf_f32(const Geom &g, WgradRfPlan &p)
         if (!q.QB) continue;
         q.SPP = (q.QB * g.P + 3) / 4;
         // x pitches with the fewest LDS bank conflicts on the B reads, then
-        // the smallest
-        int bc = 1 << 30;
-        for (int WP = g.W; WP < g.W + 16; ++WP)
-            for (int IS = g.H * WP; IS < g.H * WP + 16; ++IS) {
-                const int c = x_read_conflicts(g, q, WP, IS);
-                if (c < bc) { bc = c; q.WP = WP; q.IS = IS; }
-            }
+        // the smallest (independent of the batch size, so searched once per
+        // layer shape and variant)
+        static SearchMemo<std::pair<int, int>> memo;
+        const int key[12] = {g.IC, g.H, g.W, g.OC, g.KH, g.KW, g.S, q.NBWV, q.QB, q.CCS, 0, 0};
+        const std::pair<int, int> pitch = memo.get(key, [&] {
+            int bc = 1 << 30, bw = g.W, bi = g.H * g.W;
+            for (int WP = g.W; WP < g.W + 16; ++WP)
+                for (int IS = g.H * WP; IS < g.H * WP + 16; ++IS) {
+                    const int c = x_read_conflicts(g, q, WP, IS);
+                    if (c < bc) { bc = c; bw = WP; bi = IS; }
+                }
+            return std::make_pair(bw, bi);
+        });
+        q.WP = pitch.first;
+        q.IS = pitch.second;
         q.bufsz = q.QB * q.CCS * q.IS + q.QB * g.P * q.OCP + 1;
         q.lds = size_t(2) * q.bufsz * 16;
         if (q.lds > 150 * 1024) continue;
-        // one workgroup per CU: splits fill 256 CUs, in multiples of 8 (one per XCD)
-        int splits = std::max(1, 256 / q.chunks);
-        if (splits >= 8) splits -= splits % 8;
+        // one workgroup per CU: splits fill the CUs, in multiples of the
+        // XCD count (one split per XCD)
+        int splits = std::max(1, g.ncu / q.chunks);
+        if (splits >= g.nxcd) splits -= splits % g.nxcd;
         splits = std::min({splits, NQ, 64});
         // a split's quads fill whole phases, so a phase never reaches into
         // the next split (only past the batch, where the loads return zeros)
         q.QPS = ((NQ + splits - 1) / splits + q.QB - 1) / q.QB * q.QB;
         q.splits = (NQ + q.QPS - 1) / q.QPS;
         const int nph = (q.QPS + q.QB - 1) / q.QB;
-        // split z runs on XCD z % 8 (32 CUs) with all its chunks
-        const double rounds = std::ceil(double((q.splits + 7) / 8 * q.chunks) / 32.0);
+        // split z runs on XCD z % nxcd with all its chunks
+        const double rounds = std::ceil(double((q.splits + g.nxcd - 1) / g.nxcd * q.chunks) /
+                                        double(g.ncu / g.nxcd));
         // cycles per phase: two MFMA waves per SIMD at 32 cycles per MFMA,
         // but no less than the loader waves' fetch (a global load's latency)
         // and stash, plus ~200 for the barrier
@@ -375,7 +386,7 @@ hipError_t launch_wgrad_rf_f32(const Geom &g, const WgradRfPlan &p, const void *
     void (*fn)(WgradRfArgs) = relu ? v->fn_relu : v->fn;
     hipError_t e = allow_max_lds(reinterpret_cast<const void *>(fn));
     if (e != hipSuccess) return e;
-    const int grid = 8 * ((p.splits + 7) / 8) * p.chunks;
+    const int grid = g.nxcd * ((p.splits + g.nxcd - 1) / g.nxcd) * p.chunks;
     hipLaunchKernelGGL(fn, dim3(grid), dim3(1024), p.lds, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

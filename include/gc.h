@@ -142,6 +142,15 @@ int gc_conv_bwd(const void *x, const void *w, const void *dy, const void *y_mask
                 void *dw, void *workspace, size_t ws_bytes,
                 const gc_conv_desc *d, int relu, int dtype, void *stream);
 
+/* Which kernels an operation would run for this problem (pure host; the
+ * same selection the entry point makes, under the current kernel policy).
+ * Writes a NUL-terminated description -- the kernel family and its tiling
+ * parameters, e.g. "fwd_ws_bf16 G=4 NBW=2 ..." -- into buf (truncated to
+ * buf_bytes - 1 characters).  op is a gc_op value.  Returns GC_OK, or
+ * GC_ERR_INVALID_ARG for an invalid descriptor, op or dtype, a NULL buf or
+ * buf_bytes == 0.  Enqueues nothing. */
+int gc_conv_plan_name(int op, const gc_conv_desc *d, int dtype, char *buf, size_t buf_bytes);
+
 /* Human-readable name of a status code. */
 const char *gc_status_string(int status);
 

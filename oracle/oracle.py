@@ -35,6 +35,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
+    # GC_ORACLE_LIB names another build of conv_oracle.c (the tests' run of
+    # the pins under AddressSanitizer and UBSan)
+    other = os.environ.get("GC_ORACLE_LIB")
+    if other:
+        _lib = _bind(ctypes.CDLL(os.path.abspath(other)))
+        return _lib
     if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         build()
     _lib = _bind(ctypes.CDLL(_LIB))

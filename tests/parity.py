@@ -60,18 +60,56 @@ def draw(layer, seeds, dtype):
     return x, w, dy
 
 
-def gpu_layer(layer, x, w, dy, dtype, dev="cuda"):
-    """Forward, d_input and wgrad on the GPU; returns device tensors."""
+GUARD_BYTES = 1024
+# bit patterns no output can take: quiet NaNs with a payload
+_SENTINEL = {torch.float32: 0x7FC0A5A5, torch.bfloat16: 0x7FA5}
+
+
+class Guarded:
+    """An output tensor inside a device buffer with GUARD_BYTES of sentinel
+    words before and after it (and `offset` more elements in front, to place
+    the tensor at an address of lower alignment).  check() asserts that no
+    kernel wrote outside the tensor."""
+
+    def __init__(self, shape, dtype, dev="cuda", offset=0):
+        es = torch.tensor([], dtype=dtype).element_size()
+        self.g = GUARD_BYTES // es + offset
+        n = 1
+        for s in shape:
+            n *= int(s)
+        self.n = n
+        ib = torch.int32 if es == 4 else torch.int16
+        pat = _SENTINEL[dtype]
+        if es == 2 and pat >= 1 << 15:
+            pat -= 1 << 16
+        self.buf = torch.full((n + 2 * self.g,), pat, dtype=ib, device=dev).view(dtype)
+        self.t = self.buf[self.g:self.g + n].view(shape)   # starts as sentinel NaNs
+        self.pat, self.ib = pat, ib
+
+    def check(self, name):
+        raw = self.buf.view(self.ib)
+        for part, sl in (("before", raw[:self.g]), ("after", raw[self.g + self.n:])):
+            bad = int((sl != self.pat).sum())
+            assert bad == 0, f"{name}: {bad} guard words {part} the tensor were overwritten"
+
+
+def gpu_layer(layer, x, w, dy, dtype, dev="cuda", y_offset=0):
+    """Forward, d_input and wgrad on the GPU; returns device tensors.  Every
+    output sits between guard bands that must come back untouched; y can be
+    placed `y_offset` elements past a 1 KiB boundary."""
     td = inputs.torch_dtype(dtype)
     conv = gb.Conv(layer.x_shape, layer.w_shape, layer.stride, layer.relu, td, dev)
     xd, wd, dyd = x.to(dev), w.to(dev), dy.to(dev)
-    y = torch.full(layer.y_shape, float("nan"), dtype=td, device=dev)
-    dx = torch.full(layer.x_shape, float("nan"), dtype=td, device=dev)
-    dw = torch.full(layer.w_shape, float("nan"), dtype=td, device=dev)
+    gy = Guarded(layer.y_shape, td, dev, offset=y_offset)
+    gdx = Guarded(layer.x_shape, td, dev)
+    gdw = Guarded(layer.w_shape, td, dev)
+    y, dx, dw = gy.t, gdx.t, gdw.t
     conv.fwd(xd, wd, y)
     conv.bwd_data(dyd, wd, y, dx)
     conv.bwd_weight(xd, dyd, y, dw)
     torch.cuda.synchronize()
+    for gd, name in ((gy, "y"), (gdx, "dx"), (gdw, "dw")):
+        gd.check(name)
     return conv, y, dx, dw
 
 
@@ -83,11 +121,11 @@ def oracle_layer(layer, x, w, dy, y_gpu):
     return y, dx, dw
 
 
-def check_layer(layer, dtype, seeds=(1, 2, 3), x=None, w=None, dy=None):
+def check_layer(layer, dtype, seeds=(1, 2, 3), x=None, w=None, dy=None, y_offset=0):
     """Full element-by-element parity of all three passes; returns the errors."""
     if x is None:
         x, w, dy = draw(layer, seeds, dtype)
-    _, y, dx, dw = gpu_layer(layer, x, w, dy, dtype)
+    _, y, dx, dw = gpu_layer(layer, x, w, dy, dtype, y_offset=y_offset)
     y_ref, dx_ref, dw_ref = oracle_layer(layer, x, w, dy, y)
     errs = {"y": rel_err(f64(y), y_ref), "dx": rel_err(f64(dx), dx_ref),
             "dw": rel_err(f64(dw), dw_ref)}

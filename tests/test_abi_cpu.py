@@ -240,3 +240,50 @@ def test_bwd_workspace_covers_both_passes():
             nw = gb.gc_conv_workspace_bytes(gb.GC_OP_BWD_WEIGHT, d, dt)
             n = gb.gc_conv_workspace_bytes(gb.GC_OP_BWD, d, dt)
             assert max(nd, nw) <= n <= nd + nw + 256, (d.B, d.IC, dt, nd, nw, n)
+
+
+# ---------------------------------------------------------------------------
+# The Python binding checks every tensor's shape against the problem before
+# anything reaches the device (so these run on host tensors, without a GPU)
+# ---------------------------------------------------------------------------
+
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.float32)
+
+
+def test_binding_rejects_wrong_output_shapes():
+    x, w = _t(4, 59, 11, 15), _t(128, 59, 5, 5)
+    with pytest.raises(ValueError, match="y has shape"):
+        gb.gc_conv_fwd(x, w, _t(5, 128, 3, 4), relu=1, stride=3)
+    with pytest.raises(ValueError, match="y has shape"):
+        gb.gc_conv_fwd_bias(x, w, _t(128), _t(4, 128, 4, 4), relu=1, stride=3)
+    with pytest.raises(ValueError, match="bias has shape"):
+        gb.gc_conv_fwd_bias(x, w, _t(127), _t(4, 128, 3, 4), relu=1, stride=3)
+
+
+def test_binding_rejects_wrong_backward_shapes():
+    x, w, y = _t(4, 59, 11, 15), _t(128, 59, 5, 5), _t(4, 128, 3, 4)
+    dx, dw = _t(4, 59, 11, 15), _t(128, 59, 5, 5)
+    with pytest.raises(ValueError, match="dy has shape"):
+        gb.gc_conv_bwd_data(_t(8, 128, 3, 4), w, y, dx, relu=1, stride=3)
+    with pytest.raises(ValueError, match="y_mask has shape"):
+        gb.gc_conv_bwd_data(y, w, _t(4, 128, 3, 3), dx, relu=1, stride=3)
+    with pytest.raises(ValueError, match="dy has shape"):
+        gb.gc_conv_bwd_weight(x, _t(4, 128, 1, 2), y, dw, relu=1, stride=3, workspace=None)
+    with pytest.raises(ValueError, match="dx has shape"):
+        gb.gc_conv_bwd(x, w, y, y, _t(4, 59, 11, 14), dw, relu=1, stride=3, workspace=None)
+    with pytest.raises(ValueError, match="dw has shape"):
+        gb.gc_conv_bwd(x, w, y, y, dx, _t(128, 59, 5, 4), relu=1, stride=3, workspace=None)
+    with pytest.raises(ValueError, match="db has shape"):
+        gb.gc_conv_bwd_bias(y, y, _t(64), relu=1, x_shape=x.shape, w_shape=w.shape, stride=3,
+                            workspace=None)
+    with pytest.raises(ValueError, match="channels"):
+        gb.gc_conv_fwd(x, _t(128, 58, 5, 5), y, relu=1, stride=3)
+
+
+def test_binding_reaches_the_device_check_with_right_shapes():
+    # with every shape right, the next check is that tensors live on the GPU
+    x, w, y = _t(4, 59, 11, 15), _t(128, 59, 5, 5), _t(4, 128, 3, 4)
+    with pytest.raises(ValueError, match="device tensor"):
+        gb.gc_conv_fwd(x, w, y, relu=1, stride=3)

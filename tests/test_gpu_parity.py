@@ -2,9 +2,10 @@
 
 Covers the policy-network layer shapes of "Speedups to gemm_conv_forward and
 gemm_conv_backward kernels" (PufferLib pull request #522) at their full
-batch of 1024 in fp32 and bf16, the two-layer chain at B=16384 and 32768 on sampled
-outputs, an odd-shape sweep whose tiles end mid-tile, integer-valued inputs
-that must match bit for bit, and run-to-run determinism of wgrad.
+batch of 1024 in fp32 and bf16, the two-layer chain at B=16384 and 32768
+stage by stage on every element, an odd-shape sweep whose tiles end
+mid-tile, integer-valued inputs that must match bit for bit (at the
+workloads' batch sizes too), and run-to-run determinism of wgrad.
 """
 import numpy as np
 import pytest
@@ -57,16 +58,14 @@ def test_workload_full_parity(idx, kernel_policy):
 
 
 # ---------------------------------------------------------------------------
-# Two-layer chain at B=16384 and B=32768, stage-wise on sampled outputs
+# Two-layer chain at B=16384 and B=32768, stage-wise, every element: each
+# oracle stage gets exactly the bf16 tensors the GPU stage got (y1 as conv2's
+# input and conv1's mask, dy1 as conv1's dy)
 # ---------------------------------------------------------------------------
 
-def _sample(shape, n, seed):
-    r = np.random.default_rng(seed)
-    return np.stack([r.integers(0, s, n) for s in shape], axis=1)
-
-
 @pytest.mark.parametrize("idx", [4, 5], ids=[w.name for w in inputs.WORKLOADS[4:6]])
-def test_chain_sampled(idx):
+def test_chain_stagewise_full(idx):
+    from parity import Guarded
     wl = inputs.WORKLOADS[idx]
     l1, l2 = (Layer.of(L) for L in wl.layers)
     t = inputs.workload_inputs(wl)
@@ -75,12 +74,10 @@ def test_chain_sampled(idx):
     c1 = gb.Conv(l1.x_shape, l1.w_shape, l1.stride, l1.relu, td, dev)
     c2 = gb.Conv(l2.x_shape, l2.w_shape, l2.stride, l2.relu, td, dev)
     x, w1, w2, dy2 = (t[k].to(dev) for k in ("x", "w1", "w2", "dy"))
-    y1 = torch.empty(l1.y_shape, dtype=td, device=dev)
-    y2 = torch.empty(l2.y_shape, dtype=td, device=dev)
-    dy1 = torch.empty_like(y1)
-    dw2 = torch.empty_like(w2)
-    dx1 = torch.empty_like(x)
-    dw1 = torch.empty_like(w1)
+    g = {k: Guarded(shape, td, dev) for k, shape in (
+        ("y1", l1.y_shape), ("y2", l2.y_shape), ("dy1", l1.y_shape), ("dw2", l2.w_shape),
+        ("dx1", l1.x_shape), ("dw1", l1.w_shape))}
+    y1, y2, dy1, dw2, dx1, dw1 = (g[k].t for k in ("y1", "y2", "dy1", "dw2", "dx1", "dw1"))
     c1.fwd(x, w1, y1)
     c2.fwd(y1, w2, y2)
     c2.bwd_data(dy2, w2, None, dy1)
@@ -88,33 +85,27 @@ def test_chain_sampled(idx):
     c1.bwd_data(dy1, w1, y1, dx1)
     c1.bwd_weight(x, dy1, y1, dw1)
     torch.cuda.synchronize()
+    for k, gd in g.items():
+        gd.check(k)
+    print(f"chain B={l1.B}: copied, running the oracle", flush=True)
 
-    n = 400
     X, W1, W2, DY2 = f64(t["x"]), f64(t["w1"]), f64(t["w2"]), f64(t["dy"])
     Y1, DY1 = f64(y1), f64(dy1)
-    checks = []
-    c = _sample(l1.y_shape, n, 1)
-    checks.append(("y1", f64(y1)[tuple(c.T)], orc.conv_fwd_at(X, W1, c, l1.stride, 1)))
-    c = _sample(l2.y_shape, n, 2)
-    checks.append(("y2", f64(y2)[tuple(c.T)], orc.conv_fwd_at(Y1, W2, c, l2.stride, 0)))
-    c = _sample(l2.x_shape, n, 3)
-    checks.append(("dy1", DY1[tuple(c.T)],
-                   orc.conv_bwd_data_at(DY2, W2, None, l2.x_shape, c, l2.stride, 0)))
-    c = _sample(l2.w_shape, n, 4)
-    checks.append(("dw2", f64(dw2)[tuple(c.T)],
-                   orc.conv_bwd_weight_at(Y1, DY2, None, l2.w_shape, c, l2.stride, 0)))
-    c = _sample(l1.x_shape, n, 5)
-    checks.append(("dx1", f64(dx1)[tuple(c.T)],
-                   orc.conv_bwd_data_at(DY1, W1, Y1, l1.x_shape, c, l1.stride, 1)))
-    c = _sample(l1.w_shape, n, 6)
-    checks.append(("dw1", f64(dw1)[tuple(c.T)],
-                   orc.conv_bwd_weight_at(X, DY1, Y1, l1.w_shape, c, l1.stride, 1)))
-    for name, got, ref in checks:
-        e = rel_err(got, ref)
-        print(f"chain {name}: sampled max|diff|/max|ref| = {e:.2e}", flush=True)
+    stages = (
+        ("y1", y1, lambda: orc.conv_fwd(X, W1, l1.stride, 1)),
+        ("y2", y2, lambda: orc.conv_fwd(Y1, W2, l2.stride, 0)),
+        ("dy1", dy1, lambda: orc.conv_bwd_data(DY2, W2, None, l2.x_shape, l2.stride, 0)),
+        ("dw2", dw2, lambda: orc.conv_bwd_weight(Y1, DY2, None, l2.w_shape, l2.stride, 0)),
+        ("dx1", dx1, lambda: orc.conv_bwd_data(DY1, W1, Y1, l1.x_shape, l1.stride, 1)),
+        ("dw1", dw1, lambda: orc.conv_bwd_weight(X, DY1, Y1, l1.w_shape, l1.stride, 1)),
+    )
+    for name, got, ref_fn in stages:
+        ref = ref_fn()
+        e = rel_err(f64(got), ref)
+        print(f"chain B={l1.B} {name}: max|diff|/max|ref| = {e:.2e}", flush=True)
         assert e <= TOL["bf16"], (name, e)
+        del ref
     assert torch.all(dx1[..., 14] == 0)
-    assert torch.isfinite(dx1.float()).all() and torch.isfinite(dw1.float()).all()
 
 
 # ---------------------------------------------------------------------------
@@ -158,19 +149,32 @@ def test_odd_shapes(shape, dtype, relu, kernel_policy):
 # result cannot depend on summation order and must match exactly.
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("kernel_policy", POLICIES, ids=["auto", "generic"], indirect=True)
+INT_SHAPES = [
+    # B, IC, H, W, OC, KH, KW, S, relu: the two layer shapes at B=64, at the
+    # workloads' B=1024 (the instances the bench times) and at the chain's
+    # B=16384, and the auto-policy instance of B=600 for layer 1
+    (64, 59, 11, 15, 128, 5, 5, 3, 1), (64, 128, 3, 4, 128, 3, 3, 1, 1),
+    (600, 59, 11, 15, 128, 5, 5, 3, 1),
+    (1024, 59, 11, 15, 128, 5, 5, 3, 1), (1024, 128, 3, 4, 128, 3, 3, 1, 0),
+    (16384, 59, 11, 15, 128, 5, 5, 3, 1), (16384, 128, 3, 4, 128, 3, 3, 1, 0),
+]
+INT_CASES = [(s, p) for s in INT_SHAPES for p in POLICIES if s[0] <= 64 or p == gb.GC_POLICY_AUTO]
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("shape", [(64, 59, 11, 15, 128, 5, 5, 3), (64, 128, 3, 4, 128, 3, 3, 1)])
+@pytest.mark.parametrize("shape,kernel_policy", INT_CASES, indirect=["kernel_policy"],
+                         ids=[f"b{s[0]}-ic{s[1]}-{'auto' if p == 0 else 'generic'}" for s, p in INT_CASES])
 def test_integer_inputs_exact(shape, dtype, kernel_policy):
-    layer = Layer(*shape, relu=1)
+    layer = Layer(*shape)
+    relu = layer.relu
     x = inputs.integers(layer.x_shape, 21, dtype=dtype)
     w = inputs.integers(layer.w_shape, 22, dtype=dtype)
     dy = inputs.integers(layer.y_shape, 23, dtype=dtype)
     _, y, dx, dw = gpu_layer(layer, x, w, dy, dtype)
-    ym = f64(y)
-    y_ref = orc.conv_fwd(f64(x), f64(w), layer.stride, 1)
-    dx_ref = orc.conv_bwd_data(f64(dy), f64(w), ym, layer.x_shape, layer.stride, 1)
-    dw_ref = orc.conv_bwd_weight(f64(x), f64(dy), ym, layer.w_shape, layer.stride, 1)
+    ym = f64(y) if relu else None
+    y_ref = orc.conv_fwd(f64(x), f64(w), layer.stride, relu)
+    dx_ref = orc.conv_bwd_data(f64(dy), f64(w), ym, layer.x_shape, layer.stride, relu)
+    dw_ref = orc.conv_bwd_weight(f64(x), f64(dy), ym, layer.w_shape, layer.stride, relu)
     td = inputs.torch_dtype(dtype)
     rne = lambda a: torch.from_numpy(a).to(torch.float32).to(td).to(torch.float64).numpy()
     for name, got, ref in (("y", y, y_ref), ("dx", dx, dx_ref), ("dw", dw, dw_ref)):

@@ -1,0 +1,95 @@
+"""Which kernels the library runs, checked on the host through
+gc_conv_plan_name (no GPU needed).
+
+For the two policy-network layer shapes of "Speedups to gemm_conv_forward
+and gemm_conv_backward kernels" (PufferLib pull request #522) the
+shape-generic fallback must never run, at any batch size the encoder uses,
+and every kernel instance the planners can pick must be one the GPU parity
+tests run (tests/cases.py lists both).
+"""
+import pytest
+
+from backward_implicit_gemm_amd import binding as gb
+
+from cases import INSTANCES, LAYER_BATCHES, LAYER_SHAPES, OTHER_GPU_BATCHES, instance_key
+
+OPS = {"fwd": gb.GC_OP_FWD, "bwd_data": gb.GC_OP_BWD_DATA, "bwd_weight": gb.GC_OP_BWD_WEIGHT}
+DT = {"f32": gb.GC_F32, "bf16": gb.GC_BF16}
+
+
+def plan(layer, B, dtype, op):
+    IC, H, W, OC, KH, KW, S, _ = LAYER_SHAPES[layer]
+    return gb.gc_conv_plan_name(OPS[op], gb.make_desc(B, IC, H, W, OC, KH, KW, S), DT[dtype])
+
+
+def keys(layer, dtype, op, batches):
+    return {instance_key(plan(layer, B, dtype, op)) for B in batches}
+
+
+def test_plan_name_errors():
+    import ctypes
+    L = gb.lib()
+    d = gb.make_desc(4, 3, 5, 5, 2, 3, 3, 1)
+    buf = ctypes.create_string_buffer(8)
+    assert L.gc_conv_plan_name(gb.GC_OP_FWD, ctypes.byref(d), gb.GC_F32, None, 8) == gb.GC_ERR_INVALID_ARG
+    assert L.gc_conv_plan_name(gb.GC_OP_FWD, ctypes.byref(d), gb.GC_F32, buf, 0) == gb.GC_ERR_INVALID_ARG
+    assert L.gc_conv_plan_name(99, ctypes.byref(d), gb.GC_F32, buf, 8) == gb.GC_ERR_INVALID_ARG
+    assert L.gc_conv_plan_name(gb.GC_OP_FWD, ctypes.byref(d), 7, buf, 8) == gb.GC_ERR_INVALID_ARG
+    bad = gb.make_desc(4, 3, 2, 5, 2, 3, 3, 1)
+    assert L.gc_conv_plan_name(gb.GC_OP_FWD, ctypes.byref(bad), gb.GC_F32, buf, 8) == gb.GC_ERR_INVALID_ARG
+    # truncated, but NUL-terminated
+    assert L.gc_conv_plan_name(gb.GC_OP_FWD, ctypes.byref(d), gb.GC_F32, buf, 8) == gb.GC_OK
+    assert len(buf.value) == 7
+
+
+def test_policy_generic_is_reported():
+    prev = gb.gc_set_kernel_policy(gb.GC_POLICY_GENERIC)
+    try:
+        assert plan("layer1", 1024, "bf16", "fwd") == "igemm_generic_fwd"
+        assert plan("layer1", 1024, "f32", "bwd_data") == "igemm_generic_dgrad"
+        assert plan("layer2", 1024, "bf16", "bwd_weight").startswith("igemm_generic_wgrad")
+    finally:
+        gb.gc_set_kernel_policy(prev)
+
+
+def test_headline_plans():
+    # the kernels the B=1024 workloads run (the bench's per-call figures)
+    assert plan("layer1", 1024, "f32", "fwd").startswith("fwd_ws_f32<NWM=8,MB=3,TS=7,NCG=15,CPP=3> G=4")
+    assert plan("layer1", 1024, "f32", "bwd_weight").startswith("wgrad_rf_f32<NBWV=6>")
+    assert plan("layer1", 1024, "bf16", "fwd").startswith("fwd_ws_bf16<NBW=2,MB=3,TS=7,NCG=8,CPP=3> G=4")
+    assert plan("layer2", 1024, "bf16", "fwd").startswith("fwd_ws_bf16<NBW=1,MB=1,TS=3,NCG=16,CPP=16> G=8")
+
+
+ENCODER_BATCHES = (256, 512, 768, 1024, 2048, 4096, 8192, 16384, 32768)
+
+
+@pytest.mark.parametrize("layer", sorted(LAYER_SHAPES))
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_layer_shapes_never_run_the_generic_kernels(layer, dtype):
+    for B in ENCODER_BATCHES:
+        for op in (gb.GC_OP_FWD, gb.GC_OP_BWD_DATA, gb.GC_OP_BWD_WEIGHT, gb.GC_OP_BWD):
+            IC, H, W, OC, KH, KW, S, _ = LAYER_SHAPES[layer]
+            name = gb.gc_conv_plan_name(op, gb.make_desc(B, IC, H, W, OC, KH, KW, S), DT[dtype])
+            assert "generic" not in name, (layer, dtype, B, op, name)
+
+
+def _sweep():
+    # every batch size up to 70, then a stride-29 walk to 4200 plus the
+    # points where the planners switch, then a sample up to 40000
+    s = set(range(1, 71)) | set(range(71, 4200, 29)) | set(range(4200, 40000, 997))
+    s |= {205, 226, 387, 415, 510, 511, 512, 513, 618, 639, 765, 766, 772, 1016, 1017, 1020,
+          1021, 1227, 1542, 2033, 2039, 4065, 4069}
+    return sorted(s)
+
+
+@pytest.mark.parametrize("key", sorted(INSTANCES), ids=["-".join(k) for k in sorted(INSTANCES)])
+def test_every_reachable_instance_is_gpu_tested(key):
+    layer, dtype, op = key
+    tested = keys(layer, dtype, op, LAYER_BATCHES[(layer, dtype)])
+    # the GPU batch list reaches exactly the listed instances ...
+    assert tested == INSTANCES[key], (tested ^ INSTANCES[key])
+    # ... and a sweep of batch sizes reaches no other
+    reached = keys(layer, dtype, op, _sweep())
+    assert reached <= INSTANCES[key], reached - INSTANCES[key]
+    for B in OTHER_GPU_BATCHES[layer]:
+        assert instance_key(plan(layer, B, dtype, op)) in INSTANCES[key]
