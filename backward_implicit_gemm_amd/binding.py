@@ -21,7 +21,7 @@ EXPORTED = (
     "gc_conv_out_dims", "gc_conv_workspace_bytes", "gc_conv_fwd", "gc_conv_bwd_data",
     "gc_conv_bwd_weight", "gc_status_string", "gc_fastdiv_selfcheck", "gc_version",
     "gc_set_kernel_policy", "gc_conv_fwd_bias", "gc_conv_bwd_bias", "gc_conv_bwd",
-    "gc_conv_plan_name",
+    "gc_conv_plan_name", "gc_conv_fwd_noalloc",
 )
 GC_POLICY_AUTO, GC_POLICY_GENERIC = 0, 1
 
@@ -55,6 +55,8 @@ def lib():
     L.gc_conv_workspace_bytes.restype = sz
     L.gc_conv_fwd.argtypes = [vp, vp, vp, vp, sz, dp, i, i, vp]
     L.gc_conv_fwd.restype = i
+    L.gc_conv_fwd_noalloc.argtypes = [vp, vp, vp, dp, i, i, vp]
+    L.gc_conv_fwd_noalloc.restype = i
     L.gc_conv_fwd_bias.argtypes = [vp, vp, vp, vp, vp, sz, dp, i, i, vp]
     L.gc_conv_fwd_bias.restype = i
     L.gc_conv_bwd_bias.argtypes = [vp, vp, vp, vp, sz, dp, i, i, vp]
@@ -195,6 +197,18 @@ def gc_conv_fwd(x, w, y, relu, stride, workspace=None, stream=None):
     st = lib().gc_conv_fwd(_dev(x, "x", dt), _dev(w, "w", dt), _dev(y, "y", dt), wp, wn,
                            ctypes.byref(desc), int(relu), dt, _stream(stream))
     _check("gc_conv_fwd", st)
+    return y
+
+
+def gc_conv_fwd_noalloc(x, w, y, relu, stride, stream=None):
+    """y = relu?(conv(x, w)) via gc_conv_fwd_noalloc (no workspace: the
+    library's static per-GPU scratch)."""
+    dt = _dtype_code(x)
+    desc = desc_from(x.shape, w.shape, stride)
+    _expect(y, "y", _y_shape(desc))
+    st = lib().gc_conv_fwd_noalloc(_dev(x, "x", dt), _dev(w, "w", dt), _dev(y, "y", dt),
+                                   ctypes.byref(desc), int(relu), dt, _stream(stream))
+    _check("gc_conv_fwd_noalloc", st)
     return y
 
 

@@ -293,6 +293,42 @@ void name_wgrad(const WgradSel &s, char *buf, size_t n, size_t &at)
     case WgradKind::Generic: append(buf, n, at, "igemm_generic_wgrad splits=%d", s.splits); break;
     }
 }
+// Scratch memory of gc_conv_fwd_noalloc: a file-scope device array (each
+// GPU the library runs on holds its own copy until the process ends), used
+// for the forward's packed weights.  Host code never passes the array's name
+// to a kernel (on the host it only stands for the symbol); it passes the
+// device address hipGetSymbolAddress gives for the current device, taken
+// once per device.
+constexpr size_t kNoallocScratchBytes = size_t(2) << 20;
+__device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+// The current device's address of `scratch`, or nullptr (and *err set) if
+// it cannot be had.
+void *scratch_address(hipError_t *err)
+{
+    constexpr int kMaxDev = 64;
+    static std::mutex m;
+    static void *addr[kMaxDev];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess && (dev < 0 || dev >= kMaxDev)) e = hipErrorInvalidDevice;
+    if (e != hipSuccess) {
+        *err = e;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lk(m);
+    if (!addr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+            return nullptr;
+        }
+        addr[dev] = ptr;
+    }
+    return addr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -384,6 +420,30 @@ int gc_conv_fwd(const void *x, const void *w, void *y, void *workspace, size_t w
                 const gc_conv_desc *d, int relu, int dtype, void *stream)
 {
     return conv_fwd(x, w, nullptr, y, workspace, ws_bytes, d, relu, dtype, stream);
+}
+
+int gc_conv_fwd_noalloc(const void *x, const void *w, void *y, const gc_conv_desc *d, int relu,
+                        int dtype, void *stream)
+{
+    // the same checks as gc_conv_fwd, then the workspace the plan needs
+    // against the static scratch, all before any HIP call
+    Geom g;
+    const int st = check_desc(d, &g);
+    if (st != GC_OK) return st;
+    if (!valid_dtype(dtype) || (relu != 0 && relu != 1)) return GC_ERR_INVALID_ARG;
+    if (!x || !w || !y) return GC_ERR_INVALID_ARG;
+    if (!aligned(x, dtype) || !aligned(w, dtype) || !aligned(y, dtype)) return GC_ERR_INVALID_ARG;
+    const size_t need = gc_conv_workspace_bytes(GC_OP_FWD, d, dtype);
+    if (need > kNoallocScratchBytes) return GC_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (need) {
+        hipError_t e = hipSuccess;
+        ws = scratch_address(&e);
+        if (!ws) return hip_status(e);
+    }
+    // the packed weights are written in full by the call before they are
+    // read, so nothing in the scratch needs clearing
+    return conv_fwd(x, w, nullptr, y, ws, need ? kNoallocScratchBytes : 0, d, relu, dtype, stream);
 }
 
 int gc_conv_fwd_bias(const void *x, const void *w, const void *bias, void *y, void *workspace,

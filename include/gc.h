@@ -96,6 +96,20 @@ int gc_conv_fwd(const void *x, const void *w, void *y,
                 void *workspace, size_t ws_bytes,
                 const gc_conv_desc *d, int relu, int dtype, void *stream);
 
+/* The forward pass of gc_conv_fwd, for callers that cannot allocate memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without a workspace, the same results bit
+ * for bit.  Its scratch memory (the packed weights) is a static device array
+ * of 2 MiB per GPU, held by each GPU the library runs on until the process
+ * ends; it covers both layer shapes of the PR page at every batch size, and
+ * a problem whose gc_conv_workspace_bytes(GC_OP_FWD, ...) exceeds it returns
+ * GC_ERR_WORKSPACE before anything is enqueued.  Every call on one GPU shares that
+ * GPU's array, so calls that may overlap in time on one GPU (on different
+ * streams, or from different threads) race and must not be issued; calls
+ * on one stream are ordered and safe.  It never allocates or frees memory. */
+int gc_conv_fwd_noalloc(const void *x, const void *w, void *y,
+                        const gc_conv_desc *d, int relu, int dtype, void *stream);
+
 /* Forward pass with a bias: y = f(conv(x, w) + bias[oc]).  bias [OC] has the
  * storage type and is added in fp32 before the ReLU; everything else is as in
  * gc_conv_fwd (same workspace size).  bias must not be NULL. */

@@ -287,3 +287,20 @@ def test_binding_reaches_the_device_check_with_right_shapes():
     x, w, y = _t(4, 59, 11, 15), _t(128, 59, 5, 5), _t(4, 128, 3, 4)
     with pytest.raises(ValueError, match="device tensor"):
         gb.gc_conv_fwd(x, w, y, relu=1, stride=3)
+
+
+def test_noalloc_forward_rejects_before_any_launch():
+    # validation and the scratch-size check come before anything is enqueued,
+    # so they run without a GPU (FAKE pointers are never touched)
+    L = gb.lib()
+    big = gb.make_desc(2, 59, 11, 15, 512, 5, 5, 3)      # layer 1 with 512 output channels
+    assert gb.gc_conv_workspace_bytes(gb.GC_OP_FWD, big, gb.GC_F32) > (2 << 20)
+    assert L.gc_conv_fwd_noalloc(FAKE, FAKE, FAKE, ctypes.byref(big), 0, gb.GC_F32, None) == gb.GC_ERR_WORKSPACE
+    assert L.gc_conv_fwd_noalloc(None, FAKE, FAKE, ctypes.byref(L1), 1, gb.GC_F32, None) == gb.GC_ERR_INVALID_ARG
+    assert L.gc_conv_fwd_noalloc(FAKE, FAKE, FAKE, ctypes.byref(L1), 2, gb.GC_F32, None) == gb.GC_ERR_INVALID_ARG
+    assert L.gc_conv_fwd_noalloc(FAKE, FAKE, FAKE, None, 1, gb.GC_F32, None) == gb.GC_ERR_INVALID_ARG
+    # both page-1 layer shapes fit the scratch at any batch size
+    for B in (1, 1024, 32768):
+        for shape in ((59, 11, 15, 128, 5, 5, 3), (128, 3, 4, 128, 3, 3, 1)):
+            for dt in (gb.GC_F32, gb.GC_BF16):
+                assert gb.gc_conv_workspace_bytes(gb.GC_OP_FWD, gb.make_desc(B, *shape), dt) <= (2 << 20)
