@@ -10,16 +10,21 @@ forward and backward separately over 50 warmup and 200 timed iterations.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
 
-Prints one JSON line per workload: throughput in TFLOP/s of algorithmic work
+Prints one JSON line: throughput in TFLOP/s of algorithmic work
 (2*B*OC*OH*OW*IC*KH*KW per pass, three passes per step) over K steps, each
 step replayed as one HIP graph between HIP events on the launch stream; the
 same K steps issued eagerly (host work included); the step timed cold
 (caches flushed by a 640 MB write before each replay); the launch floor (a
-graph of as many one-element kernels as a step launches); per-call GPU times
-from graphs of back-to-back copies of each call; the backward through
-gc_conv_bwd (d_input and wgrad in one call) per call and as a step; a roofline entry for the
-dominant call; and the CPU oracle timed on this host on a bounded sample
-(default workload only).
+graph of as many one-element kernels as a step launches); per-call GPU times,
+hot (graphs of back-to-back copies of each call) and cold (each call alone
+after a cache flush, median of several); the backward through gc_conv_bwd
+(d_input and wgrad in one call); a roofline entry for the dominant call; and
+the CPU oracle timed on this host on a bounded sample.  The same line carries,
+under "workloads", every other workload's step and per-call times with each
+call's fraction of its binding roofline (bf16: algorithmic bytes over the cold
+time against HBM; fp32: flops over the hot time against fp32 MFMA), and under
+"data_independence" the layer-1 bf16 calls rerun with x scaled by 1/8 and 8.
+--workload NAME (or --all) prints the full line of other workloads.
 """
 import argparse
 import hashlib
@@ -60,6 +65,9 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--all", action="store_true", help="every workload, one line each")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="default workload only: skip the other workloads and the "
+                         "data-independence leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle leg")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -107,7 +115,10 @@ def measured_traffic(workload, op):
     return None if e is None else e.get("bytes_per_launch")
 
 
-def run_gpu(wl, steps, warmup):
+def run_gpu(wl, steps, warmup, x_scale=1.0, extras=True):
+    """Times workload wl.  x_scale multiplies the input x (a power of two
+    leaves every product exact up to the exponent); extras=False skips the
+    eager and bias timings."""
     import torch
 
     from backward_implicit_gemm_amd import binding as gb
@@ -118,6 +129,8 @@ def run_gpu(wl, steps, warmup):
     t = inputs.workload_inputs(wl)
     layers = wl.layers
     convs = [gb.Conv(L.x_shape, L.w_shape, L.stride, L.relu, td, dev) for L in layers]
+    if x_scale != 1.0:
+        t["x"] = (t["x"].float() * x_scale).to(td)
     if len(layers) == 1:
         xs = [t["x"].to(dev)]
         ws = [t["w"].to(dev)]
@@ -210,12 +223,14 @@ def run_gpu(wl, steps, warmup):
     del g
 
     # The same steps issued eagerly through the C ABI, host work included.
-    start.record(stream)
-    for _ in range(steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_eager = start.elapsed_time(end) / steps
+    ms_eager = None
+    if extras:
+        start.record(stream)
+        for _ in range(steps):
+            step()
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms_eager = start.elapsed_time(end) / steps
 
     # Per call: a graph of REPS back-to-back copies of the call, replayed and
     # timed with HIP events on the launch stream, so each figure is the
@@ -237,6 +252,7 @@ def run_gpu(wl, steps, warmup):
         torch.cuda.synchronize()
         per_call[name] = start.elapsed_time(end) / (replays * reps) * 1e3
         del g
+    per_call_cold = {name: cold_call_us(f, stream, dev) for name, f in calls}
 
     # The whole backward of each layer through gc_conv_bwd (one call for
     # d_input and wgrad; fewer launches where a fused plan exists), per call
@@ -259,6 +275,8 @@ def run_gpu(wl, steps, warmup):
         torch.cuda.synchronize()
         fused["us_per_call"][name] = round(start.elapsed_time(end) / (replays * reps) * 1e3, 3)
         del g
+    fused["us_per_call_cold"] = {name: round(cold_call_us(f, stream, dev), 3)
+                                 for name, f in fused_calls}
     fwd_calls = [c for c in calls if c[0].startswith("fwd")]
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -287,7 +305,7 @@ def run_gpu(wl, steps, warmup):
         bias_calls.append((f"fwd_bias{i + 1}", lambda c=c, i=i, b=b, yb=yb: c.fwd_bias(xs[i], ws[i], b, yb)))
         bias_calls.append((f"bwd_bias{i + 1}", lambda c=c, i=i, db=db: c.bwd_bias(dys[i], ys[i], db)))
     bias_us = {}
-    for name, f in bias_calls:
+    for name, f in (bias_calls if extras else []):
         f()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -302,7 +320,45 @@ def run_gpu(wl, steps, warmup):
         torch.cuda.synchronize()
         bias_us[name] = start.elapsed_time(end) / (replays * reps) * 1e3
         del g
-    return ms_step, ms_eager, per_call, bias_us, ms_cold, floor, fused
+    return {"ms_step": ms_step, "ms_eager": ms_eager, "per_call": per_call,
+            "per_call_cold": per_call_cold, "bias_us": bias_us, "ms_cold": ms_cold,
+            "floor": floor, "fused": fused}
+
+
+def cold_call_us(f, stream, dev, reps=4, rounds=5):
+    """One call's GPU time from HBM.  Graph A holds `reps` copies of [a 640 MB
+    write, the call], graph B the same writes alone; the write is more than
+    the 256 MB MALL and every L2 together, so each copy of the call starts
+    with cold caches.  A and B are replayed in turn between HIP events on the
+    launch stream, and the call's time is (median A - median B) / reps, which
+    leaves out the writes and the graph launch."""
+    import torch
+
+    flush = torch.empty(640 << 20, dtype=torch.uint8, device=dev)
+    f()
+    ga, gb_ = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(ga):
+        for _ in range(reps):
+            flush.fill_(1)
+            f()
+    with torch.cuda.graph(gb_):
+        for _ in range(reps):
+            flush.fill_(1)
+    ga.replay()
+    gb_.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    ta, tb = [], []
+    for _ in range(rounds):
+        for g, ts in ((ga, ta), (gb_, tb)):
+            start.record(stream)
+            g.replay()
+            end.record(stream)
+            torch.cuda.synchronize()
+            ts.append(start.elapsed_time(end) * 1e3)
+    del ga, gb_, flush
+    return max(0.0, (statistics.median(ta) - statistics.median(tb)) / reps)
 
 
 def cpu_baseline(wl, budget_s):
@@ -350,28 +406,61 @@ CALL_KERNELS = {
               "bf16": ["dz_groups_bf16", "wgrad_ws_bf16", "wgrad_reduce"]},
 }
 
-def report(wl, ms_step, ms_eager, per_call, bias_us, ms_cold, floor, steps, warmup, cpu, fused=None):
-    L0 = wl.layers[0]
+def call_work(wl):
+    """Algorithmic (flops, bytes) of every call of a step."""
     esize = 4 if wl.dtype == "f32" else 2
-    flops_step = sum(3 * layer_flops(L) for L in wl.layers)
-    # per-call algorithmic work
     work = {}
     for i, L in enumerate(wl.layers):
         b = layer_bytes(L, esize)
         for op in ("fwd", "dgrad", "wgrad"):
             work[f"{op}{i + 1}"] = (layer_flops(L), b[op])
-    dom = max(per_call, key=per_call.get)
-    fl, by = work[dom]
-    us = per_call[dom]
+    return work
+
+
+def call_roofline(wl, name, us_hot, us_cold):
+    """A call against its binding roofline: fp32 is MFMA-bound at these
+    arithmetic intensities (priced on the hot time), bf16 HBM-bound (priced on
+    the cold time, with the hot figure beside it as possibly MALL-resident)."""
+    fl, by = call_work(wl)[name]
     if wl.dtype == "f32":
-        bound, peak, unit, achieved = "mfma", PEAK["mfma_f32"], "TFLOP/s", fl / (us * 1e-6) / 1e12
-    else:
-        # bf16 at these shapes sits left of the MFMA ridge: HBM-bound
-        bound, peak, unit, achieved = "hbm", PEAK["hbm_gbs"], "GB/s", by / (us * 1e-6) / 1e9
-    roof = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": measured_traffic(wl.name, dom),
-            "kernel_call": dom, "kernels": CALL_KERNELS[dom.rstrip("0123456789")][wl.dtype],
-            "us_per_launch": round(us, 3)}
+        a = fl / (us_hot * 1e-6) / 1e12
+        return {"bound": "mfma", "achieved": round(a, 3), "peak": PEAK["mfma_f32"],
+                "unit": "TFLOP/s", "frac": round(a / PEAK["mfma_f32"], 4)}
+    a = by / (us_cold * 1e-6) / 1e9
+    a_hot = by / (us_hot * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(a, 3), "peak": PEAK["hbm_gbs"], "unit": "GB/s",
+            "frac": round(a / PEAK["hbm_gbs"], 4), "frac_hot": round(a_hot / PEAK["hbm_gbs"], 4)}
+
+
+def workload_summary(wl, m):
+    """Step and per-call figures of one workload, each call against its roofline."""
+    calls = {}
+    for name, us in m["per_call"].items():
+        cold = m["per_call_cold"][name]
+        r = call_roofline(wl, name, us, cold)
+        calls[name] = {"us_hot": round(us, 3), "us_cold": round(cold, 3), "frac": r["frac"],
+                       **({"frac_hot": r["frac_hot"]} if "frac_hot" in r else {})}
+    return {"dtype": wl.dtype, "bound": "mfma" if wl.dtype == "f32" else "hbm",
+            "ms_per_step": round(m["ms_step"], 5), "ms_per_step_cold": round(m["ms_cold"], 5),
+            "tflops_step": round(sum(3 * layer_flops(L) for L in wl.layers)
+                                 / (m["ms_step"] * 1e-3) / 1e12, 3),
+            "calls": calls, "fused_bwd": m["fused"], "launch_floor": m["floor"]}
+
+
+def report(wl, m, steps, warmup, cpu, others=None, data_ind=None):
+    L0 = wl.layers[0]
+    flops_step = sum(3 * layer_flops(L) for L in wl.layers)
+    per_call, ms_step = m["per_call"], m["ms_step"]
+    # the dominant call: the slowest, hot for fp32 (MFMA-bound), cold for bf16
+    times = per_call if wl.dtype == "f32" else m["per_call_cold"]
+    dom = max(times, key=times.get)
+    roof = call_roofline(wl, dom, per_call[dom], m["per_call_cold"][dom])
+    roof.pop("frac_hot", None)
+    roof.update({"traffic": measured_traffic(wl.name, dom), "kernel_call": dom,
+                 "kernels": CALL_KERNELS[dom.rstrip("0123456789")][wl.dtype],
+                 "us_per_launch": round(times[dom], 3),
+                 "timing": "hot graph replays" if wl.dtype == "f32"
+                 else "cold: each launch after a 640 MB cache flush, median"})
     value = flops_step / (ms_step * 1e-3) / 1e12
     fwd_us = sum(v for k, v in per_call.items() if k.startswith("fwd"))
     bwd_us = sum(v for k, v in per_call.items() if not k.startswith("fwd"))
@@ -387,9 +476,9 @@ def report(wl, ms_step, ms_eager, per_call, bias_us, ms_cold, floor, steps, warm
         "steps": steps,
         "warmup": warmup,
         "ms_per_step": round(ms_step, 5),
-        "ms_per_step_eager": round(ms_eager, 5),
-        "ms_per_step_cold": round(ms_cold, 5),
-        "launch_floor": floor,
+        "ms_per_step_eager": None if m["ms_eager"] is None else round(m["ms_eager"], 5),
+        "ms_per_step_cold": round(m["ms_cold"], 5),
+        "launch_floor": m["floor"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": vs,
@@ -403,17 +492,42 @@ def report(wl, ms_step, ms_eager, per_call, bias_us, ms_cold, floor, steps, warm
         },
         "us_per_iter": {"fwd": round(fwd_us, 3), "bwd": round(bwd_us, 3),
                         **{k: round(v, 3) for k, v in per_call.items()}},
+        "us_per_call_cold": {k: round(v, 3) for k, v in m["per_call_cold"].items()},
         "tflops": {"fwd": round(sum(layer_flops(L) for L in wl.layers) / (fwd_us * 1e-6) / 1e12, 3),
                    "bwd": round(sum(2 * layer_flops(L) for L in wl.layers) / (bwd_us * 1e-6) / 1e12, 3)},
         "roofline": roof,
-        "bias_us_per_call": {k: round(v, 3) for k, v in bias_us.items()},
-        "fused_bwd": fused,
+        "calls": workload_summary(wl, m)["calls"],
+        "bias_us_per_call": {k: round(v, 3) for k, v in m["bias_us"].items()},
+        "fused_bwd": m["fused"],
         "cpu_baseline": cpu,
     }
     if vs is not None:
         line["baseline_note"] = ("page 1 gemm_fast fwd+bwd on an unnamed NVIDIA GPU: "
                                  f"{PAGE1_US[wl.name][0]} + {PAGE1_US[wl.name][1]} us; context only")
+    if others:
+        line["workloads"] = others
+    if data_ind:
+        line["data_independence"] = data_ind
     return line
+
+
+DATA_INDEPENDENCE_WORKLOAD = "layer1_bf16_relu_b1024"
+
+
+def data_independence(wl, base, steps, warmup):
+    """The workload's calls again with x scaled by 1/8 and by 8 (the method's
+    work does not depend on the values): hot and cold microseconds per call,
+    and each as a ratio to the unscaled run's."""
+    out = {}
+    for scale in (0.125, 8.0):
+        m = run_gpu(wl, steps, warmup, x_scale=scale, extras=False)
+        out[f"x*{scale:g}"] = {
+            name: {"us_hot": round(m["per_call"][name], 3),
+                   "us_cold": round(m["per_call_cold"][name], 3),
+                   "ratio_hot": round(m["per_call"][name] / base["per_call"][name], 4),
+                   "ratio_cold": round(m["per_call_cold"][name] / base["per_call_cold"][name], 4)}
+            for name in m["per_call"]}
+    return out
 
 
 def main():
@@ -440,13 +554,29 @@ def main():
         if name not in names:
             print(f"unknown workload {name}; choose from {names}", file=sys.stderr)
             sys.exit(2)
-        wl = inputs.WORKLOADS[names.index(name)]
-        ms, ms_eager, per_call, bias_us, ms_cold, floor, fused = run_gpu(wl, a.steps, a.warmup)
+    byname = {w.name: w for w in inputs.WORKLOADS}
+    default_run = not a.all and a.workload == DEFAULT_WORKLOAD
+    for name in todo:
+        wl = byname[name]
+        m = run_gpu(wl, a.steps, a.warmup)
+        print(f"# {name}: {m['ms_step'] * 1e3:.1f} us per step", file=sys.stderr, flush=True)
+        others, dind = None, None
+        if default_run and not a.headline_only:
+            # every other workload's figures, and the data-independence leg
+            others = {}
+            for other in names:
+                if other == name:
+                    continue
+                mo = run_gpu(byname[other], a.steps, a.warmup, extras=False)
+                others[other] = workload_summary(byname[other], mo)
+                print(f"# {other}: {mo['ms_step'] * 1e3:.1f} us per step", file=sys.stderr,
+                      flush=True)
+                if other == DATA_INDEPENDENCE_WORKLOAD:
+                    dind = data_independence(byname[other], mo, a.steps, a.warmup)
         cpu = None
         if not a.no_cpu and name == DEFAULT_WORKLOAD:
             cpu = cpu_baseline(wl, a.cpu_seconds)
-        print(json.dumps(report(wl, ms, ms_eager, per_call, bias_us, ms_cold, floor, a.steps, a.warmup,
-                                cpu, fused)), flush=True)
+        print(json.dumps(report(wl, m, a.steps, a.warmup, cpu, others, dind)), flush=True)
 
 
 if __name__ == "__main__":

@@ -11,13 +11,19 @@ import bench  # noqa: E402
 from backward_implicit_gemm_amd import inputs  # noqa: E402
 
 
-def _line(name):
-    wl = next(w for w in inputs.WORKLOADS if w.name == name)
+def _measured(wl, hot=None, cold=None):
     per_call = {}
     for i in range(len(wl.layers)):
         per_call.update({f"fwd{i + 1}": 50.0, f"dgrad{i + 1}": 60.0, f"wgrad{i + 1}": 55.0})
     floor = {"kernels_per_step": 6, "us_per_step": 12.0, "us_per_kernel": 2.0}
-    return wl, bench.report(wl, 0.2, 0.25, per_call, {}, 0.3, floor, 100, 20, None)
+    return {"ms_step": 0.2, "ms_eager": 0.25, "per_call": hot or per_call,
+            "per_call_cold": cold or {k: v + 10.0 for k, v in per_call.items()},
+            "bias_us": {}, "ms_cold": 0.3, "floor": floor, "fused": None}
+
+
+def _line(name, **kw):
+    wl = next(w for w in inputs.WORKLOADS if w.name == name)
+    return wl, bench.report(wl, _measured(wl), 100, 20, None, **kw)
 
 
 def test_report_carries_the_contract_keys():
@@ -38,10 +44,31 @@ def test_report_carries_the_contract_keys():
     assert abs(line["value"] - 3 * flops / 0.2e-3 / 1e12) < 1e-2
 
 
-def test_report_bf16_is_priced_against_hbm():
-    _, line = _line("layer1_bf16_relu_b1024")
-    assert line["roofline"]["bound"] == "hbm" and line["roofline"]["unit"] == "GB/s"
-    assert line["dtype"] == "bf16"
+def test_report_bf16_is_priced_against_hbm_on_cold_times():
+    wl, line = _line("layer1_bf16_relu_b1024")
+    roof = line["roofline"]
+    assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and line["dtype"] == "bf16"
+    # d_input's algorithmic bytes (dy, y as the mask, w, dx) over its cold 70 us
+    L = wl.layers[0]
+    by = 2 * (2 * L.B * 128 * 12 + 128 * 59 * 25 + L.B * 59 * 165)
+    assert roof["kernel_call"] == "dgrad1" and roof["us_per_launch"] == 70.0
+    assert abs(roof["achieved"] - by / 70e-6 / 1e9) < 1e-2
+    assert abs(line["calls"]["dgrad1"]["frac_hot"] - by / 60e-6 / 1e9 / 8000) < 1e-4
+
+
+def test_report_carries_other_workloads_and_data_independence():
+    others = {}
+    for w in inputs.WORKLOADS:
+        if w.name != bench.DEFAULT_WORKLOAD:
+            others[w.name] = bench.workload_summary(w, _measured(w))
+    _, line = _line(bench.DEFAULT_WORKLOAD, others=others, data_ind={"x*8": {}})
+    json.dumps(line)
+    assert set(line["workloads"]) == {w.name for w in inputs.WORKLOADS} - {bench.DEFAULT_WORKLOAD}
+    c = line["workloads"]["layer1_bf16_relu_b1024"]["calls"]
+    assert set(c) == {"fwd1", "dgrad1", "wgrad1"} and 0 < c["fwd1"]["frac"] < 1
+    assert set(line["workloads"]["chain_bf16_b16384"]["calls"]) == {
+        "fwd1", "fwd2", "dgrad1", "dgrad2", "wgrad1", "wgrad2"}
+    assert "data_independence" in line
 
 
 def test_more_than_one_gpu_is_refused():
