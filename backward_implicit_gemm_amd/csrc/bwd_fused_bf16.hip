@@ -4,7 +4,7 @@
 // The separate calls launch: the d_input weight packing, the d_input kernel,
 // the dz regrouping, the wgrad partial-tile kernel and the fixed-order
 // reduction.  Here:
-//   1. one pre-pass launch: workgroups 0..ngroups-1 regroup dz (masked) for
+//   1. one pre-pass launch: the first ngroups*kDzSlices workgroups regroup dz (masked) for
 //      wgrad, the rest pack the weights for d_input;
 //   2. one main launch whose grid holds the d_input workgroups followed by the
 //      wgrad workgroups -- the two sets are independent, so they run side by
@@ -32,10 +32,10 @@ __global__ void __launch_bounds__(kDzNT) bwd_prep_bf16(const u16 *__restrict__ d
                                                        int KS, int total, int npack)
 {
     const int bid = blockIdx.x;
-    if (bid < ngroups)
+    if (bid < ngroups * kDzSlices)
         dz_groups_bf16_body(dy, ym, dzg, g, relu, PP, bid);
     else
-        pack_w_dgrad_bf16_body(w, wp, g, CC, NBC, KS, total, bid - ngroups, npack);
+        pack_w_dgrad_bf16_body(w, wp, g, CC, NBC, KS, total, bid - ngroups * kDzSlices, npack);
 }
 
 // d_input workgroups first (n_dg of them, an (image group, channel group)
@@ -54,20 +54,22 @@ __global__ void __launch_bounds__(64 * NW) bwd_fused_bf16(DgradBfArgs da, WgradB
 }
 
 struct FusedVariant {
-    int MB, KS, TAPS, NBW, NSTEP;
+    int MB, KS, TAPS, NBW, NSTEP, JW;
     void (*fn)(DgradBfArgs, WgradBfArgs, int, int, int);   // both grids in one launch
     void (*fn_d)(DgradBfArgs);                              // d_input alone
     void (*fn_w)(WgradBfArgs);                              // wgrad alone (16 waves)
 };
 // The (d_input, wgrad) kernel pairs the planners choose for the policy
 // network's layers at B=1024 and B=16384; other shapes use separate calls.
-#define FV(MB, KS, TAPS, NBW, NSTEP)                                                   \
-    {MB, KS, TAPS, NBW, NSTEP, bwd_fused_bf16<8, MB, KS, TAPS, NBW, 2, NSTEP>,          \
-     dgrad_ig_bf16<8, MB, KS, TAPS, NBW, 2>, wgrad_ws_bf16<NSTEP>}
+#define FV(MB, KS, TAPS, NBW, NSTEP, JW)                                              \
+    {MB, KS, TAPS, NBW, NSTEP, JW, bwd_fused_bf16<8, MB, KS, TAPS, NBW, 2, NSTEP>,     \
+     dgrad_ig_bf16<8, MB, KS, TAPS, NBW, 2>, wgrad_ws_bf16<NSTEP, JW>}
+// (both grids in one launch run the 8-wave wgrad body, whose tiles are 128
+// columns: JW = 2)
 const FusedVariant kFusedVariants[] = {
-    FV(3, 4, 4, 1, 3),    // 59 -> 128, 11x15, 5x5, stride 3
-    FV(3, 4, 2, 1, 1),    // 128 -> 128, 3x4, 3x3, B=1024
-    FV(2, 4, 2, 2, 1),    // 128 -> 128, 3x4, 3x3, B=16384
+    FV(3, 4, 4, 1, 3, 2), FV(3, 4, 4, 1, 3, 4),    // 59 -> 128, 11x15, 5x5, stride 3
+    FV(3, 4, 2, 1, 1, 2), FV(3, 4, 2, 1, 1, 4),    // 128 -> 128, 3x4, 3x3, B=1024
+    FV(2, 4, 2, 2, 1, 2), FV(2, 4, 2, 2, 1, 4),    // 128 -> 128, 3x4, 3x3, B=16384
 };
 #undef FV
 
@@ -75,7 +77,8 @@ const FusedVariant *pick_fused(const DgradBfPlan &d, const WgradBfPlan &w)
 {
     if (d.NW != 8 || d.GP != 2) return nullptr;
     for (const auto &v : kFusedVariants)
-        if (v.MB == d.MB && v.KS == d.KS && v.TAPS == d.TAPS && v.NBW == d.NBW && v.NSTEP == w.NSTEP)
+        if (v.MB == d.MB && v.KS == d.KS && v.TAPS == d.TAPS && v.NBW == d.NBW &&
+            v.NSTEP == w.NSTEP && v.JW == w.JW)
             return &v;
     return nullptr;
 }
@@ -88,19 +91,23 @@ bool plan_bwd_fused_bf16(const Geom &g, BwdFusedBfPlan &p)
 {
     BwdFusedBfPlan q{};
     if (!plan_dgrad_ig_bf16(g, q.d) || !plan_wgrad_ig_bf16(g, q.w)) return false;
-    if (!pick_fused(q.d, q.w)) return false;
-    q.ws_w_offset = align256(q.d.ws_bytes);
-    q.ws_bytes = q.ws_w_offset + q.w.ws_bytes;
     // One grid for both main kernels gives every workgroup the larger LDS
     // size, which can cut how many d_input workgroups share a CU.  Put them
     // in one launch only when the d_input grid still fits the chip in one
     // round at that size (the small problems, where the saved launch and
     // the overlap of the two tails matter); else launch them one after the
     // other, keeping the merged pre-pass.
-    const size_t lds = std::max(q.d.lds, q.w.lds);
+    // The single grid runs the 8-wave wgrad body, whose tiles are 128 columns
+    WgradBfPlan w128{};
+    const bool have128 = plan_wgrad_bf16_tiles(g, 2, w128);
+    const size_t lds = have128 ? std::max(q.d.lds, w128.lds) : 0;
     const int per_cu = lds ? int((160 * 1024) / lds) : 8;
     const int n_dg = (g.B + q.d.G - 1) / q.d.G * q.d.cgroups;
-    q.fuse_main = n_dg <= g.ncu * std::max(per_cu, 1);
+    q.fuse_main = have128 && n_dg <= g.ncu * std::max(per_cu, 1);
+    if (q.fuse_main) q.w = w128;
+    if (!pick_fused(q.d, q.w)) return false;
+    q.ws_w_offset = align256(q.d.ws_bytes);
+    q.ws_bytes = q.ws_w_offset + q.w.ws_bytes;
     p = q;
     return true;
 }
@@ -118,7 +125,7 @@ hipError_t launch_bwd_fused_bf16(const Geom &g, const BwdFusedBfPlan &p, const v
         d.RP < 16 * d.MB + d.G || d.CC * (d.G / 4) > d.GP * ((64 * d.NW) / g.HW))
         return hipErrorInvalidValue;
     if (2 * wp.CCW * wp.nblk > kWgNT || wp.PP * 128 != wp.NSTEP * kWgNT || g.OC > 128 || g.HW < 8 ||
-        g.OC * g.P * 8 > kDzChunks * kDzNT * 8)
+        kDzOC * g.P > kDzChunks * kDzNT || (p.fuse_main && wp.JW != 2))
         return hipErrorInvalidValue;
     const int total = d.nchunks * d.NBC * d.KS * 64;
     if (size_t(total) * 16 > d.ws_bytes) return hipErrorInvalidValue;
@@ -131,13 +138,13 @@ hipError_t launch_bwd_fused_bf16(const Geom &g, const BwdFusedBfPlan &p, const v
 
     // 1. dz regrouping and d_input weight packing
     const int npack = std::min((total + 255) / 256, 2048);
-    const size_t dz_lds = size_t(2) * 8 * g.OC * g.P * sizeof(u16);
+    const size_t dz_lds = dz_groups_lds(g);
     hipError_t e = allow_max_lds(reinterpret_cast<const void *>(&bwd_prep_bf16));
     if (e == hipSuccess) e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
     if (e == hipSuccess) e = allow_max_lds(reinterpret_cast<const void *>(v->fn_d));
     if (e == hipSuccess) e = allow_max_lds(reinterpret_cast<const void *>(v->fn_w));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_prep_bf16, dim3(wp.ngroups + npack), dim3(kDzNT), dz_lds, s,
+    hipLaunchKernelGGL(bwd_prep_bf16, dim3(wp.ngroups * kDzSlices + npack), dim3(kDzNT), dz_lds, s,
                        (const u16 *)dy, (const u16 *)ym, dzg, g, relu, wp.PP, wp.ngroups,
                        (const u16 *)w, wpk, d.CC, d.NBC, d.KS, total, npack);
     e = hipGetLastError();

@@ -280,8 +280,8 @@ void name_wgrad(const WgradSel &s, char *buf, size_t n, size_t &at)
 {
     switch (s.k) {
     case WgradKind::IgBf16:
-        append(buf, n, at, "wgrad_ws_bf16<NSTEP=%d> ncol=%d splits=%d", s.bf.NSTEP, s.bf.ncol,
-               s.bf.splits);
+        append(buf, n, at, "wgrad_ws_bf16<NSTEP=%d,JW=%d> ncol=%d splits=%d", s.bf.NSTEP, s.bf.JW,
+               s.bf.ncol, s.bf.splits);
         break;
     case WgradKind::RfF32:
         append(buf, n, at, "wgrad_rf_f32<NBWV=%d> chunks=%d splits=%d", s.rf.NBWV, s.rf.chunks,

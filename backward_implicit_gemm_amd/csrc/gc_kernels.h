@@ -83,6 +83,8 @@ hipError_t launch_bwd_fused_bf16(const Geom &g, const BwdFusedBfPlan &p, const v
                                  const void *w, const void *dy, const void *ym, void *dx, void *dw,
                                  void *ws, int relu, hipStream_t s);
 bool plan_wgrad_ig_bf16(const Geom &g, WgradBfPlan &p);
+// the same for one given tile width (64*JW columns)
+bool plan_wgrad_bf16_tiles(const Geom &g, int JW, WgradBfPlan &p);
 // dz regrouping, the partial-tile kernel and the fixed-order reduction into dw
 hipError_t launch_wgrad_ig_bf16(const Geom &g, const WgradBfPlan &p, const void *x, const void *dy,
                                 const void *ym, void *dw, void *ws, int relu, hipStream_t s);

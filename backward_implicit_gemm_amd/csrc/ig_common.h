@@ -222,11 +222,12 @@ struct DgradIgPlan {
 // bf16 wgrad on bf16 MFMA (wgrad_ig_bf16.hip).
 struct WgradBfPlan {
     int NSTEP;    // MFMA steps per 8-image group, PP / 4
+    int JW;       // 16-column blocks per MFMA wave: tiles of 64*JW columns
     int PP;       // output positions padded to a multiple of 4
-    int CCW;      // input channels staged per 128-column tile (widest span)
+    int CCW;      // input channels staged per column tile (widest span)
     int nblk;     // 8-pixel blocks per channel plane
     int HWP;      // LDS pixel slots per staged channel (nblk * 8)
-    int ncol;     // 128-column tiles over IC*KH*KW
+    int ncol;     // column tiles over IC*KH*KW
     int ngroups;  // 8-image groups, ceil(B / 8)
     int gps;      // groups per split
     int splits;   // workgroup rows (partial tiles)

@@ -28,57 +28,69 @@ __device__ __forceinline__ int xslot(int p) { return p + (p >> 3); }
 
 // dzg unit ((bg*PP + p)*128 + oc) = the 8 images of group bg at (oc, p),
 // masked; zero for positions >= P, channels >= OC and images >= B.  One
-// workgroup per group: the group's images are contiguous in dy and y
-// (8*OC*P elements each), so they are copied into LDS with 16-byte loads and
-// transposed there.
+// workgroup per (group, slice of kDzOC output channels): a slice of one image
+// is contiguous in dy and y (kDzOC*P elements), so the group's 8 slices are
+// copied into LDS with 16-byte loads and transposed there.
 constexpr int kDzNT = 256;
-constexpr int kDzChunks = 8;      // 16-byte loads per thread per tensor: 8*OC*P <= 8*256*8
-// The body for group bg; the __global__ wrapper below runs one per workgroup.
+constexpr int kDzOC = 32;               // output channels per workgroup
+constexpr int kDzSlices = 128 / kDzOC;  // workgroups per image group
+constexpr int kDzChunks = 2;            // 16-byte loads per thread per tensor: 8*kDzOC*P/8 <= 2*256
+// The body for unit = group * kDzSlices + slice; the __global__ wrapper
+// below runs one per workgroup.
 __device__ __forceinline__ void dz_groups_bf16_body(const u16 *__restrict__ dy,
                                                     const u16 *__restrict__ ym,
                                                     uint4 *__restrict__ dzg, const Geom &g,
-                                                    int relu, int PP, int bg)
+                                                    int relu, int PP, int unit)
 {
     extern __shared__ __attribute__((aligned(16))) uint4 dz_lds[];
     const int tid = threadIdx.x;
+    const int bg = unit / kDzSlices, oc0 = (unit - bg * kDzSlices) * kDzOC;
     const int nimg = min(8, g.B - bg * 8);
+    const int nloc = max(0, min(kDzOC, g.OC - oc0));   // real channels of the slice
     const int per = g.OC * g.P;                      // elements per image
-    const int m = nimg * per;                        // contiguous elements of the group
-    const uint32_t base = uint32_t(bg) * 8 * per;
-    u16 *sdy = reinterpret_cast<u16 *>(dz_lds);      // [8][per]
-    u16 *sym = sdy + 8 * per;
-    const int m8 = m >> 3;
-    uint4 vd[kDzChunks], vm[kDzChunks];
+    const int L = nloc * g.P;                        // contiguous elements per image slice
+    const int LS = kDzOC * g.P;                      // LDS stride of an image slice
+    const uint32_t base = uint32_t(bg) * 8 * per + uint32_t(oc0) * g.P;
+    u16 *sdy = reinterpret_cast<u16 *>(dz_lds);      // [8][LS]
+    u16 *sym = sdy + 8 * LS;
+    if ((L & 7) == 0) {
+        const int per8 = L >> 3, tot = nimg * per8;
+        uint4 vd[kDzChunks], vm[kDzChunks];
 #pragma unroll
-    for (int k = 0; k < kDzChunks; ++k) {
-        const int c = tid + k * kDzNT;
-        vd[k] = vm[k] = make_uint4(0, 0, 0, 0);
-        if (c < m8) {
-            vd[k] = ldg16(dy + base + 8 * c);
-            if (relu) vm[k] = ldg16(ym + base + 8 * c);
+        for (int k = 0; k < kDzChunks; ++k) {
+            const int c = tid + k * kDzNT;
+            vd[k] = vm[k] = make_uint4(0, 0, 0, 0);
+            if (c < tot) {
+                const int i = c / per8, e = 8 * (c - i * per8);
+                vd[k] = ldg16(dy + base + uint32_t(i) * per + e);
+                if (relu) vm[k] = ldg16(ym + base + uint32_t(i) * per + e);
+            }
         }
-    }
 #pragma unroll
-    for (int k = 0; k < kDzChunks; ++k) {
-        const int c = tid + k * kDzNT;
-        if (c < m8) {
-            __builtin_memcpy(sdy + 8 * c, &vd[k], 16);
-            __builtin_memcpy(sym + 8 * c, &vm[k], 16);
+        for (int k = 0; k < kDzChunks; ++k) {
+            const int c = tid + k * kDzNT;
+            if (c < tot) {
+                const int i = c / per8, e = 8 * (c - i * per8);
+                __builtin_memcpy(sdy + i * LS + e, &vd[k], 16);
+                __builtin_memcpy(sym + i * LS + e, &vm[k], 16);
+            }
         }
-    }
-    for (int e = 8 * m8 + tid; e < m; e += kDzNT) {
-        sdy[e] = dy[base + e];
-        sym[e] = relu ? ym[base + e] : u16(0);
+    } else {
+        for (int c = tid; c < nimg * L; c += kDzNT) {
+            const int i = c / L, e = c - i * L;
+            sdy[i * LS + e] = dy[base + uint32_t(i) * per + e];
+            sym[i * LS + e] = relu ? ym[base + uint32_t(i) * per + e] : u16(0);
+        }
     }
     __syncthreads();
-    for (int u = tid; u < PP * 128; u += kDzNT) {
-        const int p = u >> 7, oc = u & 127;
+    for (int u = tid; u < PP * kDzOC; u += kDzNT) {
+        const int p = u / kDzOC, ol = u - p * kDzOC;
         u16 v[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             u16 d = 0;
-            if (i < nimg && p < g.P && oc < g.OC) {
-                const int e = i * per + oc * g.P + p;
+            if (i < nimg && p < g.P && ol < nloc) {
+                const int e = i * LS + ol * g.P + p;
                 d = sdy[e];
                 if (relu && uint32_t(sym[e]) - 1u >= 0x7F80u) d = 0;   // keep where 0 < y <= +inf
             }
@@ -89,9 +101,11 @@ __device__ __forceinline__ void dz_groups_bf16_body(const u16 *__restrict__ dy,
         o.y = v[2] | (uint32_t(v[3]) << 16);
         o.z = v[4] | (uint32_t(v[5]) << 16);
         o.w = v[6] | (uint32_t(v[7]) << 16);
-        dzg[(uint32_t(bg) * PP + p) * 128 + oc] = o;
+        dzg[(uint32_t(bg) * PP + p) * 128 + oc0 + ol] = o;
     }
 }
+// LDS bytes of one regrouping workgroup
+inline size_t dz_groups_lds(const Geom &g) { return size_t(2) * 8 * kDzOC * g.P * sizeof(u16); }
 __global__ void __launch_bounds__(kDzNT) __attribute__((unused)) dz_groups_bf16(const u16 *__restrict__ dy,
                                                         const u16 *__restrict__ ym,
                                                         uint4 *__restrict__ dzg, Geom g, int relu,
@@ -303,9 +317,10 @@ __device__ __forceinline__ void wgrad_ig_bf16_body(const WgradBfArgs &a, int bid
 // The loaders store stage i+1 (loaded during stage i-1) into the other LDS
 // buffer and issue the loads of stage i+2 while the MFMAs run stage i; one
 // barrier per stage hands the buffers over.
-template <int NSTEP>
+template <int NSTEP, int JW>
 __device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid)
 {
+    constexpr int TW = 64 * JW;       // columns per workgroup tile
     extern __shared__ __attribute__((aligned(16))) uint4 lds4[];
     const Geom &g = a.g;
     const WgradBfPlan &p = a.p;
@@ -313,7 +328,7 @@ __device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid
     const bool loader = wave >= 8;
     const int tid = loader ? int(threadIdx.x) - kWgNT : int(threadIdx.x);   // index within the role
     const int wm = wave & 1;          // output channels 64*wm .. +63
-    const int wn = wave >> 1;         // columns 32*wn .. +31 of the tile
+    const int wn = wave >> 1;         // columns 16*JW*wn .. 16*JW*wn + 16*JW-1 of the tile
     const int N = g.K;                // IC*KH*KW columns
     // Workgroups are dealt to the XCDs round-robin by id; ids are laid out so
     // that all column tiles of one split (one image range) share an XCD,
@@ -321,7 +336,7 @@ __device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid
     const int xcd = bid % g.nxcd, slot = bid / g.nxcd;
     const int split = (slot / p.ncol) * g.nxcd + xcd;
     if (split >= p.splits) return;
-    const int n0 = (slot % p.ncol) * 128;
+    const int n0 = (slot % p.ncol) * TW;
     const int c_lo = n0 / g.KK;
     const int gb = split * p.gps;
     const int ge = min(gb + p.gps, p.ngroups);
@@ -332,13 +347,13 @@ __device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid
     uint4 *ds = lds4 + 2 * xbuf;                  // [2][PP][128]
 
     // ---- per-lane fragment offsets (16-byte units) -------------------------
-    // B (x): column n = n0 + 32*wn + 16*j + lane%16 -> (ic, kh, kw); position
+    // B (x): column n = n0 + 16*JW*wn + 16*j + lane%16 -> (ic, kh, kw); position
     // p = 4*s + lane/16 -> pixel (oh*S, ow*S).  Padded columns and positions
     // read a valid pixel; their dz is zero or their result is not stored.
-    int xcol[2], xpl[2], xrow[NSTEP], drow[NSTEP];
+    int xcol[JW], xpl[JW], xrow[NSTEP], drow[NSTEP];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int n = min(n0 + 32 * wn + 16 * j + (lane & 15), N - 1);
+    for (int j = 0; j < JW; ++j) {
+        const int n = min(n0 + 16 * JW * wn + 16 * j + (lane & 15), N - 1);
         uint32_t ic, kk, kh, kw;
         fdivmod(uint32_t(n), g.fd_KK, ic, kk);
         fdivmod(kk, g.fd_KW, kh, kw);
@@ -354,9 +369,9 @@ __device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid
         xrow[s] = int(oh) * g.S * g.W + int(ow) * g.S;
         drow[s] = pp * 128 + 64 * wm + (lane & 15);
     }
-    int xoff[2][NSTEP];      // LDS slot of this lane's B value per column block and step
+    int xoff[JW][NSTEP];     // LDS slot of this lane's B value per column block and step
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < JW; ++j)
 #pragma unroll
         for (int s = 0; s < NSTEP; ++s) xoff[j][s] = xpl[j] + xslot(xcol[j] + xrow[s]);
 
@@ -416,26 +431,26 @@ __device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid
         for (int k = 0; k < NSTEP; ++k) dd[tid + k * kWgNT] = st.d[k];
     };
 
-    f32x4 acc[4][2];
+    f32x4 acc[4][JW];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < JW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto mfma_stage = [&](int buf) {
         const uint4 *xb = xs + buf * xbuf;
         const uint4 *db = ds + buf * dbuf;
 #pragma unroll
         for (int s = 0; s < NSTEP; ++s) {
-            bf16x8 af[4], bfr[2];
+            bf16x8 af[4], bfr[JW];
 #pragma unroll
             for (int i = 0; i < 4; ++i) af[i] = __builtin_bit_cast(bf16x8, db[drow[s] + 16 * i]);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) bfr[j] = __builtin_bit_cast(bf16x8, xb[xoff[j][s]]);
+            for (int j = 0; j < JW; ++j) bfr[j] = __builtin_bit_cast(bf16x8, xb[xoff[j][s]]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < JW; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
     };
@@ -467,8 +482,8 @@ __device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid
     // ---- partial tile: lane holds rows 4*(lane/16) + v of column lane%16 ----
     float *part = a.part + size_t(split) * g.OC * N;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int n = n0 + 32 * wn + 16 * j + (lane & 15);
+    for (int j = 0; j < JW; ++j) {
+        const int n = n0 + 16 * JW * wn + 16 * j + (lane & 15);
         if (n >= N) continue;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -486,10 +501,10 @@ __global__ void __launch_bounds__(kWgNT) wgrad_ig_bf16(WgradBfArgs a)
     wgrad_ig_bf16_body<NSTEP>(a, blockIdx.x);
 }
 
-template <int NSTEP>
+template <int NSTEP, int JW>
 __global__ void __launch_bounds__(2 * kWgNT) wgrad_ws_bf16(WgradBfArgs a)
 {
-    wgrad_ws_bf16_body<NSTEP>(a, blockIdx.x);
+    wgrad_ws_bf16_body<NSTEP, JW>(a, blockIdx.x);
 }
 
 }  // namespace

@@ -18,9 +18,9 @@ LAYER_SHAPES = {
 # (layer, dtype) -> batch sizes run element by element against the oracle
 LAYER_BATCHES = {
     ("layer1", "f32"): (64, 512, 600, 800, 1024),
-    ("layer1", "bf16"): (64, 512, 600, 800, 1024),
+    ("layer1", "bf16"): (64, 512, 600, 800, 1024, 4096),
     ("layer2", "f32"): (64, 400, 512, 600, 1024, 2048, 4096),
-    ("layer2", "bf16"): (8, 64, 639, 1024, 1227, 1542, 2048, 4096),
+    ("layer2", "bf16"): (8, 64, 639, 1024, 1227, 1542, 2048, 4096, 16384),
 }
 
 # (layer, dtype, op) -> kernel instances (family<compile-time parameters>)
@@ -41,7 +41,7 @@ INSTANCES = {
         "dgrad_ig_bf16<MB=3,KS=4,TAPS=4,NBW=1>",
         "dgrad_ig_bf16<MB=3,KS=4,TAPS=4,NBW=2>",
     },
-    ("layer1", "bf16", "bwd_weight"): {"wgrad_ws_bf16<NSTEP=3>"},
+    ("layer1", "bf16", "bwd_weight"): {"wgrad_ws_bf16<NSTEP=3,JW=2>", "wgrad_ws_bf16<NSTEP=3,JW=4>"},
     ("layer2", "f32", "fwd"): {
         "fwd_ws_f32<NWM=4,MB=1,TS=3,NCG=32,CPP=32>",
         "fwd_ws_f32<NWM=4,MB=1,TS=3,NCG=32,CPP=21>",
@@ -68,7 +68,7 @@ INSTANCES = {
         "dgrad_ig_bf16<MB=3,KS=4,TAPS=2,NBW=2>",
         "dgrad_ig_bf16<MB=4,KS=4,TAPS=2,NBW=1>",
     },
-    ("layer2", "bf16", "bwd_weight"): {"wgrad_ws_bf16<NSTEP=1>"},
+    ("layer2", "bf16", "bwd_weight"): {"wgrad_ws_bf16<NSTEP=1,JW=2>", "wgrad_ws_bf16<NSTEP=1,JW=4>"},
 }
 
 # batch sizes other GPU tests run for these shapes (the workload table at
