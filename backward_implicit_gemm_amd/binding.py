@@ -16,12 +16,13 @@ LIB_PATH = os.path.join(_HERE, "libgc.so")
 GC_OK, GC_ERR_INVALID_ARG, GC_ERR_UNSUPPORTED, GC_ERR_WORKSPACE, GC_ERR_HIP = range(5)
 GC_F32, GC_BF16 = 0, 1
 GC_OP_FWD, GC_OP_BWD_DATA, GC_OP_BWD_WEIGHT, GC_OP_BWD_BIAS, GC_OP_BWD = 0, 1, 2, 3, 4
+GC_OP_BWD_WEIGHT_BIAS = 5
 
 EXPORTED = (
     "gc_conv_out_dims", "gc_conv_workspace_bytes", "gc_conv_fwd", "gc_conv_bwd_data",
     "gc_conv_bwd_weight", "gc_status_string", "gc_fastdiv_selfcheck", "gc_version",
     "gc_set_kernel_policy", "gc_conv_fwd_bias", "gc_conv_bwd_bias", "gc_conv_bwd",
-    "gc_conv_plan_name", "gc_conv_fwd_noalloc",
+    "gc_conv_plan_name", "gc_conv_fwd_noalloc", "gc_conv_bwd_weight_bias",
 )
 GC_POLICY_AUTO, GC_POLICY_GENERIC = 0, 1
 
@@ -65,6 +66,8 @@ def lib():
     L.gc_conv_bwd_data.restype = i
     L.gc_conv_bwd_weight.argtypes = [vp, vp, vp, vp, vp, sz, dp, i, i, vp]
     L.gc_conv_bwd_weight.restype = i
+    L.gc_conv_bwd_weight_bias.argtypes = [vp, vp, vp, vp, vp, vp, sz, dp, i, i, vp]
+    L.gc_conv_bwd_weight_bias.restype = i
     L.gc_conv_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, dp, i, i, vp]
     L.gc_conv_bwd.restype = i
     L.gc_status_string.argtypes = [i]
@@ -271,6 +274,23 @@ def gc_conv_bwd_weight(x, dy, y_mask, dw, relu, stride, workspace, stream=None):
     return dw
 
 
+def gc_conv_bwd_weight_bias(x, dy, y_mask, dw, db, relu, stride, workspace, stream=None):
+    """dw and db together (dy masked by y_mask > 0 when relu) via gc_conv_bwd_weight_bias."""
+    dt = _dtype_code(x)
+    desc = desc_from(x.shape, dw.shape, stride)
+    ys = _y_shape(desc)
+    _expect(dy, "dy", ys)
+    _expect(y_mask, "y_mask", ys)
+    _expect(db, "db", (desc.OC,))
+    wp, wn = _ws(workspace)
+    st = lib().gc_conv_bwd_weight_bias(_dev(x, "x", dt), _dev(dy, "dy", dt),
+                                       _dev(y_mask, "y_mask", dt), _dev(dw, "dw", dt),
+                                       _dev(db, "db", dt), wp, wn, ctypes.byref(desc), int(relu),
+                                       dt, _stream(stream))
+    _check("gc_conv_bwd_weight_bias", st)
+    return dw, db
+
+
 def gc_conv_bwd(x, w, dy, y_mask, dx, dw, relu, stride, workspace, stream=None):
     """dx and dw together (dy masked by y_mask > 0 when relu) via gc_conv_bwd."""
     dt = _dtype_code(x)
@@ -302,7 +322,7 @@ class Conv:
         self.y_shape = (x_shape[0], w_shape[0], OH, OW)
         self.ws = {op: workspace_for(op, self.desc, self.dt, device)
                    for op in (GC_OP_FWD, GC_OP_BWD_DATA, GC_OP_BWD_WEIGHT, GC_OP_BWD_BIAS,
-                              GC_OP_BWD)}
+                              GC_OP_BWD, GC_OP_BWD_WEIGHT_BIAS)}
 
     def fwd(self, x, w, y, stream=None):
         return gc_conv_fwd(x, w, y, self.relu, self.stride, self.ws[GC_OP_FWD], stream)
@@ -321,6 +341,10 @@ class Conv:
 
     def fwd_bias(self, x, w, bias, y, stream=None):
         return gc_conv_fwd_bias(x, w, bias, y, self.relu, self.stride, self.ws[GC_OP_FWD], stream)
+
+    def bwd_weight_bias(self, x, dy, y, dw, db, stream=None):
+        return gc_conv_bwd_weight_bias(x, dy, y if self.relu else None, dw, db, self.relu,
+                                       self.stride, self.ws[GC_OP_BWD_WEIGHT_BIAS], stream)
 
     def bwd_bias(self, dy, y, db, stream=None):
         return gc_conv_bwd_bias(dy, y if self.relu else None, db, self.relu, self.x_shape,

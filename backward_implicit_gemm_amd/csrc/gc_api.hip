@@ -161,6 +161,14 @@ bool wgrad_f32_rf_plan(const Geom &g, WgradRfPlan &p)
 {
     return use_ig() && cached_plan<WgradRfPlan, plan_wgrad_rf_f32>(g, p);
 }
+bool wgrad_bf16_bias_plan(const Geom &g, WgradBfPlan &p)
+{
+    return use_ig() && cached_plan<WgradBfPlan, plan_wgrad_ig_bf16_bias>(g, p);
+}
+bool wgrad_f32_rf_bias_plan(const Geom &g, WgradRfPlan &p)
+{
+    return use_ig() && cached_plan<WgradRfPlan, plan_wgrad_rf_f32_bias>(g, p);
+}
 bool wgrad_plan(const Geom &g, WgradIgPlan &p)
 {
     return use_ig() && cached_plan<std::remove_reference_t<decltype(p)>, plan_wgrad_ig_f32>(g, p);
@@ -222,6 +230,24 @@ WgradSel select_wgrad(const Geom &g, int dtype)
         s.k = WgradKind::Generic;
         s.splits = wgrad_generic_splits(g);
     }
+    return s;
+}
+
+// wgrad with the bias gradient: the bias as one more column of the wgrad
+// tiles where the kernels have it (bf16, and the fp32 image-quad kernel),
+// else wgrad and the separate bias-gradient kernels.
+enum class WgradBiasKind { IgBf16, RfF32, Separate };
+struct WgradBiasSel {
+    WgradBiasKind k;
+    WgradBfPlan bf;
+    WgradRfPlan rf;
+};
+WgradBiasSel select_wgrad_bias(const Geom &g, int dtype)
+{
+    WgradBiasSel s{};
+    if (dtype == GC_BF16 && wgrad_bf16_bias_plan(g, s.bf)) s.k = WgradBiasKind::IgBf16;
+    else if (dtype == GC_F32 && wgrad_f32_rf_bias_plan(g, s.rf)) s.k = WgradBiasKind::RfF32;
+    else s.k = WgradBiasKind::Separate;
     return s;
 }
 
@@ -377,6 +403,13 @@ size_t gc_conv_workspace_bytes(int op, const gc_conv_desc *d, int dtype)
         return size_t(s.splits) * g.OC * g.K * sizeof(float);
     }
     case GC_OP_BWD_BIAS: return bias_grad_ws_bytes(g);
+    case GC_OP_BWD_WEIGHT_BIAS: {
+        const WgradBiasSel s = select_wgrad_bias(g, dtype);
+        if (s.k == WgradBiasKind::IgBf16) return s.bf.ws_bytes;
+        if (s.k == WgradBiasKind::RfF32) return s.rf.ws_bytes;
+        // wgrad's workspace, then the bias gradient's at the next 256-byte boundary
+        return round256(gc_conv_workspace_bytes(GC_OP_BWD_WEIGHT, d, dtype)) + bias_grad_ws_bytes(g);
+    }
     case GC_OP_BWD: {
         BwdFusedBfPlan p;
         if (dtype == GC_BF16 && bwd_fused_plan(g, p)) return p.ws_bytes;
@@ -523,12 +556,12 @@ int gc_conv_bwd_weight(const void *x, const void *dy, const void *y_mask, void *
     if (sel.k == WgradKind::IgBf16) {
         if (!workspace || ws_bytes < sel.bf.ws_bytes) return GC_ERR_WORKSPACE;
         if (reinterpret_cast<uintptr_t>(workspace) % 256) return GC_ERR_WORKSPACE;
-        return hip_status(launch_wgrad_ig_bf16(g, sel.bf, x, dy, y_mask, dw, workspace, relu, s));
+        return hip_status(launch_wgrad_ig_bf16(g, sel.bf, x, dy, y_mask, dw, nullptr, workspace, relu, s));
     }
     if (sel.k == WgradKind::RfF32) {
         if (!workspace || ws_bytes < sel.rf.ws_bytes) return GC_ERR_WORKSPACE;
         if (reinterpret_cast<uintptr_t>(workspace) % 16) return GC_ERR_WORKSPACE;
-        return hip_status(launch_wgrad_rf_f32(g, sel.rf, x, dy, y_mask, dw, workspace, relu, s));
+        return hip_status(launch_wgrad_rf_f32(g, sel.rf, x, dy, y_mask, dw, nullptr, workspace, relu, s));
     }
     const int splits = sel.splits;
     const size_t need = size_t(splits) * g.OC * g.K * sizeof(float);
@@ -547,6 +580,43 @@ int gc_conv_bwd_weight(const void *x, const void *dy, const void *y_mask, void *
         if (e == hipSuccess) e = launch_wgrad_reduce<bf16_t>(part, dw, splits, g.OC * g.K, s);
     }
     return hip_status(e);
+}
+
+int gc_conv_bwd_weight_bias(const void *x, const void *dy, const void *y_mask, void *dw, void *db,
+                            void *workspace, size_t ws_bytes, const gc_conv_desc *d, int relu,
+                            int dtype, void *stream)
+{
+    Geom g;
+    int st = check_desc(d, &g);
+    if (st != GC_OK) return st;
+    if (!valid_dtype(dtype) || (relu != 0 && relu != 1)) return GC_ERR_INVALID_ARG;
+    if (!x || !dy || !dw || !db) return GC_ERR_INVALID_ARG;
+    if ((relu == 1) != (y_mask != nullptr)) return GC_ERR_INVALID_ARG;
+    if (!aligned(x, dtype) || !aligned(dy, dtype) || !aligned(dw, dtype) || !aligned(db, dtype) ||
+        (y_mask && !aligned(y_mask, dtype)))
+        return GC_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const WgradBiasSel sel = select_wgrad_bias(g, dtype);
+    if (sel.k == WgradBiasKind::IgBf16) {
+        if (!workspace || ws_bytes < sel.bf.ws_bytes) return GC_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(workspace) % 256) return GC_ERR_WORKSPACE;
+        return hip_status(launch_wgrad_ig_bf16(g, sel.bf, x, dy, y_mask, dw, db, workspace, relu, s));
+    }
+    if (sel.k == WgradBiasKind::RfF32) {
+        if (!workspace || ws_bytes < sel.rf.ws_bytes) return GC_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(workspace) % 16) return GC_ERR_WORKSPACE;
+        return hip_status(launch_wgrad_rf_f32(g, sel.rf, x, dy, y_mask, dw, db, workspace, relu, s));
+    }
+    // no bias column: wgrad, then the bias gradient, each in its part of the workspace
+    const size_t ww = gc_conv_workspace_bytes(GC_OP_BWD_WEIGHT, d, dtype);
+    const size_t off = round256(ww);
+    const size_t need = off + bias_grad_ws_bytes(g);
+    if (!workspace || ws_bytes < need) return GC_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256) return GC_ERR_WORKSPACE;
+    st = gc_conv_bwd_weight(x, dy, y_mask, dw, ww ? workspace : nullptr, ww, d, relu, dtype, stream);
+    if (st != GC_OK) return st;
+    return gc_conv_bwd_bias(dy, y_mask, db, static_cast<char *>(workspace) + off, ws_bytes - off, d,
+                            relu, dtype, stream);
 }
 
 int gc_conv_bwd(const void *x, const void *w, const void *dy, const void *y_mask, void *dx,
@@ -594,6 +664,23 @@ int gc_conv_plan_name(int op, const gc_conv_desc *d, int dtype, char *buf, size_
     case GC_OP_BWD_DATA: name_dgrad(select_dgrad(g, dtype), buf, buf_bytes, at); break;
     case GC_OP_BWD_WEIGHT: name_wgrad(select_wgrad(g, dtype), buf, buf_bytes, at); break;
     case GC_OP_BWD_BIAS: append(buf, buf_bytes, at, "bias_partials+bias_final"); break;
+    case GC_OP_BWD_WEIGHT_BIAS: {
+        const WgradBiasSel s = select_wgrad_bias(g, dtype);
+        WgradSel w{};
+        if (s.k == WgradBiasKind::IgBf16) {
+            w.k = WgradKind::IgBf16;
+            w.bf = s.bf;
+        } else if (s.k == WgradBiasKind::RfF32) {
+            w.k = WgradKind::RfF32;
+            w.rf = s.rf;
+        } else {
+            w = select_wgrad(g, dtype);
+        }
+        name_wgrad(w, buf, buf_bytes, at);
+        append(buf, buf_bytes, at, s.k == WgradBiasKind::Separate ? " + bias_partials+bias_final"
+                                                                  : " +bias column");
+        break;
+    }
     case GC_OP_BWD: {
         BwdFusedBfPlan fp;
         if (dtype == GC_BF16 && bwd_fused_plan(g, fp)) {

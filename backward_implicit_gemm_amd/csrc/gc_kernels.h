@@ -74,8 +74,12 @@ hipError_t launch_dgrad_rf_f32(const Geom &g, const DgradBfPlan &p, const void *
 // fp32 wgrad with image-quad staging: partial tiles then the fixed-order
 // reduction into dw (fp32 storage only)
 bool plan_wgrad_rf_f32(const Geom &g, WgradRfPlan &p);
+// the same with the bias gradient as one more column (x = 1) of the tiles
+bool plan_wgrad_rf_f32_bias(const Geom &g, WgradRfPlan &p);
+// db (the bias gradient) is written when the plan has the bias column
 hipError_t launch_wgrad_rf_f32(const Geom &g, const WgradRfPlan &p, const void *x, const void *dy,
-                               const void *ym, void *dw, void *ws, int relu, hipStream_t s);
+                               const void *ym, void *dw, void *db, void *ws, int relu,
+                               hipStream_t s);
 // bf16 backward (d_input + wgrad) in three launches: pre-passes, both main
 // kernels in one grid, reduction.  Same results as the separate calls.
 bool plan_bwd_fused_bf16(const Geom &g, BwdFusedBfPlan &p);
@@ -83,11 +87,14 @@ hipError_t launch_bwd_fused_bf16(const Geom &g, const BwdFusedBfPlan &p, const v
                                  const void *w, const void *dy, const void *ym, void *dx, void *dw,
                                  void *ws, int relu, hipStream_t s);
 bool plan_wgrad_ig_bf16(const Geom &g, WgradBfPlan &p);
+// the same with the bias gradient as one more column (x = 1) of the tiles
+bool plan_wgrad_ig_bf16_bias(const Geom &g, WgradBfPlan &p);
 // the same for one given tile width (64*JW columns)
-bool plan_wgrad_bf16_tiles(const Geom &g, int JW, WgradBfPlan &p);
+bool plan_wgrad_bf16_tiles(const Geom &g, int JW, WgradBfPlan &p, int bias = 0);
 // dz regrouping, the partial-tile kernel and the fixed-order reduction into dw
 hipError_t launch_wgrad_ig_bf16(const Geom &g, const WgradBfPlan &p, const void *x, const void *dy,
-                                const void *ym, void *dw, void *ws, int relu, hipStream_t s);
+                                const void *ym, void *dw, void *db, void *ws, int relu,
+                                hipStream_t s);
 hipError_t launch_dgrad_ig_bf16(const Geom &g, const DgradBfPlan &p, const void *dy, const void *w,
                                 const void *ym, void *dx, void *ws, int relu, hipStream_t s);
 
@@ -95,5 +102,10 @@ hipError_t launch_dgrad_ig_bf16(const Geom &g, const DgradBfPlan &p, const void 
 // (wgrad_reduce.hip).
 template <typename T>
 hipError_t launch_wgrad_reduce(const float *part, void *dw, int splits, int n, hipStream_t s);
+// The same over partial rows of NP columns: columns 0..N-1 of row oc go to
+// dw[oc][...], column N to db[oc], the rest (padding) nowhere.
+template <typename T>
+hipError_t launch_wgrad_reduce_bias(const float *part, void *dw, void *db, int splits, int OC, int N,
+                                    int NP, hipStream_t s);
 
 }  // namespace gc

@@ -223,6 +223,8 @@ struct DgradIgPlan {
 struct WgradBfPlan {
     int NSTEP;    // MFMA steps per 8-image group, PP / 4
     int JW;       // 16-column blocks per MFMA wave: tiles of 64*JW columns
+    int bias;     // also the bias gradient: column K of the tiles, with x = 1
+    int NP;       // columns per partial row: K, or K+1 rounded up to 4 with the bias
     int PP;       // output positions padded to a multiple of 4
     int CCW;      // input channels staged per column tile (widest span)
     int nblk;     // 8-pixel blocks per channel plane
@@ -233,7 +235,7 @@ struct WgradBfPlan {
     int splits;   // workgroup rows (partial tiles)
     size_t lds;       // double-buffered x and dz stages
     size_t dz_bytes;  // regrouped dz at the front of the workspace
-    size_t ws_bytes;  // dz_bytes + splits * OC * K fp32 partials
+    size_t ws_bytes;  // dz_bytes + splits * OC * NP fp32 partials
 };
 
 // fp32 wgrad with image-quad staging (wgrad_rf_f32.hip).
@@ -254,8 +256,10 @@ struct WgradRfPlan {
     int WP, IS;   // x LDS slots per pixel row / per channel
     int OCP;      // dz LDS slots per output position (>= OC)
     int bufsz;    // 16-byte slots per LDS buffer (x, dz, one zero slot)
+    int bias;     // also the bias gradient: column K of the tiles, with x = 1
+    int NP;       // columns per partial row: K, or K+1 rounded up to 4 with the bias
     size_t lds;
-    size_t ws_bytes;   // splits * OC * K fp32 partials
+    size_t ws_bytes;   // splits * OC * NP fp32 partials
 };
 
 struct WgradIgPlan {

@@ -51,18 +51,19 @@ const WgradBfVariant *pick_wgrad_bf(int nstep, int jw)
 // of splits trades MFMA parallelism (at least ~one workgroup per CU) against
 // the fp32 partial traffic (splits x OC x K x 4 bytes, written and read
 // back once).
-bool plan_wgrad_bf16_tiles(const Geom &g, int JW, WgradBfPlan &p)
+bool plan_wgrad_bf16_tiles(const Geom &g, int JW, WgradBfPlan &p, int bias)
 {
     if (g.OC > 128 || g.P > 16 || g.HW < 8) return false;
     const int PP = (g.P + 3) / 4 * 4;
     const int NSTEP = PP / 4;
     if (!pick_wgrad_bf(NSTEP, JW)) return false;
     const int N = g.K, TW = 64 * JW;
-    const int ncol = (N + TW - 1) / TW;
+    const int ncol = (N + bias + TW - 1) / TW;     // the bias is column N
     // widest channel span of any tile
     int CCW = 0;
     for (int t = 0; t < ncol; ++t) {
-        const int lo = t * TW / g.KK, hi = std::min(g.IC - 1, (std::min(N, t * TW + TW) - 1) / g.KK);
+        const int lo = std::min(t * TW, N - 1) / g.KK;
+        const int hi = std::min(g.IC - 1, (std::min(N, t * TW + TW) - 1) / g.KK);
         CCW = std::max(CCW, hi - lo + 1);
     }
     const int nblk = (g.HW + 7) / 8;
@@ -76,18 +77,20 @@ bool plan_wgrad_bf16_tiles(const Geom &g, int JW, WgradBfPlan &p)
     // traffic stays small against the operand traffic
     int splits = std::max(1, std::min(ngroups, (g.ncu + ncol - 1) / ncol));
     if (splits > g.nxcd) splits = splits / g.nxcd * g.nxcd;
-    const double part_bytes = double(g.OC) * N * 4;
+    const int NP = bias ? (N + 1 + 3) / 4 * 4 : N;
+    const double part_bytes = double(g.OC) * NP * 4;
     const double in_bytes = double(g.B) * g.IC * g.HW * 2;
     const double budget = std::max(0.75 * in_bytes, 12.0 * 1024 * 1024);
     while (splits > g.nxcd && splits * part_bytes > budget) splits -= g.nxcd;
     while (splits > 1 && splits <= g.nxcd && splits * part_bytes > budget) --splits;
     const int gps = (ngroups + splits - 1) / splits;
     splits = (ngroups + gps - 1) / gps;
-    p.NSTEP = NSTEP; p.JW = JW; p.PP = PP; p.CCW = CCW; p.nblk = nblk; p.HWP = HWP;
+    p.NSTEP = NSTEP; p.JW = JW; p.bias = bias; p.NP = NP;
+    p.PP = PP; p.CCW = CCW; p.nblk = nblk; p.HWP = HWP;
     p.ncol = ncol; p.ngroups = ngroups; p.gps = gps; p.splits = splits;
     p.lds = lds;
     p.dz_bytes = (size_t(ngroups) * PP * 128 * 16 + 255) / 256 * 256;
-    p.ws_bytes = p.dz_bytes + size_t(splits) * g.OC * N * 4;
+    p.ws_bytes = p.dz_bytes + size_t(splits) * g.OC * NP * 4;
     return true;
 }
 
@@ -98,19 +101,23 @@ bool plan_wgrad_bf16_tiles(const Geom &g, int JW, WgradBfPlan &p)
 // per group.  They are taken when their grid covers the CUs (the chain's
 // B=16384: conv1 wgrad 184 -> 144 us, conv2 67 -> 51 us); below that (B=1024:
 // 96 workgroups, 26.8 -> 30.2 us) the 128-column tiles run.
-bool plan_wgrad_ig_bf16(const Geom &g, WgradBfPlan &p)
+static bool plan_wgrad_bf16(const Geom &g, WgradBfPlan &p, int bias)
 {
     WgradBfPlan q{};
-    if (plan_wgrad_bf16_tiles(g, 4, q) && 10 * q.ncol * q.splits >= 9 * g.ncu) {
+    if (plan_wgrad_bf16_tiles(g, 4, q, bias) && 10 * q.ncol * q.splits >= 9 * g.ncu) {
         p = q;
         return true;
     }
-    return plan_wgrad_bf16_tiles(g, 2, p);
+    return plan_wgrad_bf16_tiles(g, 2, p, bias);
 }
 
+bool plan_wgrad_ig_bf16(const Geom &g, WgradBfPlan &p) { return plan_wgrad_bf16(g, p, 0); }
+bool plan_wgrad_ig_bf16_bias(const Geom &g, WgradBfPlan &p) { return plan_wgrad_bf16(g, p, 1); }
+
 hipError_t launch_wgrad_ig_bf16(const Geom &g, const WgradBfPlan &p, const void *x, const void *dy,
-                                const void *ym, void *dw, void *ws, int relu, hipStream_t s)
+                                const void *ym, void *dw, void *db, void *ws, int relu, hipStream_t s)
 {
+    if (p.bias && !db) return hipErrorInvalidValue;
     hipError_t e;
     const WgradBfVariant *v = pick_wgrad_bf(p.NSTEP, p.JW);
     if (!v || 2 * p.CCW * p.nblk > kWgNT || p.PP * 128 != p.NSTEP * kWgNT || g.OC > 128 || g.HW < 8)
@@ -132,6 +139,7 @@ hipError_t launch_wgrad_ig_bf16(const Geom &g, const WgradBfPlan &p, const void 
     hipLaunchKernelGGL(v->fn, dim3(g.nxcd * slots), dim3(2 * kWgNT), p.lds, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (p.bias) return launch_wgrad_reduce_bias<bf16_t>(part, dw, db, p.splits, g.OC, g.K, p.NP, s);
     return launch_wgrad_reduce<bf16_t>(part, dw, p.splits, g.OC * g.K, s);
 }
 

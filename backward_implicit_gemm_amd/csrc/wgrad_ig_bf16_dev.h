@@ -337,7 +337,8 @@ __device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid
     const int split = (slot / p.ncol) * g.nxcd + xcd;
     if (split >= p.splits) return;
     const int n0 = (slot % p.ncol) * TW;
-    const int c_lo = n0 / g.KK;
+    // (a tile holding only the bias column stages channel IC-1, unused)
+    const int c_lo = min(n0, N - 1) / g.KK;
     const int gb = split * p.gps;
     const int ge = min(gb + p.gps, p.ngroups);
 
@@ -351,8 +352,10 @@ __device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid
     // p = 4*s + lane/16 -> pixel (oh*S, ow*S).  Padded columns and positions
     // read a valid pixel; their dz is zero or their result is not stored.
     int xcol[JW], xpl[JW], xrow[NSTEP], drow[NSTEP];
+    bool ones[JW];        // the bias column: B is 1 for every image
 #pragma unroll
     for (int j = 0; j < JW; ++j) {
+        ones[j] = p.bias && n0 + 16 * JW * wn + 16 * j + (lane & 15) == N;
         const int n = min(n0 + 16 * JW * wn + 16 * j + (lane & 15), N - 1);
         uint32_t ic, kk, kh, kw;
         fdivmod(uint32_t(n), g.fd_KK, ic, kk);
@@ -446,7 +449,10 @@ __device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid
 #pragma unroll
             for (int i = 0; i < 4; ++i) af[i] = __builtin_bit_cast(bf16x8, db[drow[s] + 16 * i]);
 #pragma unroll
-            for (int j = 0; j < JW; ++j) bfr[j] = __builtin_bit_cast(bf16x8, xb[xoff[j][s]]);
+            for (int j = 0; j < JW; ++j)
+                bfr[j] = __builtin_bit_cast(bf16x8, ones[j] ? make_uint4(0x3F803F80u, 0x3F803F80u,
+                                                                         0x3F803F80u, 0x3F803F80u)
+                                                            : xb[xoff[j][s]]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -480,17 +486,19 @@ __device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid
     }
 
     // ---- partial tile: lane holds rows 4*(lane/16) + v of column lane%16 ----
-    float *part = a.part + size_t(split) * g.OC * N;
+    // columns K+bias .. NP-1 (row padding) are written as zeros
+    float *part = a.part + size_t(split) * g.OC * p.NP;
 #pragma unroll
     for (int j = 0; j < JW; ++j) {
         const int n = n0 + 16 * JW * wn + 16 * j + (lane & 15);
-        if (n >= N) continue;
+        if (n >= p.NP) continue;
+        const bool real = n < N + p.bias;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int oc = 64 * wm + 16 * i + 4 * (lane >> 4) + v;
-                if (oc < g.OC) part[uint32_t(oc) * N + n] = acc[i][j][v];
+                if (oc < g.OC) part[uint32_t(oc) * p.NP + n] = real ? acc[i][j][v] : 0.f;
             }
     }
 }

@@ -43,7 +43,7 @@ __device__ __forceinline__ float comp(const float4 &v, int i)
 }
 
 
-template <int NBWV, bool RELU>
+template <int NBWV, bool RELU, bool BIAS>
 __global__ void __launch_bounds__(1024) wgrad_rf_f32(WgradRfArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) float4 lds4w[];
@@ -66,7 +66,8 @@ __global__ void __launch_bounds__(1024) wgrad_rf_f32(WgradRfArgs a)
     const int qe = min(p.NQ, qs + p.QPS);
     const int nph = qe > qs ? (qe - qs + p.QB - 1) / p.QB : 0;
     const int col0 = chunk * p.NBW * 16;
-    const int c_lo = int(fdiv(uint32_t(col0), g.fd_KK));
+    // (a chunk holding only the bias column stages channel IC-1, unused)
+    const int c_lo = int(fdiv(uint32_t(min(col0, g.K - 1)), g.fd_KK));
     const int c_hi = min(g.IC - 1, int(fdiv(uint32_t(min(g.K, col0 + p.NBW * 16) - 1), g.fd_KK)));
     const int QX = p.CCS * p.IS, QD = g.P * p.OCP;  // LDS slots per quad: x, dz
     const int xsz = p.QB * QX;                      // x slots of a buffer
@@ -145,9 +146,11 @@ __global__ void __launch_bounds__(1024) wgrad_rf_f32(WgradRfArgs a)
     const int mblk = wave % p.MBLK, nsub = wave / p.MBLK;
     const int oc_a = mblk * 16 + (lane & 15);            // A row of this lane
     int coloff[NBWV];
+    bool ones[NBWV];      // the bias column: B is 1 for every image
 #pragma unroll
     for (int nb = 0; nb < NBWV; ++nb) {
         const int col = col0 + (nsub * NBWV + nb) * 16 + (lane & 15);
+        ones[nb] = BIAS && col == g.K;
         coloff[nb] = 0;
         if (col < g.K) {
             uint32_t ic, t, kh, kw;
@@ -208,7 +211,9 @@ __global__ void __launch_bounds__(1024) wgrad_rf_f32(WgradRfArgs a)
                     const float4 av = buf[drow[s]];
                     float4 bv[NBWV];
 #pragma unroll
-                    for (int nb = 0; nb < NBWV; ++nb) bv[nb] = buf[xrow[s] + coloff[nb]];
+                    for (int nb = 0; nb < NBWV; ++nb)
+                        bv[nb] = BIAS && ones[nb] ? make_float4(1.f, 1.f, 1.f, 1.f)
+                                                  : buf[xrow[s] + coloff[nb]];
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -221,17 +226,19 @@ __global__ void __launch_bounds__(1024) wgrad_rf_f32(WgradRfArgs a)
         __syncthreads();
     }
 
-    // partial tile: C row 4*(lane/16) + v is oc, column lane%16 is k
+    // partial tile: C row 4*(lane/16) + v is oc, column lane%16 is k;
+    // columns K+bias .. NP-1 (row padding) are written as zeros
     if (wave_on) {
-        float *out = a.part + size_t(split) * g.OC * g.K;
+        float *out = a.part + size_t(split) * g.OC * p.NP;
 #pragma unroll
         for (int nb = 0; nb < NBWV; ++nb) {
             const int col = col0 + (nsub * NBWV + nb) * 16 + (lane & 15);
-            if (col >= g.K) continue;
+            if (col >= p.NP) continue;
+            const bool real = col < g.K + p.bias;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int oc = mblk * 16 + 4 * (lane >> 4) + v;
-                if (oc < g.OC) out[size_t(oc) * g.K + col] = acc[nb][v];
+                if (oc < g.OC) out[size_t(oc) * p.NP + col] = real ? acc[nb][v] : 0.f;
             }
         }
     }
@@ -239,10 +246,12 @@ __global__ void __launch_bounds__(1024) wgrad_rf_f32(WgradRfArgs a)
 
 struct WgradRfVariant {
     int NBWV;
-    void (*fn)(WgradRfArgs);       // without ReLU
-    void (*fn_relu)(WgradRfArgs);  // dz masked by y > 0
+    void (*fn[2][2])(WgradRfArgs);   // [relu: dz masked by y > 0][bias column]
 };
-#define WR_V(N) {N, wgrad_rf_f32<N, false>, wgrad_rf_f32<N, true>}
+#define WR_V(N)                                                                     \
+    {N,                                                                             \
+     {{wgrad_rf_f32<N, false, false>, wgrad_rf_f32<N, false, true>},                \
+      {wgrad_rf_f32<N, true, false>, wgrad_rf_f32<N, true, true>}}}
 const WgradRfVariant kWgradRfVariants[] = {WR_V(2), WR_V(3), WR_V(4), WR_V(6), WR_V(8)};
 #undef WR_V
 
@@ -286,7 +295,7 @@ static int x_read_conflicts(const Geom &g, const WgradRfPlan &q, int WP, int IS)
     return cost;
 }
 
-bool plan_wgrad_rf_f32(const Geom &g, WgradRfPlan &p)
+static bool plan_wgrad_rf_impl(const Geom &g, WgradRfPlan &p, int bias)
 {
     const int MBLK = (g.OC + 15) / 16;
     if (MBLK > 8) return false;
@@ -298,7 +307,8 @@ bool plan_wgrad_rf_f32(const Geom &g, WgradRfPlan &p)
         (2 * size_t(g.B) + 128) * g.OC * g.P * 4 >= (size_t(1) << 32))
         return false;
     const int WN = MBLK == 1 ? 8 : MBLK == 2 ? 4 : MBLK <= 4 ? 2 : 1;
-    const int NBT = (g.K + 15) / 16;
+    const int NC = g.K + bias;              // computed columns
+    const int NBT = (NC + 15) / 16;
     const int NQ = (g.B + 3) / 4;
     double best = 1e300;
     for (const auto &v : kWgradRfVariants) {
@@ -306,10 +316,13 @@ bool plan_wgrad_rf_f32(const Geom &g, WgradRfPlan &p)
         q.NBWV = v.NBWV; q.MBLK = MBLK; q.WN = WN; q.NBW = WN * v.NBWV;
         q.chunks = (NBT + q.NBW - 1) / q.NBW;
         q.NQ = NQ;
+        q.bias = bias;
+        q.NP = bias ? (g.K + 1 + 3) / 4 * 4 : g.K;
         q.CCS = 0;
         int min_span = 1 << 30;
         for (int c = 0; c < q.chunks; ++c) {
-            const int lo = c * q.NBW * 16, hi = std::min(g.K, (c + 1) * q.NBW * 16) - 1;
+            const int lo = std::min(c * q.NBW * 16, g.K - 1);
+            const int hi = std::min(g.K, (c + 1) * q.NBW * 16) - 1;
             q.CCS = std::max(q.CCS, hi / g.KK - lo / g.KK + 1);
             min_span = std::min(min_span, hi / g.KK - lo / g.KK + 1);
         }
@@ -331,7 +344,7 @@ bool plan_wgrad_rf_f32(const Geom &g, WgradRfPlan &p)
         // the smallest (independent of the batch size, so searched once per
         // layer shape and variant)
         static SearchMemo<std::pair<int, int>> memo;
-        const int key[12] = {g.IC, g.H, g.W, g.OC, g.KH, g.KW, g.S, q.NBWV, q.QB, q.CCS, 0, 0};
+        const int key[12] = {g.IC, g.H, g.W, g.OC, g.KH, g.KW, g.S, q.NBWV, q.QB, q.CCS, bias, 0};
         const std::pair<int, int> pitch = memo.get(key, [&] {
             int bc = 1 << 30, bw = g.W, bi = g.H * g.W;
             for (int WP = g.W; WP < g.W + 16; ++WP)
@@ -364,9 +377,9 @@ bool plan_wgrad_rf_f32(const Geom &g, WgradRfPlan &p)
         // and stash, plus ~200 for the barrier
         const double phase = std::max(2.0 * 4 * q.NBWV * q.SPP * 32, 3000.0) + 200.0;
         const double wg_cycles = nph * phase;
-        const double part_bytes = 2.0 * q.splits * g.OC * double(g.K) * 4;
+        const double part_bytes = 2.0 * q.splits * g.OC * double(q.NP) * 4;
         const double cost = rounds * wg_cycles + part_bytes / 5e12 * 2.4e9;
-        q.ws_bytes = size_t(q.splits) * g.OC * g.K * sizeof(float);
+        q.ws_bytes = size_t(q.splits) * g.OC * q.NP * sizeof(float);
         if (cost < best) {
             best = cost;
             p = q;
@@ -375,21 +388,26 @@ bool plan_wgrad_rf_f32(const Geom &g, WgradRfPlan &p)
     return best < 1e300;
 }
 
+bool plan_wgrad_rf_f32(const Geom &g, WgradRfPlan &p) { return plan_wgrad_rf_impl(g, p, 0); }
+bool plan_wgrad_rf_f32_bias(const Geom &g, WgradRfPlan &p) { return plan_wgrad_rf_impl(g, p, 1); }
+
 hipError_t launch_wgrad_rf_f32(const Geom &g, const WgradRfPlan &p, const void *x, const void *dy,
-                               const void *ym, void *dw, void *ws, int relu, hipStream_t s)
+                               const void *ym, void *dw, void *db, void *ws, int relu, hipStream_t s)
 {
+    if (p.bias && !db) return hipErrorInvalidValue;
     const WgradRfVariant *v = pick_wgrad_rf(p.NBWV);
     if (!v || p.QB * p.XU > 512 || p.QB * p.DU > 512 || p.SPP > kSppMax)
         return hipErrorInvalidValue;
     if (reinterpret_cast<uintptr_t>(ws) % 16) return hipErrorInvalidValue;
     WgradRfArgs a{g, (const float *)x, (const float *)dy, (const float *)ym, (float *)ws, relu, p};
-    void (*fn)(WgradRfArgs) = relu ? v->fn_relu : v->fn;
+    void (*fn)(WgradRfArgs) = v->fn[relu ? 1 : 0][p.bias ? 1 : 0];
     hipError_t e = allow_max_lds(reinterpret_cast<const void *>(fn));
     if (e != hipSuccess) return e;
     const int grid = g.nxcd * ((p.splits + g.nxcd - 1) / g.nxcd) * p.chunks;
     hipLaunchKernelGGL(fn, dim3(grid), dim3(1024), p.lds, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (p.bias) return launch_wgrad_reduce_bias<float>((const float *)ws, dw, db, p.splits, g.OC, g.K, p.NP, s);
     return launch_wgrad_reduce<float>((const float *)ws, dw, p.splits, g.OC * g.K, s);
 }
 

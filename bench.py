@@ -304,6 +304,9 @@ def run_gpu(wl, steps, warmup, x_scale=1.0, extras=True):
         yb = torch.empty_like(ys[i])
         bias_calls.append((f"fwd_bias{i + 1}", lambda c=c, i=i, b=b, yb=yb: c.fwd_bias(xs[i], ws[i], b, yb)))
         bias_calls.append((f"bwd_bias{i + 1}", lambda c=c, i=i, db=db: c.bwd_bias(dys[i], ys[i], db)))
+        dwb = torch.empty_like(dws[i])
+        bias_calls.append((f"wgrad_bias{i + 1}",
+                           lambda c=c, i=i, db=db, dwb=dwb: c.bwd_weight_bias(xs[i], dys[i], ys[i], dwb, db)))
     bias_us = {}
     for name, f in (bias_calls if extras else []):
         f()

@@ -71,7 +71,8 @@ typedef enum {
     GC_OP_BWD_DATA = 1,     /* gc_conv_bwd_data */
     GC_OP_BWD_WEIGHT = 2,   /* gc_conv_bwd_weight */
     GC_OP_BWD_BIAS = 3,     /* gc_conv_bwd_bias */
-    GC_OP_BWD = 4           /* gc_conv_bwd */
+    GC_OP_BWD = 4,          /* gc_conv_bwd */
+    GC_OP_BWD_WEIGHT_BIAS = 5   /* gc_conv_bwd_weight_bias */
 } gc_op;
 
 /* Problem size.  No padding, dilation 1, one group. */
@@ -141,6 +142,20 @@ int gc_conv_bwd_data(const void *dy, const void *w, const void *y_mask, void *dx
 int gc_conv_bwd_weight(const void *x, const void *dy, const void *y_mask, void *dw,
                        void *workspace, size_t ws_bytes,
                        const gc_conv_desc *d, int relu, int dtype, void *stream);
+
+/* wgrad and the bias gradient together: dw as gc_conv_bwd_weight computes it
+ * and db[oc] = sum_{b,oh,ow} dz[b,oc,oh,ow] as gc_conv_bwd_bias does (db [OC]
+ * in the storage type; dz = dy masked by y_mask > 0 when relu == 1).  The PR
+ * page times the bias gradient as a kernel of its own (its bias-grad lines);
+ * here db is one more column of the wgrad tiles, whose x operand is 1, so
+ * it is summed from the dz already staged for wgrad and finished by the same
+ * fixed-order reduction (bit-identical from run to run).  Shapes whose wgrad
+ * kernel has no such column run gc_conv_bwd_weight and gc_conv_bwd_bias.
+ * Workspace: gc_conv_workspace_bytes(GC_OP_BWD_WEIGHT_BIAS, ...), 256-byte
+ * aligned.  db must not be NULL. */
+int gc_conv_bwd_weight_bias(const void *x, const void *dy, const void *y_mask, void *dw,
+                            void *db, void *workspace, size_t ws_bytes,
+                            const gc_conv_desc *d, int relu, int dtype, void *stream);
 
 /* The whole backward of a layer in one call: dx as gc_conv_bwd_data and dw
  * as gc_conv_bwd_weight compute them, with the same arguments and the same

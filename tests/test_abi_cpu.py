@@ -304,3 +304,17 @@ def test_noalloc_forward_rejects_before_any_launch():
         for shape in ((59, 11, 15, 128, 5, 5, 3), (128, 3, 4, 128, 3, 3, 1)):
             for dt in (gb.GC_F32, gb.GC_BF16):
                 assert gb.gc_conv_workspace_bytes(gb.GC_OP_FWD, gb.make_desc(B, *shape), dt) <= (2 << 20)
+
+
+def test_wgrad_bias_argument_errors():
+    L = gb.lib()
+    call = lambda *p, relu=1, dt=0, ws=None, wsb=0: L.gc_conv_bwd_weight_bias(
+        *p, ws, wsb, ctypes.byref(L1), relu, dt, None)
+    assert call(FAKE, FAKE, FAKE, FAKE, None) == gb.GC_ERR_INVALID_ARG          # db NULL
+    assert call(FAKE, FAKE, None, FAKE, FAKE) == gb.GC_ERR_INVALID_ARG          # relu without mask
+    assert call(FAKE, FAKE, FAKE, FAKE, FAKE, relu=0) == gb.GC_ERR_INVALID_ARG  # mask without relu
+    assert call(FAKE, FAKE, FAKE, FAKE, FAKE) == gb.GC_ERR_WORKSPACE            # no workspace
+    for dt in (gb.GC_F32, gb.GC_BF16):
+        n = gb.gc_conv_workspace_bytes(gb.GC_OP_BWD_WEIGHT_BIAS, L1, dt)
+        assert n >= gb.gc_conv_workspace_bytes(gb.GC_OP_BWD_WEIGHT, L1, dt) > 0
+        assert "bias column" in gb.gc_conv_plan_name(gb.GC_OP_BWD_WEIGHT_BIAS, L1, dt)

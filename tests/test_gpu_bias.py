@@ -131,3 +131,97 @@ def test_bias_bf16_several_groups_per_workgroup(shape):
     b = _bias(layer, 78, "bf16")
     ey, eb, _, _ = _check(layer, "bf16", x, w, b, dy)
     print(f"{shape}: y(bias)={ey:.2e} db={eb:.2e}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# gc_conv_bwd_weight_bias: dw and db from one wgrad pass (db as the wgrad
+# tiles' extra column with x = 1), against the oracle and against the two
+# separate calls
+# ---------------------------------------------------------------------------
+
+def _wb(layer, dtype, x, dy, seeds_y):
+    dev = "cuda"
+    td = inputs.torch_dtype(dtype)
+    conv = gb.Conv(layer.x_shape, layer.w_shape, layer.stride, layer.relu, td, dev)
+    xd, dyd = x.to(dev), dy.to(dev)
+    # a ReLU mask from a forward pass of random weights
+    w = inputs.uniform(layer.w_shape, seeds_y, 1.0 / np.sqrt(layer.IC * layer.KH * layer.KW), dtype)
+    y = torch.empty(layer.y_shape, dtype=td, device=dev)
+    conv.fwd(xd, w.to(dev), y)
+    from parity import Guarded
+    gdw, gdb = Guarded(layer.w_shape, td, dev), Guarded((layer.OC,), td, dev)
+    conv.bwd_weight_bias(xd, dyd, y, gdw.t, gdb.t)
+    dw2 = torch.empty_like(gdw.t)
+    db2 = torch.empty_like(gdb.t)
+    conv.bwd_weight(xd, dyd, y, dw2)
+    conv.bwd_bias(dyd, y, db2)
+    torch.cuda.synchronize()
+    gdw.check("dw")
+    gdb.check("db")
+    return conv, y, gdw.t, gdb.t, dw2, db2
+
+
+WB_SHAPES = [
+    # the two layer shapes at the batches that run 128- and 256-column wgrad
+    # tiles, ragged and odd shapes (some without a bias column: separate calls)
+    (1024, 59, 11, 15, 128, 5, 5, 3, 1), (1024, 128, 3, 4, 128, 3, 3, 1, 0),
+    (16384, 59, 11, 15, 128, 5, 5, 3, 1), (16384, 128, 3, 4, 128, 3, 3, 1, 0),
+    (37, 128, 3, 4, 96, 3, 3, 1, 1), (9, 59, 11, 15, 128, 5, 5, 3, 0),
+    (3, 3, 7, 8, 4, 3, 3, 2, 1), (5, 7, 6, 6, 130, 6, 6, 1, 0),
+]
+
+
+@pytest.mark.parametrize("shape", WB_SHAPES, ids=["x".join(map(str, s)) for s in WB_SHAPES])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_wgrad_with_bias_column(shape, dtype):
+    layer = Layer(*shape)
+    d = gb.make_desc(*shape[:8])
+    name = gb.gc_conv_plan_name(gb.GC_OP_BWD_WEIGHT_BIAS, d,
+                                gb.GC_F32 if dtype == "f32" else gb.GC_BF16)
+    x, _, dy = draw(layer, (shape[0] + 3, 4, 5), dtype)
+    _, y, dw, db, dw2, db2 = _wb(layer, dtype, x, dy, 6)
+    ym = f64(y) if layer.relu else None
+    dw_ref = orc.conv_bwd_weight(f64(x), f64(dy), ym, layer.w_shape, layer.stride, layer.relu)
+    db_ref = orc.conv_bwd_bias(f64(dy), ym, layer.relu)
+    ew, eb = rel_err(f64(dw), dw_ref), rel_err(f64(db), db_ref)
+    print(f"{shape} {dtype} [{name}]: dw={ew:.2e} db={eb:.2e}", flush=True)
+    assert ew <= TOL[dtype] and eb <= TOL[dtype], (ew, eb)
+    # with the same splits, the same dw as gc_conv_bwd_weight bit for bit
+    # (same kernel and summation order, one more column)
+    plain = gb.gc_conv_plan_name(gb.GC_OP_BWD_WEIGHT, d, gb.GC_F32 if dtype == "f32" else gb.GC_BF16)
+    splits = lambda n: n.split("splits=")[1].split()[0]
+    if "bias column" not in name:
+        assert torch.equal(dw, dw2) and torch.equal(db, db2)
+    elif splits(name) == splits(plain):
+        view = torch.int16 if dtype == "bf16" else torch.int32
+        assert torch.equal(dw.view(view), dw2.view(view))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_wgrad_with_bias_column_integer_exact(dtype):
+    # integer inputs: every partial sum is exact, so db and dw must equal the
+    # rounded exact results whatever the order
+    layer = Layer(1024, 59, 11, 15, 128, 5, 5, 3, 1)
+    x = inputs.integers(layer.x_shape, 41, dtype=dtype)
+    dy = inputs.integers(layer.y_shape, 42, dtype=dtype)
+    _, y, dw, db, _, _ = _wb(layer, dtype, x, dy, 43)
+    ym = f64(y)
+    dw_ref = orc.conv_bwd_weight(f64(x), f64(dy), ym, layer.w_shape, layer.stride, 1)
+    db_ref = orc.conv_bwd_bias(f64(dy), ym, 1)
+    td = inputs.torch_dtype(dtype)
+    rne = lambda a: torch.from_numpy(a).to(torch.float32).to(td).to(torch.float64).numpy()
+    assert np.array_equal(f64(dw), rne(dw_ref))
+    assert np.array_equal(f64(db), rne(db_ref))
+
+
+def test_wgrad_with_bias_column_deterministic():
+    layer = Layer(1024, 59, 11, 15, 128, 5, 5, 3, 1)
+    x, _, dy = draw(layer, (7, 8, 9), "bf16")
+    conv, y, dw, db, _, _ = _wb(layer, "bf16", x, dy, 10)
+    xd, dyd = x.cuda(), dy.cuda()
+    for _ in range(3):
+        dw2, db2 = torch.empty_like(dw), torch.empty_like(db)
+        conv.bwd_weight_bias(xd, dyd, y, dw2, db2)
+        torch.cuda.synchronize()
+        assert torch.equal(dw2.view(torch.int16), dw.view(torch.int16))
+        assert torch.equal(db2.view(torch.int16), db.view(torch.int16))
