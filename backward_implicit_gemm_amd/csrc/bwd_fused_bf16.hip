@@ -63,7 +63,7 @@ struct FusedVariant {
 // network's layers at B=1024 and B=16384; other shapes use separate calls.
 #define FV(MB, KS, TAPS, NBW, NSTEP, JW)                                              \
     {MB, KS, TAPS, NBW, NSTEP, JW, bwd_fused_bf16<8, MB, KS, TAPS, NBW, 2, NSTEP>,     \
-     dgrad_ig_bf16<8, MB, KS, TAPS, NBW, 2>, wgrad_ws_bf16<NSTEP, JW>}
+     dgrad_ig_bf16<8, MB, KS, TAPS, NBW, 2>, wgrad_ws_bf16<NSTEP, JW, false>}
 // (both grids in one launch run the 8-wave wgrad body, whose tiles are 128
 // columns: JW = 2)
 const FusedVariant kFusedVariants[] = {

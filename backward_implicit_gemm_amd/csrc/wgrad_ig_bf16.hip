@@ -28,9 +28,9 @@ namespace {
 // The role-split kernel (16 waves) runs the standalone call.
 struct WgradBfVariant {
     int NSTEP, JW;
-    void (*fn)(WgradBfArgs);
+    void (*fn[2])(WgradBfArgs);     // [bias column]
 };
-#define WB_V(NSTEP, JW) {NSTEP, JW, wgrad_ws_bf16<NSTEP, JW>}
+#define WB_V(NSTEP, JW) {NSTEP, JW, {wgrad_ws_bf16<NSTEP, JW, false>, wgrad_ws_bf16<NSTEP, JW, true>}}
 const WgradBfVariant kWgradBfVariants[] = {
     WB_V(1, 2), WB_V(1, 4), WB_V(2, 2), WB_V(2, 4),
     WB_V(3, 2), WB_V(3, 4), WB_V(4, 2), WB_V(4, 4),
@@ -128,7 +128,8 @@ hipError_t launch_wgrad_ig_bf16(const Geom &g, const WgradBfPlan &p, const void 
     if (kDzOC * g.P > kDzChunks * kDzNT) return hipErrorInvalidValue;
     e = allow_max_lds(reinterpret_cast<const void *>(&dz_groups_bf16));
     if (e != hipSuccess) return e;
-    e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
+    void (*fn)(WgradBfArgs) = v->fn[p.bias ? 1 : 0];
+    e = allow_max_lds(reinterpret_cast<const void *>(fn));
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(dz_groups_bf16, dim3(p.ngroups * kDzSlices), dim3(kDzNT), dz_lds, s,
                        (const u16 *)dy, (const u16 *)ym, dzg, g, relu, p.PP);
@@ -136,7 +137,7 @@ hipError_t launch_wgrad_ig_bf16(const Geom &g, const WgradBfPlan &p, const void 
     if (e != hipSuccess) return e;
     WgradBfArgs a{g, (const u16 *)x, dzg, part, p};
     const int slots = (p.splits + g.nxcd - 1) / g.nxcd * p.ncol;    // per XCD
-    hipLaunchKernelGGL(v->fn, dim3(g.nxcd * slots), dim3(2 * kWgNT), p.lds, s, a);
+    hipLaunchKernelGGL(fn, dim3(g.nxcd * slots), dim3(2 * kWgNT), p.lds, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.bias) return launch_wgrad_reduce_bias<bf16_t>(part, dw, db, p.splits, g.OC, g.K, p.NP, s);

@@ -317,7 +317,10 @@ __device__ __forceinline__ void wgrad_ig_bf16_body(const WgradBfArgs &a, int bid
 // The loaders store stage i+1 (loaded during stage i-1) into the other LDS
 // buffer and issue the loads of stage i+2 while the MFMAs run stage i; one
 // barrier per stage hands the buffers over.
-template <int NSTEP, int JW>
+// BIAS: the plan's bias column is computed (a compile-time switch: a per-lane
+// select of the B operand inside the MFMA loop costs the plain wgrad a third
+// of its time at JW = 4)
+template <int NSTEP, int JW, bool BIAS>
 __device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid)
 {
     constexpr int TW = 64 * JW;       // columns per workgroup tile
@@ -355,7 +358,7 @@ __device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid
     bool ones[JW];        // the bias column: B is 1 for every image
 #pragma unroll
     for (int j = 0; j < JW; ++j) {
-        ones[j] = p.bias && n0 + 16 * JW * wn + 16 * j + (lane & 15) == N;
+        ones[j] = BIAS && n0 + 16 * JW * wn + 16 * j + (lane & 15) == N;
         const int n = min(n0 + 16 * JW * wn + 16 * j + (lane & 15), N - 1);
         uint32_t ic, kk, kh, kw;
         fdivmod(uint32_t(n), g.fd_KK, ic, kk);
@@ -450,7 +453,7 @@ __device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid
             for (int i = 0; i < 4; ++i) af[i] = __builtin_bit_cast(bf16x8, db[drow[s] + 16 * i]);
 #pragma unroll
             for (int j = 0; j < JW; ++j)
-                bfr[j] = __builtin_bit_cast(bf16x8, ones[j] ? make_uint4(0x3F803F80u, 0x3F803F80u,
+                bfr[j] = __builtin_bit_cast(bf16x8, BIAS && ones[j] ? make_uint4(0x3F803F80u, 0x3F803F80u,
                                                                          0x3F803F80u, 0x3F803F80u)
                                                             : xb[xoff[j][s]]);
 #pragma unroll
@@ -509,10 +512,10 @@ __global__ void __launch_bounds__(kWgNT) wgrad_ig_bf16(WgradBfArgs a)
     wgrad_ig_bf16_body<NSTEP>(a, blockIdx.x);
 }
 
-template <int NSTEP, int JW>
+template <int NSTEP, int JW, bool BIAS>
 __global__ void __launch_bounds__(2 * kWgNT) wgrad_ws_bf16(WgradBfArgs a)
 {
-    wgrad_ws_bf16_body<NSTEP, JW>(a, blockIdx.x);
+    wgrad_ws_bf16_body<NSTEP, JW, BIAS>(a, blockIdx.x);
 }
 
 }  // namespace
