@@ -23,7 +23,11 @@ the CPU oracle timed on this host on a bounded sample.  The same line carries,
 under "workloads", every other workload's step and per-call times with each
 call's fraction of its binding roofline (bf16: algorithmic bytes over the cold
 time against HBM; fp32: flops over the hot time against fp32 MFMA), and under
-"data_independence" the layer-1 bf16 calls rerun with x scaled by 1/8 and 8.
+"data_independence" the layer-1 bf16 calls rerun with x scaled by 1/8 and 8,
+and under "hbm_copy" the bandwidth a plain 1 GiB device copy reaches here
+(reads + writes), beside which each bf16 call's fraction of the measured
+copy rate is given as "frac_copy" (the roofline fractions use the published
+8 TB/s).
 --workload NAME (or --all) prints the full line of other workloads.
 """
 import argparse
@@ -450,6 +454,54 @@ def workload_summary(wl, m):
             "calls": calls, "fused_bwd": m["fused"], "launch_floor": m["floor"]}
 
 
+def hbm_copy():
+    """A plain device-to-device copy of 1 GiB, four copies per graph replay,
+    median of five replays: bytes read plus bytes written per second."""
+    import torch
+
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(4):
+            dst.copy_(src)
+    g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(5):
+        start.record()
+        g.replay()
+        end.record()
+        torch.cuda.synchronize()
+        ts.append(start.elapsed_time(end) * 1e-3)
+    t = statistics.median(ts)
+    del g, src, dst
+    gbs = 2 * 4 * n / t / 1e9
+    return {"gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK["hbm_gbs"], 4),
+            "bytes_per_copy": 2 * n, "us_per_copy": round(t / 4 * 1e6, 2)}
+
+
+def add_copy_fractions(line, copy):
+    """frac_copy for every HBM-bound call: its algorithmic bytes over its cold
+    time, as a fraction of the measured copy rate."""
+    def upd(calls):
+        for c in calls.values():
+            if "frac" in c and c.get("bound", "hbm") == "hbm":
+                c["frac_copy"] = round(c["frac"] * PEAK["hbm_gbs"] / copy["gbs"], 4)
+    for w in line.get("workloads", {}).values():
+        if w["bound"] == "hbm":
+            upd(w["calls"])
+    if line["roofline"]["bound"] == "hbm":
+        upd(line["calls"])
+        line["roofline"]["frac_copy"] = round(line["roofline"]["achieved"] / copy["gbs"], 4)
+    line["hbm_copy"] = copy
+    return line
+
+
 def report(wl, m, steps, warmup, cpu, others=None, data_ind=None):
     L0 = wl.layers[0]
     flops_step = sum(3 * layer_flops(L) for L in wl.layers)
@@ -579,7 +631,10 @@ def main():
         cpu = None
         if not a.no_cpu and name == DEFAULT_WORKLOAD:
             cpu = cpu_baseline(wl, a.cpu_seconds)
-        print(json.dumps(report(wl, m, a.steps, a.warmup, cpu, others, dind)), flush=True)
+        line = report(wl, m, a.steps, a.warmup, cpu, others, dind)
+        if default_run and not a.headline_only:
+            line = add_copy_fractions(line, hbm_copy())
+        print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

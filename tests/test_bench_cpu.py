@@ -75,3 +75,18 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_copy_fractions_are_added_to_hbm_bound_calls():
+    others = {w.name: bench.workload_summary(w, _measured(w))
+              for w in inputs.WORKLOADS if w.name != bench.DEFAULT_WORKLOAD}
+    _, line = _line(bench.DEFAULT_WORKLOAD, others=others)
+    copy = {"gbs": 5000.0, "frac_of_peak": 0.625, "bytes_per_copy": 2 << 30, "us_per_copy": 400.0}
+    line = bench.add_copy_fractions(line, copy)
+    json.dumps(line)
+    assert line["hbm_copy"] == copy
+    c = line["workloads"]["layer1_bf16_relu_b1024"]["calls"]["fwd1"]
+    assert abs(c["frac_copy"] - c["frac"] * 8000.0 / 5000.0) < 1e-3
+    # fp32 calls are priced against MFMA and get no copy fraction
+    assert "frac_copy" not in line["calls"]["wgrad1"]
+    assert "frac_copy" not in line["workloads"]["layer2_fp32_b1024"]["calls"]["fwd1"]
