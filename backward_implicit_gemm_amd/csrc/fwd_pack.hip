@@ -5,10 +5,11 @@
 // Both forwards order the reduction index (channel group, tap, channel in the
 // group), so that a lane's MFMA operand is a run of consecutive channels at one
 // tap: 8 channels (16 bytes) for v_mfma_f32_16x16x32_bf16, 4 channels (16
-// bytes) for v_mfma_f32_16x16x4_f32.  OIHW weights hold a tap's channels KH*KW
-// elements apart, so a small pass per call gathers them into fragment order,
-// padding channels and taps with zeros; each wave then streams its fragments
-// as contiguous 1 KB reads.
+// bytes) for v_mfma_f32_16x16x4_f32 (whose steps may also share one tap
+// among four channel groups, see FwdF32Steps).  OIHW weights hold a tap's
+// channels KH*KW elements apart, so a small pass per call gathers them into
+// fragment order, padding channels and taps with zeros; each wave then
+// streams its fragments as contiguous 1 KB reads.
 #include "gc_kernels.h"
 #include "ig_common.h"
 
@@ -48,27 +49,44 @@ __global__ void __launch_bounds__(256) pack_w_fwd_bf16(const u16 *__restrict__ w
     }
 }
 
-// Packed weights, 16-byte units ((nb*NCG + cg)*TS + s)*64 + lane holding
-// w[16*nb + lane%16][4*cg + j][4*s + lane/16] for j = 0..3 (zero past OC, IC
-// or KH*KW).
+// Packed fp32 weights, 16-byte units (nb*NFRAG + f)*64 + lane: step f of
+// block nb (FwdF32Steps order), lane = n%16 + 16*q, holding four consecutive
+// channels of column n = 16*nb + lane%16 at one tap: for a full step (group
+// cg, tap step s) channels 4*cg .. 4*cg+3 at tap 4*s + q; for a shared step l
+// of a phase, channels of group 4*l + q of the phase at the last tap.  Zero
+// past OC, IC or KH*KW, and for lane groups past the phase's groups.
 __global__ void __launch_bounds__(256) pack_w_fwd_f32(const float *__restrict__ w,
-                                                      float4 *__restrict__ wf, Geom g, int NCG,
-                                                      int TS, int total)
+                                                      float4 *__restrict__ wf, Geom g,
+                                                      FwdF32Steps st, int total)
 {
+    const int nfrag = st.nfrag();
     for (int u = blockIdx.x * 256 + threadIdx.x; u < total; u += gridDim.x * 256) {
-        const int lane = u & 63;
-        int rest = u >> 6;
-        const int s = rest % TS;
-        rest /= TS;
-        const int cg = rest % NCG;
-        const int nb = rest / NCG;
+        const int lane = u & 63, q = lane >> 4;
+        int f = (u >> 6) % nfrag;
+        const int nb = (u >> 6) / nfrag;
+        int ph = 0;
+        while (f >= st.nsteps(ph)) {
+            f -= st.nsteps(ph);
+            ++ph;
+        }
+        int cg, t;
+        bool ok;
+        if (f < st.nfull(ph)) {
+            cg = ph * st.CPP + f / st.tsf();
+            t = 4 * (f % st.tsf()) + q;
+            ok = true;
+        } else {
+            const int l = f - st.nfull(ph);
+            cg = ph * st.CPP + 4 * l + q;
+            t = g.KK - 1;
+            ok = 4 * l + q < st.ncg(ph);
+        }
         const int n = nb * 16 + (lane & 15);
-        const int t = 4 * s + (lane >> 4);
         float v[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int ic = 4 * cg + j;
-            v[j] = (n < g.OC && ic < g.IC && t < g.KK) ? w[(size_t(n) * g.IC + ic) * g.KK + t] : 0.f;
+            v[j] = (ok && n < g.OC && ic < g.IC && t < g.KK) ? w[(size_t(n) * g.IC + ic) * g.KK + t] : 0.f;
         }
         wf[u] = make_float4(v[0], v[1], v[2], v[3]);
     }
@@ -140,13 +158,15 @@ hipError_t launch_pack_w_fwd_bf16(const Geom &g, int NCG, int TS, int nblocks, c
     return hipGetLastError();
 }
 
-hipError_t launch_pack_w_fwd_f32(const Geom &g, int NCG, int TS, int nblocks, const void *w,
-                                 void *wf, size_t ws_bytes, hipStream_t s)
+hipError_t launch_pack_w_fwd_f32(const Geom &g, int NCG, int CPP, int TS, int lo, int nblocks,
+                                 const void *w, void *wf, size_t ws_bytes, hipStream_t s)
 {
-    const int total = nblocks * NCG * TS * 64;
+    const FwdF32Steps st{NCG, CPP, TS, lo};
+    if (CPP < 1 || TS < 1 || (lo && (TS < 2 || g.KK != 4 * (TS - 1) + 1))) return hipErrorInvalidValue;
+    const int total = nblocks * st.nfrag() * 64;
     if (size_t(total) * 16 > ws_bytes) return hipErrorInvalidValue;
     hipLaunchKernelGGL(pack_w_fwd_f32, dim3(std::min((total + 255) / 256, 1024)), dim3(256), 0, s,
-                       (const float *)w, (float4 *)wf, g, NCG, TS, total);
+                       (const float *)w, (float4 *)wf, g, st, total);
     return hipGetLastError();
 }
 

@@ -1,11 +1,14 @@
 // fwd_ws_f32.hip -- forward convolution, fp32 storage, fp32 MFMA
 // (v_mfma_f32_16x16x4_f32), with loader waves and MFMA waves.
 //
-// The reduction runs in blocks of 16 k = 4 channels x 4 taps, so a lane's four MFMA steps read four
-// consecutive channels at one tap: x staged channels-innermost
-// [group][image][pixel][4] through 4x4 register transposes, weights
-// pre-packed into float4 fragments and streamed from L2 through a register
-// ring.  The roles are split as in fwd_ws_bf16.hip, because a wave's
+// The reduction runs in blocks of 16 k = 4 channels x 4 taps, so a lane's
+// four MFMA steps read four consecutive channels at one tap: x staged
+// channels-innermost [group][image][pixel][4] through 4x4 register
+// transposes, weights pre-packed into float4 fragments and streamed from L2
+// through a register ring.  When KH*KW = 4*(TS-1) + 1 (5x5 and 3x3 kernels),
+// the last tap of each channel group is not padded to a step of its own:
+// one step covers it for four groups, lane group q reading group 4l+q of
+// the phase (FwdF32Steps), which removes the zero-padded taps' MFMAs.  The roles are split as in fwd_ws_bf16.hip, because a wave's
 // vector-memory counter is in order and the x loads (HBM) would otherwise
 // hold up every later weight-ring wait (L2):
 //   * NWM loader waves: branch-free buffer loads (channels past IC and images
@@ -44,14 +47,16 @@ __device__ __forceinline__ float comp(const float4 &v, int i)
 
 // GS: LDS slots per staged channel group, a compile-time bound on G*IS, so
 // that the offsets of the groups and buffers are instruction immediates.
-template <int NWM, int MB, int TS, int NCG, int CPP, int D, int GS>
+template <int NWM, int MB, int TS, int NCG, int CPP, int D, int GS, bool LO>
 __global__ void __launch_bounds__(128 * NWM) __attribute__((amdgpu_waves_per_eu(1, NWM / 2)))
 fwd_ws_f32(FwdWsF32Args a)
 {
     extern __shared__ __attribute__((aligned(16))) float4 lds4f[];
     const Geom &g = a.g;
-    constexpr int NPH = (NCG + CPP - 1) / CPP;
-    constexpr int NFRAG = NCG * TS;
+    constexpr FwdF32Steps ST{NCG, CPP, TS, LO};
+    constexpr int NPH = ST.nph();
+    constexpr int NFRAG = ST.nfrag();
+    constexpr int TSF = ST.tsf();
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b0 = blockIdx.x * a.G;
     const int gimg = min(a.G, g.B - b0);
@@ -130,9 +135,9 @@ fwd_ws_f32(FwdWsF32Args a)
             rowoff[mb] = int(img) * a.IS + int(oh) * g.S * a.WP + int(ow) * g.S;
         }
     }
-    int toff[TS];
+    int toff[TSF];
 #pragma unroll
-    for (int s = 0; s < TS; ++s) {
+    for (int s = 0; s < TSF; ++s) {
         const int t = 4 * s + (lane >> 4);
         toff[s] = 0;
         if (t < g.KK) {
@@ -141,46 +146,58 @@ fwd_ws_f32(FwdWsF32Args a)
             toff[s] = int(kh) * a.WP + int(kw);
         }
     }
+    // shared steps: the last tap, in channel group (4l + q) of the phase
+    int t_last = 0, q_last = 0;
+    if (LO) {
+        uint32_t kh, kw;
+        fdivmod(uint32_t(g.KK - 1), g.fd_KW, kh, kw);
+        t_last = int(kh) * a.WP + int(kw);
+        q_last = (lane >> 4) * gstride + t_last;
+    }
 
     f32x4 acc[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // LDS slot of step k's A operand for row block mb (phase-relative): a full
+    // step (group k / TSF, taps 4*(k % TSF) + q) or shared step l = k - nfull
+    // (lanes past the phase's groups read a valid slot; their B is zero)
+    auto a_slot = [&](int ph, int k, int mb) {
+        const int nfull = ST.nfull(ph);
+        if (k < nfull) return (k / TSF) * gstride + rowoff[mb] + toff[k % TSF];
+        const int l = k - nfull;
+        const int nv = ST.ncg(ph) - 4 * l;
+        return 4 * l * gstride + rowoff[mb] + ((lane >> 4) < nv ? q_last : t_last);
+    };
+
     __syncthreads();                                 // phase 0 staged
 #pragma unroll
     for (int ph = 0; ph < NPH; ++ph) {
         const float4 *xbuf = lds4f + (ph & 1) * bufsz;
-        // A fragments one tap step ahead of their MFMAs
+        const int nst = ST.nsteps(ph), f0 = ST.base(ph);
+        // A fragments one step ahead of their MFMAs
         float4 af[2][MB];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) af[0][mb] = xbuf[rowoff[mb] + toff[0]];
+        for (int mb = 0; mb < MB; ++mb) af[0][mb] = xbuf[a_slot(ph, 0, mb)];
 #pragma unroll
-        for (int cg = ph * CPP; cg < (ph + 1) * CPP && cg < NCG; ++cg) {
-            const float4 *xb = xbuf + (cg - ph * CPP) * gstride;
+        for (int k = 0; k < nst; ++k) {
+            const int f = f0 + k;
+            const int cur = k & 1;
+            if (k + 1 < nst) {
 #pragma unroll
-            for (int st = 0; st < TS; ++st) {
-                const int f = cg * TS + st;
-                const int cur = ((cg - ph * CPP) * TS + st) & 1;   // step within the phase
-                // the next step's A: same group next tap, or next group's first
-                if (st + 1 < TS) {
-#pragma unroll
-                    for (int mb = 0; mb < MB; ++mb) af[cur ^ 1][mb] = xb[rowoff[mb] + toff[st + 1]];
-                } else if (cg + 1 < (ph + 1) * CPP && cg + 1 < NCG) {
-#pragma unroll
-                    for (int mb = 0; mb < MB; ++mb) af[cur ^ 1][mb] = xb[gstride + rowoff[mb] + toff[0]];
-                }
-                const float4 bv = ring[f % D];
-                if (f + D < NFRAG) ring[f % D] = bload16s(wrs, w_vo, (f + D) * 1024);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int mb = 0; mb < MB; ++mb)
-                        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(comp(af[cur][mb], j), comp(bv, j),
-                                                                       acc[mb], 0, 0, 0);
-                // keep each step's loads in their place: hoisting later steps'
-                // loads above these MFMAs would only lengthen register lives
-                __builtin_amdgcn_sched_barrier(0);
+                for (int mb = 0; mb < MB; ++mb) af[cur ^ 1][mb] = xbuf[a_slot(ph, k + 1, mb)];
             }
+            const float4 bv = ring[f % D];
+            if (f + D < NFRAG) ring[f % D] = bload16s(wrs, w_vo, (f + D) * 1024);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(comp(af[cur][mb], j), comp(bv, j),
+                                                                   acc[mb], 0, 0, 0);
+            // keep each step's loads in their place: hoisting later steps'
+            // loads above these MFMAs would only lengthen register lives
+            __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();                             // phase ph done, ph+1 staged
     }
@@ -206,10 +223,12 @@ fwd_ws_f32(FwdWsF32Args a)
 
 struct FwdWsF32Variant {
     int NWM, MB, TS, NCG, CPP, GS;
-    void (*fn)(FwdWsF32Args);
+    void (*fn[2])(FwdWsF32Args);     // [shared last-tap steps]
 };
-#define WF_V(NWM, MB, TS, NCG, CPP, GS) \
-    {NWM, MB, TS, NCG, CPP, GS, fwd_ws_f32<NWM, MB, TS, NCG, CPP, 8, GS>}
+#define WF_V(NWM, MB, TS, NCG, CPP, GS)                                   \
+    {NWM, MB, TS, NCG, CPP, GS,                                           \
+     {fwd_ws_f32<NWM, MB, TS, NCG, CPP, 8, GS, false>,                    \
+      fwd_ws_f32<NWM, MB, TS, NCG, CPP, 8, GS, true>}}
 const FwdWsF32Variant kFwdWsF32Variants[] = {
     // 59 -> 128, 11x15, 5x5, stride 3 (12 rows per image), 128 channels per workgroup
     WF_V(8, 3, 7, 15, 3, 960),    // 3 or 4 images, 36 or 48 rows
@@ -275,7 +294,8 @@ bool plan_fwd_ws_f32(const Geom &g, FwdWsPlan &p)
         if (!v) continue;
         q.lds = sizeof(float4) * 2 * size_t(q.CPP) * v->GS;
         if (q.lds > 150 * 1024) continue;
-        q.ws_bytes = size_t(ntile) * NWM * NCG * TS * 64 * 16;
+        q.lo = TS >= 2 && g.KK == 4 * (TS - 1) + 1;
+        q.ws_bytes = size_t(ntile) * NWM * FwdF32Steps{NCG, q.CPP, TS, q.lo}.nfrag() * 64 * 16;
         p = q;
         found = true;
         best_wgs = wgs; best_fill = fill; best_g = G;
@@ -290,13 +310,15 @@ hipError_t launch_fwd_ws_f32(const Geom &g, const FwdWsPlan &p, const void *x, c
     if (!v || p.G * p.nblk * p.CPP > 64 * p.NWM || g.HW < 4 || p.G * g.P > 16 * p.MB ||
         p.lds < sizeof(float4) * 2 * size_t(p.CPP) * v->GS)
         return hipErrorInvalidValue;
-    hipError_t e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
+    if (p.lo && !(p.TS >= 2 && g.KK == 4 * (p.TS - 1) + 1)) return hipErrorInvalidValue;
+    void (*fn)(FwdWsF32Args) = v->fn[p.lo ? 1 : 0];
+    hipError_t e = allow_max_lds(reinterpret_cast<const void *>(fn));
     if (e != hipSuccess) return e;
-    e = launch_pack_w_fwd_f32(g, p.NCG, p.TS, p.ntile * p.NWM, w, ws, p.ws_bytes, s);
+    e = launch_pack_w_fwd_f32(g, p.NCG, p.CPP, p.TS, p.lo, p.ntile * p.NWM, w, ws, p.ws_bytes, s);
     if (e != hipSuccess) return e;
     FwdWsF32Args a{g, (const float *)x, (const float4 *)ws, (const float *)bias, (float *)y, relu,
                    p.G, p.WP, p.IS, p.nblk};
-    hipLaunchKernelGGL(v->fn, dim3((g.B + p.G - 1) / p.G, p.ntile), dim3(128 * p.NWM), p.lds, s, a);
+    hipLaunchKernelGGL(fn, dim3((g.B + p.G - 1) / p.G, p.ntile), dim3(128 * p.NWM), p.lds, s, a);
     return hipGetLastError();
 }
 

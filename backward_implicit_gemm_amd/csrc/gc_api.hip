@@ -270,8 +270,8 @@ void name_fwd(const FwdSel &s, char *buf, size_t n, size_t &at)
 {
     switch (s.k) {
     case FwdKind::WsF32:
-        append(buf, n, at, "fwd_ws_f32<NWM=%d,MB=%d,TS=%d,NCG=%d,CPP=%d> G=%d ntile=%d", s.ws.NWM,
-               s.ws.MB, s.ws.TS, s.ws.NCG, s.ws.CPP, s.ws.G, s.ws.ntile);
+        append(buf, n, at, "fwd_ws_f32<NWM=%d,MB=%d,TS=%d,NCG=%d,CPP=%d,LO=%d> G=%d ntile=%d", s.ws.NWM,
+               s.ws.MB, s.ws.TS, s.ws.NCG, s.ws.CPP, s.ws.lo, s.ws.G, s.ws.ntile);
         break;
     case FwdKind::WsBf16:
         append(buf, n, at, "fwd_ws_bf16<NBW=%d,MB=%d,TS=%d,NCG=%d,CPP=%d> G=%d ntile=%d", s.ws.NBW,

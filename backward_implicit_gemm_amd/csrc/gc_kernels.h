@@ -54,10 +54,10 @@ size_t bias_grad_ws_bytes(const Geom &g);
 template <typename T>
 hipError_t launch_bias_grad(const Geom &g, const void *dy, const void *ym, void *db, float *part,
                             int relu, hipStream_t s);
-// packs w into the B-fragment order of the fp32 forward for `nblocks`
-// 16-channel blocks (fwd_pack.hip)
-hipError_t launch_pack_w_fwd_f32(const Geom &g, int NCG, int TS, int nblocks, const void *w,
-                                 void *wf, size_t ws_bytes, hipStream_t s);
+// packs w into the B-fragment order of the fp32 forward's MFMA steps (see
+// FwdF32Steps) for `nblocks` 16-channel blocks (fwd_pack.hip)
+hipError_t launch_pack_w_fwd_f32(const Geom &g, int NCG, int CPP, int TS, int lo, int nblocks,
+                                 const void *w, void *wf, size_t ws_bytes, hipStream_t s);
 // fp32 forward with loader and MFMA waves
 bool plan_fwd_ws_f32(const Geom &g, FwdWsPlan &p);
 hipError_t launch_fwd_ws_f32(const Geom &g, const FwdWsPlan &p, const void *x, const void *w,

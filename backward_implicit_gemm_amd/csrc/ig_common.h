@@ -156,6 +156,27 @@ constexpr uint32_t kOffNone = 0xFFFFFFF0u;   // an offset past the end of every 
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ---------------------------------------------------------------- forward --
+// MFMA steps of the fp32 forward per 16-channel block, phase by phase: a
+// phase stages ncg = min(CPP, NCG - ph*CPP) channel groups; each group takes
+// TSF tap steps (taps 4s .. 4s+3 on the four lane groups), TSF = TS, or TS-1
+// when `lo`: then KH*KW = 4*(TS-1) + 1 and the last tap of the phase's groups
+// is covered by ceil(ncg/4) shared steps, lane group q taking group 4l+q of
+// the phase (no zero-padded taps beyond the last step's unused lanes).
+struct FwdF32Steps {
+    int NCG, CPP, TS, lo;
+    __host__ __device__ constexpr int tsf() const { return lo ? TS - 1 : TS; }
+    __host__ __device__ constexpr int nph() const { return (NCG + CPP - 1) / CPP; }
+    __host__ __device__ constexpr int ncg(int ph) const { return NCG - ph * CPP < CPP ? NCG - ph * CPP : CPP; }
+    __host__ __device__ constexpr int nfull(int ph) const { return ncg(ph) * tsf(); }
+    __host__ __device__ constexpr int nsteps(int ph) const { return nfull(ph) + (lo ? (ncg(ph) + 3) / 4 : 0); }
+    __host__ __device__ constexpr int base(int ph) const
+    {
+        int b = 0;
+        for (int i = 0; i < ph; ++i) b += nsteps(i);
+        return b;
+    }
+    __host__ __device__ constexpr int nfrag() const { return base(nph()); }
+};
 // Forward with loader and MFMA waves (fwd_ws_bf16.hip, fwd_ws_f32.hip).
 struct FwdWsPlan {
     int NWM;      // MFMA waves (as many loader waves; fp32 only, bf16 uses 4)
@@ -168,6 +189,7 @@ struct FwdWsPlan {
     int NCG;      // channel groups (8 channels bf16, 4 fp32)
     int CPP;      // channel groups per staging phase
     int ntile;    // column tiles
+    int lo;       // fp32: the last tap of every channel group in shared steps (KH*KW % 4 == 1)
     int ystage;   // bf16: output staged through LDS for 16-byte stores
     size_t lds;       // the whole x tile (bf16), two phase buffers (fp32)
     size_t ws_bytes;  // packed weights

@@ -26,9 +26,9 @@ LAYER_BATCHES = {
 # (layer, dtype, op) -> kernel instances (family<compile-time parameters>)
 INSTANCES = {
     ("layer1", "f32", "fwd"): {
-        "fwd_ws_f32<NWM=8,MB=1,TS=7,NCG=15,CPP=12>",
-        "fwd_ws_f32<NWM=8,MB=2,TS=7,NCG=15,CPP=6>",
-        "fwd_ws_f32<NWM=8,MB=3,TS=7,NCG=15,CPP=3>",
+        "fwd_ws_f32<NWM=8,MB=1,TS=7,NCG=15,CPP=12,LO=1>",
+        "fwd_ws_f32<NWM=8,MB=2,TS=7,NCG=15,CPP=6,LO=1>",
+        "fwd_ws_f32<NWM=8,MB=3,TS=7,NCG=15,CPP=3,LO=1>",
     },
     ("layer1", "f32", "bwd_data"): {"dgrad_rf_f32<MB=3,KS4=8,TAPS=4>"},
     ("layer1", "f32", "bwd_weight"): {"wgrad_rf_f32<NBWV=3>", "wgrad_rf_f32<NBWV=6>"},
@@ -43,11 +43,11 @@ INSTANCES = {
     },
     ("layer1", "bf16", "bwd_weight"): {"wgrad_ws_bf16<NSTEP=3,JW=2>", "wgrad_ws_bf16<NSTEP=3,JW=4>"},
     ("layer2", "f32", "fwd"): {
-        "fwd_ws_f32<NWM=4,MB=1,TS=3,NCG=32,CPP=32>",
-        "fwd_ws_f32<NWM=4,MB=1,TS=3,NCG=32,CPP=21>",
-        "fwd_ws_f32<NWM=4,MB=1,TS=3,NCG=32,CPP=10>",
-        "fwd_ws_f32<NWM=4,MB=2,TS=3,NCG=32,CPP=5>",
-        "fwd_ws_f32<NWM=4,MB=4,TS=3,NCG=32,CPP=2>",
+        "fwd_ws_f32<NWM=4,MB=1,TS=3,NCG=32,CPP=32,LO=1>",
+        "fwd_ws_f32<NWM=4,MB=1,TS=3,NCG=32,CPP=21,LO=1>",
+        "fwd_ws_f32<NWM=4,MB=1,TS=3,NCG=32,CPP=10,LO=1>",
+        "fwd_ws_f32<NWM=4,MB=2,TS=3,NCG=32,CPP=5,LO=1>",
+        "fwd_ws_f32<NWM=4,MB=4,TS=3,NCG=32,CPP=2,LO=1>",
     },
     ("layer2", "f32", "bwd_data"): {
         "dgrad_rf_f32<MB=1,KS4=8,TAPS=2>",

@@ -54,7 +54,7 @@ def test_policy_generic_is_reported():
 
 def test_headline_plans():
     # the kernels the B=1024 workloads run (the bench's per-call figures)
-    assert plan("layer1", 1024, "f32", "fwd").startswith("fwd_ws_f32<NWM=8,MB=3,TS=7,NCG=15,CPP=3> G=4")
+    assert plan("layer1", 1024, "f32", "fwd").startswith("fwd_ws_f32<NWM=8,MB=3,TS=7,NCG=15,CPP=3,LO=1> G=4")
     assert plan("layer1", 1024, "f32", "bwd_weight").startswith("wgrad_rf_f32<NBWV=6>")
     assert plan("layer1", 1024, "bf16", "fwd").startswith("fwd_ws_bf16<NBW=2,MB=3,TS=7,NCG=8,CPP=3> G=4")
     assert plan("layer2", 1024, "bf16", "fwd").startswith("fwd_ws_bf16<NBW=1,MB=1,TS=3,NCG=16,CPP=16> G=8")
