@@ -40,11 +40,6 @@ struct FwdWsF32Args {
     int nblk;     // 4-pixel blocks per image plane
 };
 
-__device__ __forceinline__ float comp(const float4 &v, int i)
-{
-    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-
 // GS: LDS slots per staged channel group, a compile-time bound on G*IS, so
 // that the offsets of the groups and buffers are instruction immediates.
 template <int NWM, int MB, int TS, int NCG, int CPP, int D, int GS, bool LO>

@@ -156,6 +156,10 @@ bool bwd_fused_plan(const Geom &g, BwdFusedBfPlan &p)
 {
     return use_ig() && cached_plan<BwdFusedBfPlan, plan_bwd_fused_bf16>(g, p);
 }
+bool bwd_fused_f32_plan(const Geom &g, BwdFusedF32Plan &p)
+{
+    return use_ig() && cached_plan<BwdFusedF32Plan, plan_bwd_fused_f32>(g, p);
+}
 size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
 bool wgrad_f32_rf_plan(const Geom &g, WgradRfPlan &p)
 {
@@ -413,6 +417,8 @@ size_t gc_conv_workspace_bytes(int op, const gc_conv_desc *d, int dtype)
     case GC_OP_BWD: {
         BwdFusedBfPlan p;
         if (dtype == GC_BF16 && bwd_fused_plan(g, p)) return p.ws_bytes;
+        BwdFusedF32Plan pf;
+        if (dtype == GC_F32 && bwd_fused_f32_plan(g, pf)) return pf.ws_bytes;
         // d_input's workspace, then wgrad's at the next 256-byte boundary
         return round256(gc_conv_workspace_bytes(GC_OP_BWD_DATA, d, dtype)) +
                gc_conv_workspace_bytes(GC_OP_BWD_WEIGHT, d, dtype);
@@ -639,6 +645,13 @@ int gc_conv_bwd(const void *x, const void *w, const void *dy, const void *y_mask
         return hip_status(launch_bwd_fused_bf16(g, fp, x, w, dy, y_mask, dx, dw, workspace, relu,
                                                 static_cast<hipStream_t>(stream)));
     }
+    BwdFusedF32Plan ff;
+    if (dtype == GC_F32 && bwd_fused_f32_plan(g, ff)) {
+        if (ff.ws_bytes && (!workspace || ws_bytes < ff.ws_bytes)) return GC_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(workspace) % 256) return GC_ERR_WORKSPACE;
+        return hip_status(launch_bwd_fused_f32(g, ff, x, w, dy, y_mask, dx, dw, workspace, relu,
+                                               static_cast<hipStream_t>(stream)));
+    }
     // no fused plan: d_input, then wgrad, each in its part of the workspace
     const size_t wd = gc_conv_workspace_bytes(GC_OP_BWD_DATA, d, dtype);
     const size_t ww = gc_conv_workspace_bytes(GC_OP_BWD_WEIGHT, d, dtype);
@@ -690,6 +703,17 @@ int gc_conv_plan_name(int op, const gc_conv_desc *d, int dtype, char *buf, size_
             WgradSel w{};
             w.k = WgradKind::IgBf16;
             w.bf = fp.w;
+            name_wgrad(w, buf, buf_bytes, at);
+        } else if (BwdFusedF32Plan ff; dtype == GC_F32 && bwd_fused_f32_plan(g, ff)) {
+            append(buf, buf_bytes, at, "bwd_fused_f32: ");
+            DgradSel d{};
+            d.k = DgradKind::RfF32;
+            d.bf = ff.d;
+            name_dgrad(d, buf, buf_bytes, at);
+            append(buf, buf_bytes, at, " + ");
+            WgradSel w{};
+            w.k = WgradKind::RfF32;
+            w.rf = ff.w;
             name_wgrad(w, buf, buf_bytes, at);
         } else {
             name_dgrad(select_dgrad(g, dtype), buf, buf_bytes, at);

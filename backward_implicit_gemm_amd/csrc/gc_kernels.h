@@ -26,6 +26,7 @@ struct DgradBfPlan;
 struct WgradBfPlan;
 struct WgradRfPlan;
 struct BwdFusedBfPlan;
+struct BwdFusedF32Plan;
 // d_input and wgrad run on fp32 MFMA for both storage types (T = float or
 // bf16_t; bf16 is widened exactly while staging).
 bool plan_dgrad_ig_f32(const Geom &g, DgradIgPlan &p);
@@ -86,6 +87,12 @@ bool plan_bwd_fused_bf16(const Geom &g, BwdFusedBfPlan &p);
 hipError_t launch_bwd_fused_bf16(const Geom &g, const BwdFusedBfPlan &p, const void *x,
                                  const void *w, const void *dy, const void *ym, void *dx, void *dw,
                                  void *ws, int relu, hipStream_t s);
+// fp32 backward in two launches: the d_input and wgrad workgroups in one
+// grid, then the reduction.  Same results as the separate calls.
+bool plan_bwd_fused_f32(const Geom &g, BwdFusedF32Plan &p);
+hipError_t launch_bwd_fused_f32(const Geom &g, const BwdFusedF32Plan &p, const void *x,
+                                const void *w, const void *dy, const void *ym, void *dx, void *dw,
+                                void *ws, int relu, hipStream_t s);
 bool plan_wgrad_ig_bf16(const Geom &g, WgradBfPlan &p);
 // the same with the bias gradient as one more column (x = 1) of the tiles
 bool plan_wgrad_ig_bf16_bias(const Geom &g, WgradBfPlan &p);

@@ -69,6 +69,13 @@ class SearchMemo {
 // Four consecutive elements as fp32 from an element-aligned global address:
 // one 16-byte load for fp32 storage, one 8-byte load widened exactly for
 // bf16 storage.
+// Component i (0..3) of a float4, with i a compile-time constant after
+// unrolling.
+__device__ __forceinline__ float comp(const float4 &v, int i)
+{
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
 __device__ __forceinline__ float4 ld4_f32(const float *p)
 {
     float4 v;
@@ -309,6 +316,14 @@ struct BwdFusedBfPlan {
     size_t ws_w_offset;   // d.ws_bytes rounded up to 256
     size_t ws_bytes;      // ws_w_offset + w.ws_bytes
     int fuse_main;        // both main kernels in one grid
+};
+
+// fp32 backward in two launches (bwd_fused_f32.hip): the d_input and wgrad
+// workgroups in one grid, then the reduction.
+struct BwdFusedF32Plan {
+    DgradBfPlan d;
+    WgradRfPlan w;
+    size_t ws_bytes;      // w.ws_bytes (the fp32 d_input needs no workspace)
 };
 
 }  // namespace gc

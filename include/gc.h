@@ -165,7 +165,9 @@ int gc_conv_bwd_weight_bias(const void *x, const void *dy, const void *y_mask, v
  * weight packing for d_input), then the two main kernels -- in one launch
  * holding both grids side by side where the d_input grid fits the chip in
  * one round, else one after the other -- and the fixed-order reduction of
- * wgrad's partials; for other shapes the two calls one after the other.  The workspace
+ * wgrad's partials; for fp32 shapes with a fused plan, one launch holding the
+ * d_input and wgrad grids side by side, then the reduction; for other shapes
+ * the two calls one after the other.  The workspace
  * (gc_conv_workspace_bytes(GC_OP_BWD, ...)) must be 256-byte aligned. */
 int gc_conv_bwd(const void *x, const void *w, const void *dy, const void *y_mask, void *dx,
                 void *dw, void *workspace, size_t ws_bytes,

@@ -79,6 +79,26 @@ OTHER_GPU_BATCHES = {
 }
 
 
+# gc_conv_bwd in fp32 runs the d_input and wgrad bodies in one launch; each
+# (d_input, wgrad) pair the planners can pick for the layer shapes -> a
+# (layer, batch size, relu) case that reaches it
+FUSED_F32_BWD = {
+    "bwd_fused_f32: dgrad_rf_f32<MB=3,KS4=8,TAPS=4> + wgrad_rf_f32<NBWV=3>": ("layer1", 97, 1),
+    "bwd_fused_f32: dgrad_rf_f32<MB=3,KS4=8,TAPS=4> + wgrad_rf_f32<NBWV=6>": ("layer1", 250, 0),
+    "bwd_fused_f32: dgrad_rf_f32<MB=1,KS4=8,TAPS=2> + wgrad_rf_f32<NBWV=3>": ("layer2", 66, 1),
+    "bwd_fused_f32: dgrad_rf_f32<MB=2,KS4=8,TAPS=2> + wgrad_rf_f32<NBWV=3>": ("layer2", 203, 0),
+    "bwd_fused_f32: dgrad_rf_f32<MB=3,KS4=8,TAPS=2> + wgrad_rf_f32<NBWV=3>": ("layer2", 409, 1),
+}
+
+
+def fused_pair(plan_name):
+    """'bwd_fused_f32: <d_input instance> + <wgrad instance>' of a
+    gc_conv_bwd plan name (the per-batch parameters dropped)."""
+    head, _, rest = plan_name.partition(": ")
+    d, _, w = rest.partition(" + ")
+    return f"{head}: {instance_key(d)} + {instance_key(w)}"
+
+
 def instance_key(plan_name):
     """The kernel instance of one part of a plan name: 'family<...>', or the
     bare family name for kernels without compile-time parameters."""

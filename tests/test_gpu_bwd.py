@@ -1,8 +1,8 @@
 """GPU tests of gc_conv_bwd, the whole backward of a layer in one call.
 
 It must give dx and dw bit for bit equal to gc_conv_bwd_data followed by
-gc_conv_bwd_weight (bf16 shapes with a fused plan run the same kernel bodies
-in fewer launches; other shapes make the two calls), and so match the oracle
+gc_conv_bwd_weight (shapes with a fused plan run the same kernel bodies in
+fewer launches; other shapes make the two calls), and so match the oracle
 to the same tolerance.  The layer shapes are those of the policy network at
 B=1024 and of the two-layer chain at B=16384.
 """
@@ -13,6 +13,7 @@ import torch
 from backward_implicit_gemm_amd import binding as gb
 from backward_implicit_gemm_amd import inputs
 
+from cases import FUSED_F32_BWD, LAYER_SHAPES, fused_pair
 from parity import TOL, Layer, draw, f64, oracle_layer, rel_err
 
 pytestmark = pytest.mark.gpu
@@ -108,3 +109,22 @@ def test_bwd_repeated_calls_are_identical():
         torch.cuda.synchronize()
         assert _bits_equal(dx3, dx) and _bits_equal(dw3, dw)
     assert np.isfinite(f64(dw)).all()
+
+
+@pytest.mark.parametrize("pair", sorted(FUSED_F32_BWD), ids=lambda p: "{}-B{}-relu{}".format(*FUSED_F32_BWD[p]))
+def test_fused_f32_pairs(pair):
+    # every (d_input, wgrad) pair of the one-launch fp32 backward, with a
+    # batch that leaves a ragged last image group and quad
+    layer_name, B, relu = FUSED_F32_BWD[pair]
+    shape = LAYER_SHAPES[layer_name][:7]
+    layer = Layer(B, *shape, relu)
+    name = gb.gc_conv_plan_name(gb.GC_OP_BWD, gb.make_desc(B, *shape), gb.GC_F32)
+    print(f"{layer_name} B={B} relu={relu}: {name}", flush=True)
+    assert fused_pair(name) == pair
+    x, w, dy = draw(layer, (B, 5, 6 + relu), "f32")
+    y, dx, dw, dx2, dw2 = _both(layer, "f32", x, w, dy)
+    assert _bits_equal(dx, dx2) and _bits_equal(dw, dw2)
+    _, dx_ref, dw_ref = oracle_layer(layer, x, w, dy, y)
+    edx, edw = rel_err(f64(dx), dx_ref), rel_err(f64(dw), dw_ref)
+    print(f"  dx={edx:.2e} dw={edw:.2e}", flush=True)
+    assert edx <= TOL["f32"] and edw <= TOL["f32"]

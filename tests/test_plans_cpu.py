@@ -11,9 +11,11 @@ import pytest
 
 from backward_implicit_gemm_amd import binding as gb
 
-from cases import INSTANCES, LAYER_BATCHES, LAYER_SHAPES, OTHER_GPU_BATCHES, instance_key
+from cases import (FUSED_F32_BWD, INSTANCES, LAYER_BATCHES, LAYER_SHAPES, OTHER_GPU_BATCHES,
+                   fused_pair, instance_key)
 
-OPS = {"fwd": gb.GC_OP_FWD, "bwd_data": gb.GC_OP_BWD_DATA, "bwd_weight": gb.GC_OP_BWD_WEIGHT}
+OPS = {"fwd": gb.GC_OP_FWD, "bwd_data": gb.GC_OP_BWD_DATA, "bwd_weight": gb.GC_OP_BWD_WEIGHT,
+       "bwd": gb.GC_OP_BWD}
 DT = {"f32": gb.GC_F32, "bf16": gb.GC_BF16}
 
 
@@ -93,3 +95,15 @@ def test_every_reachable_instance_is_gpu_tested(key):
     assert reached <= INSTANCES[key], reached - INSTANCES[key]
     for B in OTHER_GPU_BATCHES[layer]:
         assert instance_key(plan(layer, B, dtype, op)) in INSTANCES[key]
+
+
+def test_fp32_backward_is_fused_and_every_pair_is_gpu_tested():
+    # gc_conv_bwd in fp32 takes the one-launch path at every batch size of
+    # both layer shapes, and each (d_input, wgrad) pair it can pick has a
+    # GPU case
+    for layer in LAYER_SHAPES:
+        for B in _sweep():
+            name = plan(layer, B, "f32", "bwd")
+            assert fused_pair(name) in FUSED_F32_BWD, (layer, B, name)
+    for pair, (layer, B, _) in FUSED_F32_BWD.items():
+        assert fused_pair(plan(layer, B, "f32", "bwd")) == pair
