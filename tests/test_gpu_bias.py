@@ -70,6 +70,8 @@ BIAS_SHAPES = [
     (2, 3, 32, 32, 8, 5, 5, 2),
     (9, 59, 11, 15, 128, 5, 5, 3),
     (300, 8, 5, 5, 16, 3, 3, 1),        # more images than a bias-grad workgroup has threads
+    (2, 3, 5, 5, 260, 3, 3, 1),         # more channels than a bias-grad workgroup has threads
+    (3, 4, 20, 20, 64, 3, 3, 1),        # a 4-image chunk too large to stage in LDS
 ]
 
 
