@@ -1,8 +1,9 @@
 """Benchmark: convolution forward + d_input + wgrad through libgc's C ABI.
 
 One step is one pass of the whole path over one batch -- forward (with the
-fused ReLU where the layer has one), d_input and wgrad -- on synthetic seeded
-inputs already resident in HBM.  The default workload is the policy
+fused ReLU where the layer has one), then d_input and wgrad through
+gc_conv_bwd, the library's one-call backward (the page's gemm_conv_backward
+counterpart) -- on synthetic seeded inputs already resident in HBM.  The default workload is the policy
 network's layer 1 in fp32 at B=1024 (59->128 channels, 11x15 input, 5x5
 kernel, stride 3, ReLU), as benchmarked in "Speedups to gemm_conv_forward and
 gemm_conv_backward kernels" (PufferLib pull request #522), which times
@@ -17,8 +18,10 @@ same K steps issued eagerly (host work included); the step timed cold
 (caches flushed by a 640 MB write before each replay); the launch floor (a
 graph of as many one-element kernels as a step launches); per-call GPU times,
 hot (graphs of back-to-back copies of each call) and cold (each call alone
-after a cache flush, median of several); the backward through gc_conv_bwd
-(d_input and wgrad in one call); a roofline entry for the dominant call; and
+after a cache flush, median of several), for the step's calls and for the
+two backward passes as separate calls (gc_conv_bwd_data, gc_conv_bwd_weight),
+with the step made of those separate calls beside it; a roofline entry for
+the dominant call of the step; and
 the CPU oracle timed on this host on a bounded sample.  The same line carries,
 under "workloads", every other workload's step and per-call times with each
 call's fraction of its binding roofline (bf16: algorithmic bytes over the cold
@@ -89,10 +92,12 @@ def layer_bytes(L, esize):
     nx = L.B * L.IC * L.H * L.W
     nw = L.OC * L.IC * L.KH * L.KW
     ny = L.B * L.OC * L.OH * L.OW
+    nm = ny if L.relu else 0      # y, read as the ReLU mask
     fwd = (nx + nw + ny) * esize
-    dgrad = (ny + (ny if L.relu else 0) + nw + nx) * esize
-    wgrad = (nx + ny + (ny if L.relu else 0) + nw) * esize
-    return {"fwd": fwd, "dgrad": dgrad, "wgrad": wgrad}
+    dgrad = (ny + nm + nw + nx) * esize
+    wgrad = (nx + ny + nm + nw) * esize
+    bwd = (ny + nm + nx + nw + nx + nw) * esize    # dy, y, x, w read; dx, dw written
+    return {"fwd": fwd, "dgrad": dgrad, "wgrad": wgrad, "bwd": bwd}
 
 
 def source_digest():
@@ -152,14 +157,23 @@ def run_gpu(wl, steps, warmup, x_scale=1.0, extras=True):
            for i, L in enumerate(layers)]
     dws = [torch.empty(L.w_shape, dtype=td, device=dev) for L in layers]
 
-    # calls of one step, in order: forward through the layers, then backward
+    # calls of one step, in order: forward through the layers, then the
+    # backward of each layer (d_input and wgrad in one gc_conv_bwd call), last
+    # layer first
     calls = []
     for i, c in enumerate(convs):
         calls.append((f"fwd{i + 1}", lambda c=c, i=i: c.fwd(xs[i], ws[i], ys[i])))
     for i in reversed(range(len(convs))):
         c = convs[i]
-        calls.append((f"dgrad{i + 1}", lambda c=c, i=i: c.bwd_data(dys[i], ws[i], ys[i], dxs[i])))
-        calls.append((f"wgrad{i + 1}", lambda c=c, i=i: c.bwd_weight(xs[i], dys[i], ys[i], dws[i])))
+        calls.append((f"bwd{i + 1}",
+                      lambda c=c, i=i: c.bwd(xs[i], ws[i], dys[i], ys[i], dxs[i], dws[i])))
+    # the two backward passes of each layer as separate calls, timed beside
+    # the step
+    pass_calls = []
+    for i in reversed(range(len(convs))):
+        c = convs[i]
+        pass_calls.append((f"dgrad{i + 1}", lambda c=c, i=i: c.bwd_data(dys[i], ws[i], ys[i], dxs[i])))
+        pass_calls.append((f"wgrad{i + 1}", lambda c=c, i=i: c.bwd_weight(xs[i], dys[i], ys[i], dws[i])))
 
     def step():
         for _, f in calls:
@@ -209,7 +223,7 @@ def run_gpu(wl, steps, warmup, x_scale=1.0, extras=True):
     # Launch floor: the same number of kernels as one step, each a one-element
     # add, replayed as a graph; the least time a step of that many dependent
     # launches can take.
-    nk = sum(len(CALL_KERNELS[name.rstrip("0123456789")][wl.dtype]) for name, _ in calls)
+    nk = sum(len(call_kernels(wl, name)) for name, _ in calls)
     tiny = torch.zeros(1, device=dev)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -242,7 +256,8 @@ def run_gpu(wl, steps, warmup, x_scale=1.0, extras=True):
     reps = 10
     replays = max(2, min(20, steps // reps))
     per_call = {}
-    for name, f in calls:
+    for name, f in calls + pass_calls:
+        f()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for _ in range(reps):
@@ -256,35 +271,13 @@ def run_gpu(wl, steps, warmup, x_scale=1.0, extras=True):
         torch.cuda.synchronize()
         per_call[name] = start.elapsed_time(end) / (replays * reps) * 1e3
         del g
-    per_call_cold = {name: cold_call_us(f, stream, dev) for name, f in calls}
+    per_call_cold = {name: cold_call_us(f, stream, dev) for name, f in calls + pass_calls}
 
-    # The whole backward of each layer through gc_conv_bwd (one call for
-    # d_input and wgrad; fewer launches where a fused plan exists), per call
-    # and as a step with the forward calls.
-    fused_calls = [(f"bwd{i + 1}", lambda c=c, i=i: c.bwd(xs[i], ws[i], dys[i], ys[i], dxs[i], dws[i]))
-                   for i, c in reversed(list(enumerate(convs)))]
-    fused = {"us_per_call": {}}
-    for name, f in fused_calls:
-        f()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(reps):
-                f()
-        g.replay()
-        torch.cuda.synchronize()
-        start.record(stream)
-        for _ in range(replays):
-            g.replay()
-        end.record(stream)
-        torch.cuda.synchronize()
-        fused["us_per_call"][name] = round(start.elapsed_time(end) / (replays * reps) * 1e3, 3)
-        del g
-    fused["us_per_call_cold"] = {name: round(cold_call_us(f, stream, dev), 3)
-                                 for name, f in fused_calls}
+    # The step with the backward as the two separate calls per layer.
     fwd_calls = [c for c in calls if c[0].startswith("fwd")]
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for _, f in fwd_calls + fused_calls:
+        for _, f in fwd_calls + pass_calls:
             f()
     for _ in range(warmup):
         g.replay()
@@ -294,7 +287,7 @@ def run_gpu(wl, steps, warmup, x_scale=1.0, extras=True):
         g.replay()
     end.record(stream)
     torch.cuda.synchronize()
-    fused["ms_per_step"] = round(start.elapsed_time(end) / steps, 5)
+    ms_step_separate = start.elapsed_time(end) / steps
     del g
 
     # The bias entry points (forward with a bias, bias gradient), timed the
@@ -329,7 +322,8 @@ def run_gpu(wl, steps, warmup, x_scale=1.0, extras=True):
         del g
     return {"ms_step": ms_step, "ms_eager": ms_eager, "per_call": per_call,
             "per_call_cold": per_call_cold, "bias_us": bias_us, "ms_cold": ms_cold,
-            "floor": floor, "fused": fused}
+            "floor": floor, "step_calls": [n for n, _ in calls],
+            "ms_step_separate": ms_step_separate}
 
 
 def cold_call_us(f, stream, dev, reps=4, rounds=5):
@@ -413,14 +407,37 @@ CALL_KERNELS = {
               "bf16": ["dz_groups_bf16", "wgrad_ws_bf16", "wgrad_reduce"]},
 }
 
+
+def call_kernels(wl, name):
+    """The kernels a call launches: fixed per pass, and for gc_conv_bwd the
+    ones its plan (as the library reports it) runs."""
+    op = name.rstrip("0123456789")
+    if op != "bwd":
+        return CALL_KERNELS[op][wl.dtype]
+    from backward_implicit_gemm_amd import binding as gb
+
+    L = wl.layers[int(name[len(op):]) - 1]
+    d = gb.make_desc(L.B, L.IC, L.H, L.W, L.OC, L.KH, L.KW, L.stride)
+    plan = gb.gc_conv_plan_name(gb.GC_OP_BWD, d, gb.GC_F32 if wl.dtype == "f32" else gb.GC_BF16)
+    if plan.startswith("bwd_fused_f32"):
+        return ["bwd_fused_f32", "wgrad_reduce"]
+    if plan.startswith("bwd_fused_bf16 fuse_main=1"):
+        return ["bwd_prep_bf16", "bwd_fused_bf16", "wgrad_reduce"]
+    if plan.startswith("bwd_fused_bf16"):
+        return ["bwd_prep_bf16", "dgrad_ig_bf16", "wgrad_ws_bf16", "wgrad_reduce"]
+    return CALL_KERNELS["dgrad"][wl.dtype] + CALL_KERNELS["wgrad"][wl.dtype]
+
+
 def call_work(wl):
-    """Algorithmic (flops, bytes) of every call of a step."""
+    """Algorithmic (flops, bytes) of every call: the step's (fwd, bwd) and the
+    separate backward passes (dgrad, wgrad)."""
     esize = 4 if wl.dtype == "f32" else 2
     work = {}
     for i, L in enumerate(wl.layers):
         b = layer_bytes(L, esize)
         for op in ("fwd", "dgrad", "wgrad"):
             work[f"{op}{i + 1}"] = (layer_flops(L), b[op])
+        work[f"bwd{i + 1}"] = (2 * layer_flops(L), b["bwd"])
     return work
 
 
@@ -451,7 +468,8 @@ def workload_summary(wl, m):
             "ms_per_step": round(m["ms_step"], 5), "ms_per_step_cold": round(m["ms_cold"], 5),
             "tflops_step": round(sum(3 * layer_flops(L) for L in wl.layers)
                                  / (m["ms_step"] * 1e-3) / 1e12, 3),
-            "calls": calls, "fused_bwd": m["fused"], "launch_floor": m["floor"]}
+            "ms_per_step_separate_calls": round(m["ms_step_separate"], 5),
+            "calls": calls, "launch_floor": m["floor"]}
 
 
 def hbm_copy():
@@ -506,19 +524,20 @@ def report(wl, m, steps, warmup, cpu, others=None, data_ind=None):
     L0 = wl.layers[0]
     flops_step = sum(3 * layer_flops(L) for L in wl.layers)
     per_call, ms_step = m["per_call"], m["ms_step"]
-    # the dominant call: the slowest, hot for fp32 (MFMA-bound), cold for bf16
+    # the dominant call: the step's slowest, hot for fp32 (MFMA-bound), cold
+    # for bf16
     times = per_call if wl.dtype == "f32" else m["per_call_cold"]
-    dom = max(times, key=times.get)
+    dom = max(m["step_calls"], key=times.get)
     roof = call_roofline(wl, dom, per_call[dom], m["per_call_cold"][dom])
     roof.pop("frac_hot", None)
     roof.update({"traffic": measured_traffic(wl.name, dom), "kernel_call": dom,
-                 "kernels": CALL_KERNELS[dom.rstrip("0123456789")][wl.dtype],
+                 "kernels": call_kernels(wl, dom),
                  "us_per_launch": round(times[dom], 3),
                  "timing": "hot graph replays" if wl.dtype == "f32"
                  else "cold: each launch after a 640 MB cache flush, median"})
     value = flops_step / (ms_step * 1e-3) / 1e12
     fwd_us = sum(v for k, v in per_call.items() if k.startswith("fwd"))
-    bwd_us = sum(v for k, v in per_call.items() if not k.startswith("fwd"))
+    bwd_us = sum(v for k, v in per_call.items() if k.startswith("bwd"))
     vs = None
     if wl.name in PAGE1_US:
         page_us = sum(PAGE1_US[wl.name])
@@ -553,7 +572,7 @@ def report(wl, m, steps, warmup, cpu, others=None, data_ind=None):
         "roofline": roof,
         "calls": workload_summary(wl, m)["calls"],
         "bias_us_per_call": {k: round(v, 3) for k, v in m["bias_us"].items()},
-        "fused_bwd": m["fused"],
+        "ms_per_step_separate_calls": round(m["ms_step_separate"], 5),
         "cpu_baseline": cpu,
     }
     if vs is not None:

@@ -13,12 +13,16 @@ from backward_implicit_gemm_amd import inputs  # noqa: E402
 
 def _measured(wl, hot=None, cold=None):
     per_call = {}
-    for i in range(len(wl.layers)):
-        per_call.update({f"fwd{i + 1}": 50.0, f"dgrad{i + 1}": 60.0, f"wgrad{i + 1}": 55.0})
+    n = len(wl.layers)
+    for i in range(n):
+        per_call.update({f"fwd{i + 1}": 50.0, f"bwd{i + 1}": 100.0, f"dgrad{i + 1}": 60.0,
+                         f"wgrad{i + 1}": 55.0})
     floor = {"kernels_per_step": 6, "us_per_step": 12.0, "us_per_kernel": 2.0}
+    steps = [f"fwd{i + 1}" for i in range(n)] + [f"bwd{i + 1}" for i in reversed(range(n))]
     return {"ms_step": 0.2, "ms_eager": 0.25, "per_call": hot or per_call,
             "per_call_cold": cold or {k: v + 10.0 for k, v in per_call.items()},
-            "bias_us": {}, "ms_cold": 0.3, "floor": floor, "fused": None}
+            "bias_us": {}, "ms_cold": 0.3, "floor": floor, "step_calls": steps,
+            "ms_step_separate": 0.21}
 
 
 def _line(name, **kw):
@@ -37,23 +41,32 @@ def test_report_carries_the_contract_keys():
     roof = line["roofline"]
     for k in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
         assert k in roof, k
-    # the dominant call is the slowest one; fp32 is priced against fp32 MFMA
-    assert roof["kernel_call"] == "dgrad1" and roof["bound"] == "mfma" and roof["peak"] == 157.3
+    # the dominant call is the step's slowest, the one-call backward (both
+    # passes' flops); fp32 is priced against fp32 MFMA
+    assert roof["kernel_call"] == "bwd1" and roof["bound"] == "mfma" and roof["peak"] == 157.3
+    assert roof["kernels"] == ["bwd_fused_f32", "wgrad_reduce"]
     flops = 2 * 1024 * 128 * 3 * 4 * 59 * 5 * 5
-    assert abs(roof["achieved"] - flops / 60e-6 / 1e12) < 1e-2
+    assert abs(roof["achieved"] - 2 * flops / 100e-6 / 1e12) < 1e-2
     assert abs(line["value"] - 3 * flops / 0.2e-3 / 1e12) < 1e-2
+    # the separate passes are still reported, each against its own work
+    assert abs(line["calls"]["wgrad1"]["frac"] - flops / 55e-6 / 1e12 / 157.3) < 1e-4
+    assert line["us_per_iter"]["bwd"] == 100.0 and line["ms_per_step_separate_calls"] == 0.21
 
 
 def test_report_bf16_is_priced_against_hbm_on_cold_times():
     wl, line = _line("layer1_bf16_relu_b1024")
     roof = line["roofline"]
     assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and line["dtype"] == "bf16"
-    # d_input's algorithmic bytes (dy, y as the mask, w, dx) over its cold 70 us
+    # the backward's algorithmic bytes (dy, y as the mask, x, w read; dx, dw
+    # written) over its cold 110 us
     L = wl.layers[0]
-    by = 2 * (2 * L.B * 128 * 12 + 128 * 59 * 25 + L.B * 59 * 165)
-    assert roof["kernel_call"] == "dgrad1" and roof["us_per_launch"] == 70.0
-    assert abs(roof["achieved"] - by / 70e-6 / 1e9) < 1e-2
-    assert abs(line["calls"]["dgrad1"]["frac_hot"] - by / 60e-6 / 1e9 / 8000) < 1e-4
+    nx, nw, ny = L.B * 59 * 165, 128 * 59 * 25, L.B * 128 * 12
+    by = 2 * (2 * ny + 2 * nx + 2 * nw)
+    assert roof["kernel_call"] == "bwd1" and roof["us_per_launch"] == 110.0
+    assert abs(roof["achieved"] - by / 110e-6 / 1e9) < 1e-2
+    # d_input alone: dy, y, w, dx
+    by_d = 2 * (2 * ny + nw + nx)
+    assert abs(line["calls"]["dgrad1"]["frac_hot"] - by_d / 60e-6 / 1e9 / 8000) < 1e-4
 
 
 def test_report_carries_other_workloads_and_data_independence():
@@ -65,9 +78,10 @@ def test_report_carries_other_workloads_and_data_independence():
     json.dumps(line)
     assert set(line["workloads"]) == {w.name for w in inputs.WORKLOADS} - {bench.DEFAULT_WORKLOAD}
     c = line["workloads"]["layer1_bf16_relu_b1024"]["calls"]
-    assert set(c) == {"fwd1", "dgrad1", "wgrad1"} and 0 < c["fwd1"]["frac"] < 1
+    assert set(c) == {"fwd1", "bwd1", "dgrad1", "wgrad1"} and 0 < c["fwd1"]["frac"] < 1
     assert set(line["workloads"]["chain_bf16_b16384"]["calls"]) == {
-        "fwd1", "fwd2", "dgrad1", "dgrad2", "wgrad1", "wgrad2"}
+        "fwd1", "fwd2", "bwd1", "bwd2", "dgrad1", "dgrad2", "wgrad1", "wgrad2"}
+    assert "ms_per_step_separate_calls" in line["workloads"]["chain_bf16_b16384"]
     assert "data_independence" in line
 
 
@@ -90,3 +104,14 @@ def test_copy_fractions_are_added_to_hbm_bound_calls():
     # fp32 calls are priced against MFMA and get no copy fraction
     assert "frac_copy" not in line["calls"]["wgrad1"]
     assert "frac_copy" not in line["workloads"]["layer2_fp32_b1024"]["calls"]["fwd1"]
+
+
+def test_step_call_kernels_follow_the_backward_plan():
+    # the launch floor and the roofline's kernel list count what gc_conv_bwd runs
+    by = {w.name: w for w in inputs.WORKLOADS}
+    assert bench.call_kernels(by["layer1_fp32_relu_b1024"], "bwd1") == ["bwd_fused_f32", "wgrad_reduce"]
+    assert bench.call_kernels(by["layer2_bf16_b1024"], "bwd1") == [
+        "bwd_prep_bf16", "bwd_fused_bf16", "wgrad_reduce"]
+    assert bench.call_kernels(by["layer1_bf16_relu_b1024"], "bwd1") == [
+        "bwd_prep_bf16", "dgrad_ig_bf16", "wgrad_ws_bf16", "wgrad_reduce"]
+    assert bench.call_kernels(by["layer1_fp32_relu_b1024"], "fwd1") == ["pack_w_fwd_f32", "fwd_ws_f32"]
