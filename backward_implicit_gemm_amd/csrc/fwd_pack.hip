@@ -55,41 +55,44 @@ __global__ void __launch_bounds__(256) pack_w_fwd_bf16(const u16 *__restrict__ w
 // cg, tap step s) channels 4*cg .. 4*cg+3 at tap 4*s + q; for a shared step l
 // of a phase, channels of group 4*l + q of the phase at the last tap.  Zero
 // past OC, IC or KH*KW, and for lane groups past the phase's groups.
+// Block nb is blockIdx.y.  Every phase but the last has nsteps(0) steps, so
+// the phase of step f is min(f / nsteps(0), nph - 1); the two divisions use
+// divisors prepared on the host.
 __global__ void __launch_bounds__(256) pack_w_fwd_f32(const float *__restrict__ w,
                                                       float4 *__restrict__ wf, Geom g,
-                                                      FwdF32Steps st, int total)
+                                                      FwdF32Steps st, FastDiv fd_ns0,
+                                                      FastDiv fd_tsf)
 {
     const int nfrag = st.nfrag();
-    for (int u = blockIdx.x * 256 + threadIdx.x; u < total; u += gridDim.x * 256) {
-        const int lane = u & 63, q = lane >> 4;
-        int f = (u >> 6) % nfrag;
-        const int nb = (u >> 6) / nfrag;
-        int ph = 0;
-        while (f >= st.nsteps(ph)) {
-            f -= st.nsteps(ph);
-            ++ph;
-        }
-        int cg, t;
-        bool ok;
-        if (f < st.nfull(ph)) {
-            cg = ph * st.CPP + f / st.tsf();
-            t = 4 * (f % st.tsf()) + q;
-            ok = true;
-        } else {
-            const int l = f - st.nfull(ph);
-            cg = ph * st.CPP + 4 * l + q;
-            t = g.KK - 1;
-            ok = 4 * l + q < st.ncg(ph);
-        }
-        const int n = nb * 16 + (lane & 15);
-        float v[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int ic = 4 * cg + j;
-            v[j] = (ok && n < g.OC && ic < g.IC && t < g.KK) ? w[(size_t(n) * g.IC + ic) * g.KK + t] : 0.f;
-        }
-        wf[u] = make_float4(v[0], v[1], v[2], v[3]);
+    const int nb = blockIdx.y;
+    const int u = blockIdx.x * 256 + threadIdx.x;      // unit within the block
+    if (u >= nfrag * 64) return;
+    const int lane = u & 63, q = lane >> 4;
+    int f = u >> 6;
+    const int ph = min(int(fdiv(uint32_t(f), fd_ns0)), st.nph() - 1);
+    f -= ph * st.nsteps(0);
+    int cg, t;
+    bool ok;
+    if (f < st.nfull(ph)) {
+        uint32_t s, tq;
+        fdivmod(uint32_t(f), fd_tsf, s, tq);
+        cg = ph * st.CPP + int(s);
+        t = 4 * int(tq) + q;
+        ok = true;
+    } else {
+        const int l = f - st.nfull(ph);
+        cg = ph * st.CPP + 4 * l + q;
+        t = g.KK - 1;
+        ok = 4 * l + q < st.ncg(ph);
     }
+    const int n = nb * 16 + (lane & 15);
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int ic = 4 * cg + j;
+        v[j] = (ok && n < g.OC && ic < g.IC && t < g.KK) ? w[(size_t(n) * g.IC + ic) * g.KK + t] : 0.f;
+    }
+    wf[size_t(nb) * nfrag * 64 + u] = make_float4(v[0], v[1], v[2], v[3]);
 }
 
 }  // namespace
@@ -163,10 +166,11 @@ hipError_t launch_pack_w_fwd_f32(const Geom &g, int NCG, int CPP, int TS, int lo
 {
     const FwdF32Steps st{NCG, CPP, TS, lo};
     if (CPP < 1 || TS < 1 || (lo && (TS < 2 || g.KK != 4 * (TS - 1) + 1))) return hipErrorInvalidValue;
-    const int total = nblocks * st.nfrag() * 64;
-    if (size_t(total) * 16 > ws_bytes) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(pack_w_fwd_f32, dim3(std::min((total + 255) / 256, 1024)), dim3(256), 0, s,
-                       (const float *)w, (float4 *)wf, g, st, total);
+    const int per_block = st.nfrag() * 64;
+    if (size_t(nblocks) * per_block * 16 > ws_bytes) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pack_w_fwd_f32, dim3((per_block + 255) / 256, nblocks), dim3(256), 0, s,
+                       (const float *)w, (float4 *)wf, g, st, make_fastdiv(st.nsteps(0)),
+                       make_fastdiv(st.tsf()));
     return hipGetLastError();
 }
 

@@ -81,13 +81,14 @@ OTHER_GPU_BATCHES = {
 
 # gc_conv_bwd in fp32 runs the d_input and wgrad bodies in one launch; each
 # (d_input, wgrad) pair the planners can pick for the layer shapes -> a
-# (layer, batch size, relu) case that reaches it
+# (layer, batch size) case that reaches it (run with and without the ReLU,
+# which selects a kernel of its own)
 FUSED_F32_BWD = {
-    "bwd_fused_f32: dgrad_rf_f32<MB=3,KS4=8,TAPS=4> + wgrad_rf_f32<NBWV=3>": ("layer1", 97, 1),
-    "bwd_fused_f32: dgrad_rf_f32<MB=3,KS4=8,TAPS=4> + wgrad_rf_f32<NBWV=6>": ("layer1", 250, 0),
-    "bwd_fused_f32: dgrad_rf_f32<MB=1,KS4=8,TAPS=2> + wgrad_rf_f32<NBWV=3>": ("layer2", 66, 1),
-    "bwd_fused_f32: dgrad_rf_f32<MB=2,KS4=8,TAPS=2> + wgrad_rf_f32<NBWV=3>": ("layer2", 203, 0),
-    "bwd_fused_f32: dgrad_rf_f32<MB=3,KS4=8,TAPS=2> + wgrad_rf_f32<NBWV=3>": ("layer2", 409, 1),
+    "bwd_fused_f32: dgrad_rf_f32<MB=3,KS4=8,TAPS=4> + wgrad_rf_f32<NBWV=3>": ("layer1", 97),
+    "bwd_fused_f32: dgrad_rf_f32<MB=3,KS4=8,TAPS=4> + wgrad_rf_f32<NBWV=6>": ("layer1", 250),
+    "bwd_fused_f32: dgrad_rf_f32<MB=1,KS4=8,TAPS=2> + wgrad_rf_f32<NBWV=3>": ("layer2", 66),
+    "bwd_fused_f32: dgrad_rf_f32<MB=2,KS4=8,TAPS=2> + wgrad_rf_f32<NBWV=3>": ("layer2", 203),
+    "bwd_fused_f32: dgrad_rf_f32<MB=3,KS4=8,TAPS=2> + wgrad_rf_f32<NBWV=3>": ("layer2", 409),
 }
 
 

@@ -111,11 +111,13 @@ def test_bwd_repeated_calls_are_identical():
     assert np.isfinite(f64(dw)).all()
 
 
-@pytest.mark.parametrize("pair", sorted(FUSED_F32_BWD), ids=lambda p: "{}-B{}-relu{}".format(*FUSED_F32_BWD[p]))
-def test_fused_f32_pairs(pair):
-    # every (d_input, wgrad) pair of the one-launch fp32 backward, with a
-    # batch that leaves a ragged last image group and quad
-    layer_name, B, relu = FUSED_F32_BWD[pair]
+@pytest.mark.parametrize("relu", [0, 1])
+@pytest.mark.parametrize("pair", sorted(FUSED_F32_BWD), ids=lambda p: "{}-B{}".format(*FUSED_F32_BWD[p]))
+def test_fused_f32_pairs(pair, relu):
+    # every (d_input, wgrad) pair of the one-launch fp32 backward, with and
+    # without the ReLU, at a batch that leaves a ragged last image group and
+    # quad
+    layer_name, B = FUSED_F32_BWD[pair]
     shape = LAYER_SHAPES[layer_name][:7]
     layer = Layer(B, *shape, relu)
     name = gb.gc_conv_plan_name(gb.GC_OP_BWD, gb.make_desc(B, *shape), gb.GC_F32)

@@ -105,5 +105,5 @@ def test_fp32_backward_is_fused_and_every_pair_is_gpu_tested():
         for B in _sweep():
             name = plan(layer, B, "f32", "bwd")
             assert fused_pair(name) in FUSED_F32_BWD, (layer, B, name)
-    for pair, (layer, B, _) in FUSED_F32_BWD.items():
+    for pair, (layer, B) in FUSED_F32_BWD.items():
         assert fused_pair(plan(layer, B, "f32", "bwd")) == pair
