@@ -28,14 +28,15 @@ __global__ void __launch_bounds__(kDzNT) bwd_prep_bf16(const u16 *__restrict__ d
                                                        uint4 *__restrict__ dzg, Geom g, int relu,
                                                        int PP, int ngroups,
                                                        const u16 *__restrict__ w,
-                                                       uint4 *__restrict__ wp, int CC, int NBC,
-                                                       int KS, int total, int npack)
+                                                       uint4 *__restrict__ wp, int CC,
+                                                       FastDiv fd_nbc, FastDiv fd_ks, int total,
+                                                       int npack)
 {
     const int bid = blockIdx.x;
     if (bid < ngroups * kDzSlices)
         dz_groups_bf16_body(dy, ym, dzg, g, relu, PP, bid);
     else
-        pack_w_dgrad_bf16_body(w, wp, g, CC, NBC, KS, total, bid - ngroups * kDzSlices, npack);
+        pack_w_dgrad_bf16_body(w, wp, g, CC, fd_nbc, fd_ks, total, bid - ngroups * kDzSlices, npack);
 }
 
 // d_input workgroups first (n_dg of them, an (image group, channel group)
@@ -146,7 +147,7 @@ hipError_t launch_bwd_fused_bf16(const Geom &g, const BwdFusedBfPlan &p, const v
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_prep_bf16, dim3(wp.ngroups * kDzSlices + npack), dim3(kDzNT), dz_lds, s,
                        (const u16 *)dy, (const u16 *)ym, dzg, g, relu, wp.PP, wp.ngroups,
-                       (const u16 *)w, wpk, d.CC, d.NBC, d.KS, total, npack);
+                       (const u16 *)w, wpk, d.CC, make_fastdiv(d.NBC), make_fastdiv(d.KS), total, npack);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 

@@ -151,7 +151,8 @@ hipError_t launch_dgrad_ig_bf16(const Geom &g, const DgradBfPlan &p, const void 
     hipError_t e = allow_max_lds(reinterpret_cast<const void *>(v->fn));
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(pack_w_dgrad_bf16, dim3(std::min((total + 255) / 256, 2048)), dim3(256), 0, s,
-                       (const u16 *)w, (uint4 *)ws, g, p.CC, p.NBC, p.KS, total);
+                       (const u16 *)w, (uint4 *)ws, g, p.CC, make_fastdiv(p.NBC), make_fastdiv(p.KS),
+                       total);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     DgradBfArgs a{g, (const u16 *)dy, (const u16 *)ym, (const uint4 *)ws, (u16 *)dx, relu, p,

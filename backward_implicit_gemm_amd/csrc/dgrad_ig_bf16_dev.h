@@ -17,24 +17,24 @@ typedef unsigned short u16;
 // unit holds w[32*ks + 8*(lane/16) + i][chunk*CC + icl][kk] for i = 0..7, zero
 // past OC, IC or the chunk's CC*KK columns.
 // Workgroup `bid` of `nblk` (256 threads each) packs units bid*256 + t,
-// stepping by nblk*256.
+// stepping by nblk*256; the unit index splits with divisors prepared on the
+// host (fd_ks: KS, fd_nbc: NBC).
 __device__ __forceinline__ void pack_w_dgrad_bf16_body(const u16 *__restrict__ w,
                                                        uint4 *__restrict__ wp, const Geom &g,
-                                                       int CC, int NBC, int KS, int total, int bid,
-                                                       int nblk)
+                                                       int CC, FastDiv fd_nbc, FastDiv fd_ks,
+                                                       int total, int bid, int nblk)
 {
     for (int u = bid * 256 + threadIdx.x; u < total; u += nblk * 256) {
         const int lane = u & 63;
-        int rest = u >> 6;
-        const int ks = rest % KS;
-        rest /= KS;
-        const int nbl = rest % NBC;
-        const int chunk = rest / NBC;
-        const int n = nbl * 16 + (lane & 15);
-        const int icl = n / g.KK, kk = n - icl * g.KK;
-        const int ic = chunk * CC + icl;
-        const bool ok = icl < CC && ic < g.IC;
-        const int oc0 = ks * 32 + (lane >> 4) * 8;
+        uint32_t rest, ks, chunk, nbl;
+        fdivmod(uint32_t(u >> 6), fd_ks, rest, ks);
+        fdivmod(rest, fd_nbc, chunk, nbl);
+        const int n = int(nbl) * 16 + (lane & 15);
+        uint32_t icl, kk;
+        fdivmod(uint32_t(n), g.fd_KK, icl, kk);
+        const int ic = int(chunk) * CC + int(icl);
+        const bool ok = int(icl) < CC && ic < g.IC;
+        const int oc0 = int(ks) * 32 + (lane >> 4) * 8;
         u16 v[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -49,9 +49,9 @@ __device__ __forceinline__ void pack_w_dgrad_bf16_body(const u16 *__restrict__ w
 }
 __global__ void __launch_bounds__(256) __attribute__((unused)) pack_w_dgrad_bf16(const u16 *__restrict__ w,
                                                          uint4 *__restrict__ wp, Geom g, int CC,
-                                                         int NBC, int KS, int total)
+                                                         FastDiv fd_nbc, FastDiv fd_ks, int total)
 {
-    pack_w_dgrad_bf16_body(w, wp, g, CC, NBC, KS, total, blockIdx.x, gridDim.x);
+    pack_w_dgrad_bf16_body(w, wp, g, CC, fd_nbc, fd_ks, total, blockIdx.x, gridDim.x);
 }
 
 struct DgradBfArgs {

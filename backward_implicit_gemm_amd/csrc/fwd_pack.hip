@@ -20,33 +20,32 @@ typedef unsigned short u16;
 
 // Packed weight layout, 16-byte units: ((nb*NCG + cg)*TS + s)*64 + lane,
 // lane = (n%16) + 16*q, holding w[n][8*cg + i][4*s + q] for i = 0..7 (zero
-// past OC, IC or KH*KW).
+// past OC, IC or KH*KW).  Block nb is blockIdx.y; fd_ts divides by TS.
 __global__ void __launch_bounds__(256) pack_w_fwd_bf16(const u16 *__restrict__ w,
                                                        uint4 *__restrict__ wf, Geom g, int NCG,
-                                                       int TS, int total)
+                                                       FastDiv fd_ts)
 {
-    for (int u = blockIdx.x * 256 + threadIdx.x; u < total; u += gridDim.x * 256) {
-        const int lane = u & 63;
-        int rest = u >> 6;
-        const int s = rest % TS;
-        rest /= TS;
-        const int cg = rest % NCG;
-        const int nb = rest / NCG;
-        const int n = nb * 16 + (lane & 15);
-        const int t = 4 * s + (lane >> 4);
-        u16 v[8];
+    const int nb = blockIdx.y;
+    const int per_block = NCG * int(fd_ts.d) * 64;
+    const int u = blockIdx.x * 256 + threadIdx.x;      // unit within the block
+    if (u >= per_block) return;
+    const int lane = u & 63;
+    uint32_t cg, s;
+    fdivmod(uint32_t(u >> 6), fd_ts, cg, s);
+    const int n = nb * 16 + (lane & 15);
+    const int t = 4 * int(s) + (lane >> 4);
+    u16 v[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int ic = 8 * cg + i;
-            v[i] = (n < g.OC && ic < g.IC && t < g.KK) ? w[(size_t(n) * g.IC + ic) * g.KK + t] : u16(0);
-        }
-        uint4 o;
-        o.x = v[0] | (uint32_t(v[1]) << 16);
-        o.y = v[2] | (uint32_t(v[3]) << 16);
-        o.z = v[4] | (uint32_t(v[5]) << 16);
-        o.w = v[6] | (uint32_t(v[7]) << 16);
-        wf[u] = o;
+    for (int i = 0; i < 8; ++i) {
+        const int ic = 8 * int(cg) + i;
+        v[i] = (n < g.OC && ic < g.IC && t < g.KK) ? w[(size_t(n) * g.IC + ic) * g.KK + t] : u16(0);
     }
+    uint4 o;
+    o.x = v[0] | (uint32_t(v[1]) << 16);
+    o.y = v[2] | (uint32_t(v[3]) << 16);
+    o.z = v[4] | (uint32_t(v[5]) << 16);
+    o.w = v[6] | (uint32_t(v[7]) << 16);
+    wf[size_t(nb) * per_block + u] = o;
 }
 
 // Packed fp32 weights, 16-byte units (nb*NFRAG + f)*64 + lane: step f of
@@ -154,10 +153,10 @@ void pick_lds_pitch(const Geom &g, int G, int MB, int TS, int &WP_out, int &IS_o
 hipError_t launch_pack_w_fwd_bf16(const Geom &g, int NCG, int TS, int nblocks, const void *w,
                                   void *wf, size_t ws_bytes, hipStream_t s)
 {
-    const int total = nblocks * NCG * TS * 64;
-    if (size_t(total) * 16 > ws_bytes) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(pack_w_fwd_bf16, dim3(std::min((total + 255) / 256, 1024)), dim3(256), 0, s,
-                       (const u16 *)w, (uint4 *)wf, g, NCG, TS, total);
+    const int per_block = NCG * TS * 64;
+    if (TS < 1 || size_t(nblocks) * per_block * 16 > ws_bytes) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pack_w_fwd_bf16, dim3((per_block + 255) / 256, nblocks), dim3(256), 0, s,
+                       (const u16 *)w, (uint4 *)wf, g, NCG, make_fastdiv(TS));
     return hipGetLastError();
 }
 
