@@ -2,12 +2,15 @@
 // element is the sum of its `splits` fp32 partials taken in split order
 // 0, 1, ..., splits-1, so the result does not depend on scheduling and is
 // bit-identical from run to run (no value atomics anywhere).  A thread owns
-// four consecutive elements (16-byte loads) and issues the loads of eight
-// splits before adding them, in order.
+// four consecutive elements (16-byte loads) and issues the loads of up to
+// kBatch splits before adding them, in order (the layer shapes' 8 or 16
+// splits in one round trip).
 #include "gc_kernels.h"
 
 namespace gc {
 namespace {
+
+constexpr int kBatch = 16;   // split loads in flight per thread
 
 __device__ __forceinline__ void store4(float *p, const float4 &v) { __builtin_memcpy(p, &v, 16); }
 __device__ __forceinline__ void store4(bf16_t *p, const float4 &v)
@@ -26,13 +29,13 @@ __global__ void __launch_bounds__(256) wgrad_reduce(const float *__restrict__ pa
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += gridDim.x * blockDim.x) {
         const float4 *src = reinterpret_cast<const float4 *>(part) + i;
         float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int z0 = 0; z0 < splits; z0 += 8) {
-            float4 v[8];
+        for (int z0 = 0; z0 < splits; z0 += kBatch) {
+            float4 v[kBatch];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < kBatch; ++j)
                 if (z0 + j < splits) v[j] = src[size_t(z0 + j) * n4];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < kBatch; ++j)
                 if (z0 + j < splits) {
                     s.x += v[j].x; s.y += v[j].y; s.z += v[j].z; s.w += v[j].w;
                 }
@@ -59,13 +62,13 @@ __global__ void __launch_bounds__(256) wgrad_reduce_bias(const float *__restrict
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += gridDim.x * blockDim.x) {
         const float4 *src = reinterpret_cast<const float4 *>(part) + i;
         float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int z0 = 0; z0 < splits; z0 += 8) {
-            float4 v[8];
+        for (int z0 = 0; z0 < splits; z0 += kBatch) {
+            float4 v[kBatch];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < kBatch; ++j)
                 if (z0 + j < splits) v[j] = src[size_t(z0 + j) * n4];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < kBatch; ++j)
                 if (z0 + j < splits) {
                     s.x += v[j].x; s.y += v[j].y; s.z += v[j].z; s.w += v[j].w;
                 }
