@@ -14,7 +14,8 @@ forward and backward separately over 50 warmup and 200 timed iterations.
 Prints one JSON line: throughput in TFLOP/s of algorithmic work
 (2*B*OC*OH*OW*IC*KH*KW per pass, three passes per step) over K steps, each
 step replayed as one HIP graph between HIP events on the launch stream; the
-same K steps issued eagerly (host work included); the step timed cold
+same K steps issued eagerly (host work included), all after an untimed
+pre-warm of 0.3 s of step replays and the W warmup steps; the step timed cold
 (caches flushed by a 640 MB write before each replay); the launch floor (a
 graph of as many one-element kernels as a step launches); per-call GPU times,
 hot (graphs of back-to-back copies of each call) and cold (each call alone
@@ -62,6 +63,9 @@ PAGE1_US = {
 }
 
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.md")
+
+# Seconds of untimed step replays before the warmup steps of each workload.
+PREWARM_S = 0.3
 
 
 def parse():
@@ -191,6 +195,14 @@ def run_gpu(wl, steps, warmup, x_scale=1.0, extras=True):
     step_graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(step_graph):
         step()
+    # Untimed pre-warm of PREWARM_S seconds, then the W warmup steps: a few
+    # dozen steps of a 0.1 ms step leave the GPU short of its steady clocks,
+    # and the first steps timed after them read up to ~10 % slow.
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < PREWARM_S:
+        for _ in range(20):
+            step_graph.replay()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         step_graph.replay()
     torch.cuda.synchronize()
