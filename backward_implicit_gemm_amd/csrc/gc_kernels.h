@@ -81,8 +81,9 @@ bool plan_wgrad_rf_f32_bias(const Geom &g, WgradRfPlan &p);
 hipError_t launch_wgrad_rf_f32(const Geom &g, const WgradRfPlan &p, const void *x, const void *dy,
                                const void *ym, void *dw, void *db, void *ws, int relu,
                                hipStream_t s);
-// bf16 backward (d_input + wgrad) in three launches: pre-passes, both main
-// kernels in one grid, reduction.  Same results as the separate calls.
+// bf16 backward (d_input + wgrad) in three or four launches: pre-passes, both
+// main kernels in one grid (or one after the other), reduction.  Same results
+// as the separate calls.
 bool plan_bwd_fused_bf16(const Geom &g, BwdFusedBfPlan &p);
 hipError_t launch_bwd_fused_bf16(const Geom &g, const BwdFusedBfPlan &p, const void *x,
                                  const void *w, const void *dy, const void *ym, void *dx, void *dw,

@@ -308,8 +308,8 @@ struct WgradIgPlan {
     size_t lds;
 };
 
-// bf16 backward in three launches (bwd_fused_bf16.hip): the d_input and
-// wgrad plans it runs, and where wgrad's part of the workspace starts.
+// bf16 backward in three or four launches (bwd_fused_bf16.hip): the d_input
+// and wgrad plans it runs, and where wgrad's part of the workspace starts.
 struct BwdFusedBfPlan {
     DgradBfPlan d;
     WgradBfPlan w;
