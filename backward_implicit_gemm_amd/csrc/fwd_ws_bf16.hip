@@ -327,6 +327,8 @@ bool plan_fwd_ws_bf16(const Geom &g, FwdWsPlan &p)
 {
     if (g.P > 64 || g.KK > 36 || g.HW < 8) return false;
     if (size_t(g.B) * g.IC * g.HW * 2 >= (size_t(1) << 31)) return false;
+    // the weight packing runs one grid row per 16-channel block (at most 65535)
+    if ((g.OC + 15) / 16 > 65535) return false;
     const int TS = (g.KK + 3) / 4;
     const int NCG = (g.IC + 7) / 8;
     const int nblk = (g.HW + 7) / 8;

@@ -259,6 +259,8 @@ bool plan_fwd_ws_f32(const Geom &g, FwdWsPlan &p)
 {
     if (g.P > 64 || g.KK > 36 || g.HW < 4) return false;
     if (size_t(g.B) * g.IC * g.HW * 4 >= (size_t(1) << 31)) return false;
+    // the weight packing runs one grid row per 16-channel block (at most 65535)
+    if ((g.OC + 15) / 16 > 65535) return false;
     const int NWM = g.P <= 4 ? 4 : 8;
     const int TS = (g.KK + 3) / 4, NCG = (g.IC + 3) / 4, nblk = (g.HW + 3) / 4;
     const int ntile = (g.OC + 16 * NWM - 1) / (16 * NWM);

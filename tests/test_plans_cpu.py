@@ -107,3 +107,14 @@ def test_fp32_backward_is_fused_and_every_pair_is_gpu_tested():
             assert fused_pair(name) in FUSED_F32_BWD, (layer, B, name)
     for pair, (layer, B) in FUSED_F32_BWD.items():
         assert fused_pair(plan(layer, B, "f32", "bwd")) == pair
+
+
+def test_forward_planners_respect_the_pack_grid_limit():
+    # the forward's weight packing runs one grid row per 16-channel block, so
+    # more than 65535 blocks must go to the shape-generic kernel
+    for dt in (gb.GC_F32, gb.GC_BF16):
+        # layer 1's geometry (59 -> OC, 11x15, 5x5, stride 3) with a huge OC
+        big = gb.gc_conv_plan_name(gb.GC_OP_FWD, gb.make_desc(1, 59, 11, 15, 65536 * 16, 5, 5, 3), dt)
+        assert big == "igemm_generic_fwd", big
+        ok = gb.gc_conv_plan_name(gb.GC_OP_FWD, gb.make_desc(1, 59, 11, 15, 65535 * 16, 5, 5, 3), dt)
+        assert ok.startswith("fwd_ws_"), ok
