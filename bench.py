@@ -18,7 +18,8 @@ same K steps issued eagerly (host work included), all after an untimed
 pre-warm of 0.3 s of step replays and the W warmup steps; the step timed cold
 (caches flushed by a 640 MB write before each replay); the launch floor (a
 graph of as many one-element kernels as a step launches); per-call GPU times,
-hot (graphs of back-to-back copies of each call) and cold (each call alone
+hot (graphs of back-to-back copies of each call, warmed for 20 ms, at least
+ten replays timed) and cold (each call alone
 after a cache flush, median of several), for the step's calls and for the
 two backward passes as separate calls (gc_conv_bwd_data, gc_conv_bwd_weight),
 with the step made of those separate calls beside it; a roofline entry for
@@ -64,8 +65,10 @@ PAGE1_US = {
 
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.md")
 
-# Seconds of untimed step replays before the warmup steps of each workload.
+# Seconds of untimed step replays before the warmup steps of each workload,
+# and of untimed replays of each per-call graph before it is timed.
 PREWARM_S = 0.3
+PREWARM_CALL_S = 0.02
 
 
 def parse():
@@ -264,9 +267,11 @@ def run_gpu(wl, steps, warmup, x_scale=1.0, extras=True):
 
     # Per call: a graph of REPS back-to-back copies of the call, replayed and
     # timed with HIP events on the launch stream, so each figure is the
-    # call's GPU time (its kernels plus the gaps between graph nodes).
+    # call's GPU time (its kernels plus the gaps between graph nodes), over
+    # at least 10 replays whatever K is (with 2, a 20-step run's per-call
+    # figures read up to 10 % slow).
     reps = 10
-    replays = max(2, min(20, steps // reps))
+    replays = max(10, min(20, steps // reps))
     per_call = {}
     for name, f in calls + pass_calls:
         f()
@@ -274,8 +279,10 @@ def run_gpu(wl, steps, warmup, x_scale=1.0, extras=True):
         with torch.cuda.graph(g):
             for _ in range(reps):
                 f()
-        g.replay()
-        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < PREWARM_CALL_S:
+            g.replay()
+            torch.cuda.synchronize()
         start.record(stream)
         for _ in range(replays):
             g.replay()
