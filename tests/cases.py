@@ -92,6 +92,29 @@ FUSED_F32_BWD = {
 }
 
 
+# gc_conv_bwd in bf16 for the layer shapes: each fused form the planners can
+# pick (one pre-pass, then the two main grids in one launch or one after the
+# other) -> a (layer, batch size) case that reaches it
+FUSED_BF16_BWD = {
+    "bwd_fused_bf16 fuse_main=0: dgrad_ig_bf16<MB=3,KS=4,TAPS=4,NBW=1> + wgrad_ws_bf16<NSTEP=3,JW=2>":
+        ("layer1", 205),
+    "bwd_fused_bf16 fuse_main=0: dgrad_ig_bf16<MB=3,KS=4,TAPS=4,NBW=1> + wgrad_ws_bf16<NSTEP=3,JW=4>":
+        ("layer1", 2130),
+    "bwd_fused_bf16 fuse_main=1: dgrad_ig_bf16<MB=2,KS=4,TAPS=2,NBW=2> + wgrad_ws_bf16<NSTEP=1,JW=2>":
+        ("layer2", 9),
+    "bwd_fused_bf16 fuse_main=1: dgrad_ig_bf16<MB=3,KS=4,TAPS=2,NBW=1> + wgrad_ws_bf16<NSTEP=1,JW=2>":
+        ("layer2", 17),
+    "bwd_fused_bf16 fuse_main=0: dgrad_ig_bf16<MB=2,KS=4,TAPS=2,NBW=2> + wgrad_ws_bf16<NSTEP=1,JW=2>":
+        ("layer2", 3290),
+    "bwd_fused_bf16 fuse_main=0: dgrad_ig_bf16<MB=3,KS=4,TAPS=2,NBW=1> + wgrad_ws_bf16<NSTEP=1,JW=2>":
+        ("layer2", 4102),
+    "bwd_fused_bf16 fuse_main=0: dgrad_ig_bf16<MB=2,KS=4,TAPS=2,NBW=2> + wgrad_ws_bf16<NSTEP=1,JW=4>":
+        ("layer2", 15167),
+    "bwd_fused_bf16 fuse_main=0: dgrad_ig_bf16<MB=3,KS=4,TAPS=2,NBW=1> + wgrad_ws_bf16<NSTEP=1,JW=4>":
+        ("layer2", 17161),
+}
+
+
 def fused_pair(plan_name):
     """'bwd_fused_f32: <d_input instance> + <wgrad instance>' of a
     gc_conv_bwd plan name (the per-batch parameters dropped)."""

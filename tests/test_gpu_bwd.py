@@ -13,7 +13,7 @@ import torch
 from backward_implicit_gemm_amd import binding as gb
 from backward_implicit_gemm_amd import inputs
 
-from cases import FUSED_F32_BWD, LAYER_SHAPES, fused_pair
+from cases import FUSED_BF16_BWD, FUSED_F32_BWD, LAYER_SHAPES, fused_pair
 from parity import TOL, Layer, draw, f64, oracle_layer, rel_err
 
 pytestmark = pytest.mark.gpu
@@ -130,3 +130,24 @@ def test_fused_f32_pairs(pair, relu):
     edx, edw = rel_err(f64(dx), dx_ref), rel_err(f64(dw), dw_ref)
     print(f"  dx={edx:.2e} dw={edw:.2e}", flush=True)
     assert edx <= TOL["f32"] and edw <= TOL["f32"]
+
+
+@pytest.mark.parametrize("relu", [0, 1])
+@pytest.mark.parametrize("form", sorted(FUSED_BF16_BWD), ids=lambda f: "{}-B{}".format(*FUSED_BF16_BWD[f]))
+def test_fused_bf16_forms(form, relu):
+    # every fused form of the bf16 backward (pre-pass, the two main grids in
+    # one launch or one after the other, reduction) against the separate
+    # calls and the oracle
+    layer_name, B = FUSED_BF16_BWD[form]
+    shape = LAYER_SHAPES[layer_name][:7]
+    layer = Layer(B, *shape, relu)
+    name = gb.gc_conv_plan_name(gb.GC_OP_BWD, gb.make_desc(B, *shape), gb.GC_BF16)
+    print(f"{layer_name} B={B} relu={relu}: {name}", flush=True)
+    assert fused_pair(name) == form
+    x, w, dy = draw(layer, (B, 15, 16 + relu), "bf16")
+    y, dx, dw, dx2, dw2 = _both(layer, "bf16", x, w, dy)
+    assert _bits_equal(dx, dx2) and _bits_equal(dw, dw2)
+    _, dx_ref, dw_ref = oracle_layer(layer, x, w, dy, y)
+    edx, edw = rel_err(f64(dx), dx_ref), rel_err(f64(dw), dw_ref)
+    print(f"  dx={edx:.2e} dw={edw:.2e}", flush=True)
+    assert edx <= TOL["bf16"] and edw <= TOL["bf16"]

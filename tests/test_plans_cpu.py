@@ -11,7 +11,7 @@ import pytest
 
 from backward_implicit_gemm_amd import binding as gb
 
-from cases import (FUSED_F32_BWD, INSTANCES, LAYER_BATCHES, LAYER_SHAPES, OTHER_GPU_BATCHES,
+from cases import (FUSED_BF16_BWD, FUSED_F32_BWD, INSTANCES, LAYER_BATCHES, LAYER_SHAPES, OTHER_GPU_BATCHES,
                    fused_pair, instance_key)
 
 OPS = {"fwd": gb.GC_OP_FWD, "bwd_data": gb.GC_OP_BWD_DATA, "bwd_weight": gb.GC_OP_BWD_WEIGHT,
@@ -118,3 +118,16 @@ def test_forward_planners_respect_the_pack_grid_limit():
         assert big == "igemm_generic_fwd", big
         ok = gb.gc_conv_plan_name(gb.GC_OP_FWD, gb.make_desc(1, 59, 11, 15, 65535 * 16, 5, 5, 3), dt)
         assert ok.startswith("fwd_ws_"), ok
+
+
+def test_every_bf16_fused_backward_form_is_gpu_tested():
+    # gc_conv_bwd in bf16 takes a fused form (or the separate calls, which the
+    # per-pass tests cover) at every batch size; each fused form it can pick
+    # for the layer shapes has a GPU case
+    for layer in LAYER_SHAPES:
+        for B in _sweep():
+            name = plan(layer, B, "bf16", "bwd")
+            if name.startswith("bwd_fused_bf16"):
+                assert fused_pair(name) in FUSED_BF16_BWD, (layer, B, name)
+    for form, (layer, B) in FUSED_BF16_BWD.items():
+        assert fused_pair(plan(layer, B, "bf16", "bwd")) == form
