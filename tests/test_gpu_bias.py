@@ -169,6 +169,9 @@ WB_SHAPES = [
     (1024, 59, 11, 15, 128, 5, 5, 3, 1), (1024, 128, 3, 4, 128, 3, 3, 1, 0),
     (16384, 59, 11, 15, 128, 5, 5, 3, 1), (16384, 128, 3, 4, 128, 3, 3, 1, 0),
     (37, 128, 3, 4, 96, 3, 3, 1, 1), (9, 59, 11, 15, 128, 5, 5, 3, 0),
+    # layer 1's shape with the other ReLU setting of each fp32 bias-column
+    # kernel (48-column tiles with a ReLU, 96-column tiles without)
+    (101, 59, 11, 15, 128, 5, 5, 3, 1), (301, 59, 11, 15, 128, 5, 5, 3, 0),
     (3, 3, 7, 8, 4, 3, 3, 2, 1), (5, 7, 6, 6, 130, 6, 6, 1, 0),
 ]
 
