@@ -69,7 +69,8 @@ bool plan_wgrad_bf16_tiles(const Geom &g, int JW, WgradBfPlan &p, int bias)
     const int nblk = (g.HW + 7) / 8;
     if (2 * CCW * nblk > kWgNT) return false;
     const int HWP = nblk * 9;        // 8-pixel blocks of 9 LDS slots (see xslot)
-    const size_t lds = 2 * (size_t(CCW) * HWP + size_t(PP) * 128) * 16;
+    // two stages of x (plus the bias column's unit of ones) and dz
+    const size_t lds = 2 * (size_t(CCW) * HWP + (bias ? 1 : 0) + size_t(PP) * 128) * 16;
     if (lds > 160 * 1024) return false;
     const int ngroups = (g.B + 7) / 8;
     // splits: enough workgroups to cover the CUs, in multiples of the XCD

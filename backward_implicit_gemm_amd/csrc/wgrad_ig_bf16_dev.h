@@ -317,9 +317,10 @@ __device__ __forceinline__ void wgrad_ig_bf16_body(const WgradBfArgs &a, int bid
 // The loaders store stage i+1 (loaded during stage i-1) into the other LDS
 // buffer and issue the loads of stage i+2 while the MFMAs run stage i; one
 // barrier per stage hands the buffers over.
-// BIAS: the plan's bias column is computed (a compile-time switch: a per-lane
-// select of the B operand inside the MFMA loop costs the plain wgrad a third
-// of its time at JW = 4)
+// BIAS: the plan's bias column is computed: its lanes read their B operand
+// from a unit of bf16 ones kept after each x buffer, so the MFMA loop is the
+// plain one (a per-lane select there cost the plain wgrad a third of its time
+// at JW = 4, and the bias variant spilled)
 template <int NSTEP, int JW, bool BIAS>
 __device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid)
 {
@@ -345,7 +346,10 @@ __device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid
     const int gb = split * p.gps;
     const int ge = min(gb + p.gps, p.ngroups);
 
-    const int xbuf = p.CCW * p.HWP;               // 16-byte units per x stage
+    // 16-byte units per x stage; with the bias column, one more unit holding
+    // bf16 ones, which the bias lanes read as their B operand
+    const int xones = p.CCW * p.HWP;
+    const int xbuf = xones + (BIAS ? 1 : 0);
     const int dbuf = p.PP * 128;                  // 16-byte units per dz stage
     uint4 *xs = lds4;                             // [2][CCW][HWP]
     uint4 *ds = lds4 + 2 * xbuf;                  // [2][PP][128]
@@ -379,7 +383,12 @@ __device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid
 #pragma unroll
     for (int j = 0; j < JW; ++j)
 #pragma unroll
-        for (int s = 0; s < NSTEP; ++s) xoff[j][s] = xpl[j] + xslot(xcol[j] + xrow[s]);
+        for (int s = 0; s < NSTEP; ++s) xoff[j][s] = ones[j] ? xones : xpl[j] + xslot(xcol[j] + xrow[s]);
+    if (BIAS && threadIdx.x == 0) {
+        // the ones unit of both x buffers, before the first barrier
+        xs[xones] = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+        xs[xbuf + xones] = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+    }
 
     // ---- staging -----------------------------------------------------------
     // x unit (icl, blk, half): pixels [pix, pix+8) of channel c_lo + icl for
@@ -452,10 +461,7 @@ __device__ __forceinline__ void wgrad_ws_bf16_body(const WgradBfArgs &a, int bid
 #pragma unroll
             for (int i = 0; i < 4; ++i) af[i] = __builtin_bit_cast(bf16x8, db[drow[s] + 16 * i]);
 #pragma unroll
-            for (int j = 0; j < JW; ++j)
-                bfr[j] = __builtin_bit_cast(bf16x8, BIAS && ones[j] ? make_uint4(0x3F803F80u, 0x3F803F80u,
-                                                                         0x3F803F80u, 0x3F803F80u)
-                                                            : xb[xoff[j][s]]);
+            for (int j = 0; j < JW; ++j) bfr[j] = __builtin_bit_cast(bf16x8, xb[xoff[j][s]]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
