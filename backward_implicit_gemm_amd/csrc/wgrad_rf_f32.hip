@@ -138,7 +138,8 @@ static bool plan_wgrad_rf_impl(const Geom &g, WgradRfPlan &p, int bias)
         });
         q.WP = pitch.first;
         q.IS = pitch.second;
-        q.bufsz = q.QB * q.CCS * q.IS + q.QB * g.P * q.OCP + 1;
+        // x planes, dz, the zero slot (and with the bias column a slot of ones)
+        q.bufsz = q.QB * q.CCS * q.IS + q.QB * g.P * q.OCP + 1 + bias;
         q.lds = size_t(2) * q.bufsz * 16;
         if (q.lds > 150 * 1024) continue;
         // one workgroup per CU: splits fill the CUs, in multiples of the

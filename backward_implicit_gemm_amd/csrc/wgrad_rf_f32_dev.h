@@ -49,6 +49,7 @@ __device__ __forceinline__ void wgrad_rf_f32_body(const WgradRfArgs &a, int bid)
     const int QX = p.CCS * p.IS, QD = g.P * p.OCP;  // LDS slots per quad: x, dz
     const int xsz = p.QB * QX;                      // x slots of a buffer
     const int zslot = xsz + p.QB * QD;              // the buffer's zero slot
+    const int oslot = zslot + 1;                    // with the bias column: a slot of ones
 
     // Staging units, one of each kind per thread at most.  The chunk's
     // channels of one image are contiguous in NCHW, and so is one image's dz,
@@ -122,13 +123,16 @@ __device__ __forceinline__ void wgrad_rf_f32_body(const WgradRfArgs &a, int bid)
     const bool wave_on = !loader && wave < p.MBLK * p.WN;
     const int mblk = wave % p.MBLK, nsub = wave / p.MBLK;
     const int oc_a = mblk * 16 + (lane & 15);            // A row of this lane
-    int coloff[NBWV];
-    bool ones[NBWV];      // the bias column: B is 1 for every image
+    // B slot of column block nb at step s: xrow[s] * xm[nb] + coloff[nb]; the
+    // bias column's lane takes xm = 0 and the slot of ones, so its B is 1 for
+    // every image without a select in the MFMA loop
+    int coloff[NBWV], xm[NBWV];
 #pragma unroll
     for (int nb = 0; nb < NBWV; ++nb) {
         const int col = col0 + (nsub * NBWV + nb) * 16 + (lane & 15);
-        ones[nb] = BIAS && col == g.K;
-        coloff[nb] = 0;
+        const bool ones = BIAS && col == g.K;
+        xm[nb] = ones ? 0 : 1;
+        coloff[nb] = ones ? oslot : 0;
         if (col < g.K) {
             uint32_t ic, t, kh, kw;
             fdivmod(uint32_t(col), g.fd_KK, ic, t);
@@ -167,6 +171,10 @@ __device__ __forceinline__ void wgrad_rf_f32_body(const WgradRfArgs &a, int bid)
         if (ltid == 0) {
             lds4w[zslot] = zero4;
             lds4w[p.bufsz + zslot] = zero4;
+            if (BIAS) {
+                lds4w[oslot] = make_float4(1.f, 1.f, 1.f, 1.f);
+                lds4w[p.bufsz + oslot] = make_float4(1.f, 1.f, 1.f, 1.f);
+            }
         }
         __syncthreads();
         for (int ph = 0; ph < nph; ++ph) {
@@ -189,8 +197,7 @@ __device__ __forceinline__ void wgrad_rf_f32_body(const WgradRfArgs &a, int bid)
                     float4 bv[NBWV];
 #pragma unroll
                     for (int nb = 0; nb < NBWV; ++nb)
-                        bv[nb] = BIAS && ones[nb] ? make_float4(1.f, 1.f, 1.f, 1.f)
-                                                  : buf[xrow[s] + coloff[nb]];
+                        bv[nb] = buf[(BIAS ? xrow[s] * xm[nb] : xrow[s]) + coloff[nb]];
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
 #pragma unroll
