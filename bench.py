@@ -32,7 +32,10 @@ time against HBM; fp32: flops over the hot time against fp32 MFMA), and under
 and under "hbm_copy" the bandwidth a plain 1 GiB device copy reaches here
 (reads + writes), beside which each bf16 call's fraction of the measured
 copy rate is given as "frac_copy" (the roofline fractions use the published
-8 TB/s).
+8 TB/s); each bf16 call also carries "same_bytes_copy", a plain copy moving
+the call's algorithmic bytes timed the same way (hot and cold, with its own
+fraction of 8 TB/s), and "frac_of_same_bytes_copy", the copy's cold time over
+the call's: what one launch of that size reaches here, beside the call.
 --workload NAME (or --all) prints the full line of other workloads.
 """
 import argparse
@@ -131,10 +134,11 @@ def measured_traffic(workload, op):
     return None if e is None else e.get("bytes_per_launch")
 
 
-def run_gpu(wl, steps, warmup, x_scale=1.0, extras=True):
+def run_gpu(wl, steps, warmup, x_scale=1.0, extras=True, copies=True):
     """Times workload wl.  x_scale multiplies the input x (a power of two
     leaves every product exact up to the exponent); extras=False skips the
-    eager and bias timings."""
+    eager and bias timings; copies=False skips the same-bytes copies of an
+    HBM-bound workload's calls."""
     import torch
 
     from backward_implicit_gemm_amd import binding as gb
@@ -291,6 +295,13 @@ def run_gpu(wl, steps, warmup, x_scale=1.0, extras=True):
         per_call[name] = start.elapsed_time(end) / (replays * reps) * 1e3
         del g
     per_call_cold = {name: cold_call_us(f, stream, dev) for name, f in calls + pass_calls}
+    # HBM-bound calls: a plain copy of the same number of bytes, timed the same
+    # way, as the yardstick of what one launch of that size reaches here
+    same_copy = {}
+    if copies and wl.dtype != "f32":
+        work = call_work(wl)
+        for name in per_call:
+            same_copy[name] = same_bytes_copy_us(work[name][1], stream, dev, reps, replays)
 
     # The step with the backward as the two separate calls per layer.
     fwd_calls = [c for c in calls if c[0].startswith("fwd")]
@@ -342,7 +353,44 @@ def run_gpu(wl, steps, warmup, x_scale=1.0, extras=True):
     return {"ms_step": ms_step, "ms_eager": ms_eager, "per_call": per_call,
             "per_call_cold": per_call_cold, "bias_us": bias_us, "ms_cold": ms_cold,
             "floor": floor, "step_calls": [n for n, _ in calls],
-            "ms_step_separate": ms_step_separate}
+            "ms_step_separate": ms_step_separate, "same_copy": same_copy}
+
+
+def same_bytes_copy_us(nbytes, stream, dev, reps, replays):
+    """A plain device-to-device copy moving nbytes (half read, half written),
+    the algorithmic bytes of one call: hot (a graph of `reps` back-to-back
+    copies, warmed like the calls' graphs, `replays` replays timed) and cold
+    (cold_call_us), in microseconds per copy."""
+    import torch
+
+    half = max(16, nbytes // 2 // 16 * 16)
+    src = torch.ones(half, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+
+    def f():
+        dst.copy_(src)
+
+    f()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            f()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < PREWARM_CALL_S:
+        g.replay()
+        torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(replays):
+        g.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    hot = start.elapsed_time(end) / (replays * reps) * 1e3
+    del g
+    cold = cold_call_us(f, stream, dev)
+    del src, dst
+    return {"us_hot": round(hot, 3), "us_cold": round(cold, 3), "bytes": 2 * half}
 
 
 def cold_call_us(f, stream, dev, reps=4, rounds=5):
@@ -483,6 +531,14 @@ def workload_summary(wl, m):
         r = call_roofline(wl, name, us, cold)
         calls[name] = {"us_hot": round(us, 3), "us_cold": round(cold, 3), "frac": r["frac"],
                        **({"frac_hot": r["frac_hot"]} if "frac_hot" in r else {})}
+        cp = m.get("same_copy", {}).get(name)
+        if cp:
+            # the copy's own fraction of the HBM peak, and how close the call
+            # comes to it (both cold)
+            calls[name]["same_bytes_copy"] = {
+                **cp, "frac": round(cp["bytes"] / (cp["us_cold"] * 1e-6) / 1e9 / PEAK["hbm_gbs"], 4)
+                if cp["us_cold"] > 0 else None}
+            calls[name]["frac_of_same_bytes_copy"] = round(cp["us_cold"] / cold, 4) if cold > 0 else None
     return {"dtype": wl.dtype, "bound": "mfma" if wl.dtype == "f32" else "hbm",
             "ms_per_step": round(m["ms_step"], 5), "ms_per_step_cold": round(m["ms_cold"], 5),
             "tflops_step": round(sum(3 * layer_flops(L) for L in wl.layers)
@@ -613,7 +669,7 @@ def data_independence(wl, base, steps, warmup):
     and each as a ratio to the unscaled run's."""
     out = {}
     for scale in (0.125, 8.0):
-        m = run_gpu(wl, steps, warmup, x_scale=scale, extras=False)
+        m = run_gpu(wl, steps, warmup, x_scale=scale, extras=False, copies=False)
         out[f"x*{scale:g}"] = {
             name: {"us_hot": round(m["per_call"][name], 3),
                    "us_cold": round(m["per_call_cold"][name], 3),

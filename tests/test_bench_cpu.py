@@ -115,3 +115,19 @@ def test_step_call_kernels_follow_the_backward_plan():
     assert bench.call_kernels(by["layer1_bf16_relu_b1024"], "bwd1") == [
         "bwd_prep_bf16", "dgrad_ig_bf16", "wgrad_ws_bf16", "wgrad_reduce"]
     assert bench.call_kernels(by["layer1_fp32_relu_b1024"], "fwd1") == ["pack_w_fwd_f32", "fwd_ws_f32"]
+
+
+def test_bf16_calls_carry_their_same_bytes_copy():
+    wl = next(w for w in inputs.WORKLOADS if w.name == "layer1_bf16_relu_b1024")
+    m = _measured(wl)
+    by = bench.call_work(wl)["fwd1"][1]
+    m["same_copy"] = {"fwd1": {"us_hot": 4.0, "us_cold": 6.0, "bytes": by}}
+    c = bench.workload_summary(wl, m)["calls"]
+    cp = c["fwd1"]["same_bytes_copy"]
+    json.dumps(c)
+    # the copy's bytes over its cold time against 8 TB/s, and the call's cold
+    # 60 us against the copy's 6 us
+    assert abs(cp["frac"] - by / 6e-6 / 1e9 / 8000) < 1e-4
+    assert abs(c["fwd1"]["frac_of_same_bytes_copy"] - 6.0 / 60.0) < 1e-4
+    # calls without a copy measurement carry no such keys
+    assert "same_bytes_copy" not in c["dgrad1"]
