@@ -294,7 +294,8 @@ def run_gpu(wl, steps, warmup, x_scale=1.0, extras=True, copies=True):
         torch.cuda.synchronize()
         per_call[name] = start.elapsed_time(end) / (replays * reps) * 1e3
         del g
-    per_call_cold = {name: cold_call_us(f, stream, dev) for name, f in calls + pass_calls}
+    per_call_cold = {name: cold_call_us(f, stream, dev, reps=cold_reps(per_call[name]))
+                     for name, f in calls + pass_calls}
     # HBM-bound calls: a plain copy of the same number of bytes, timed the same
     # way, as the yardstick of what one launch of that size reaches here
     same_copy = {}
@@ -388,9 +389,16 @@ def same_bytes_copy_us(nbytes, stream, dev, reps, replays):
     torch.cuda.synchronize()
     hot = start.elapsed_time(end) / (replays * reps) * 1e3
     del g
-    cold = cold_call_us(f, stream, dev)
+    cold = cold_call_us(f, stream, dev, reps=cold_reps(hot))
     del src, dst
     return {"us_hot": round(hot, 3), "us_cold": round(cold, 3), "bytes": 2 * half}
+
+
+def cold_reps(us_hot):
+    """Copies per cold-timing graph: the difference of two graph timings is
+    divided by it, so short calls get more copies (their difference is a small
+    part of the 640 MB writes' time)."""
+    return 16 if us_hot < 30.0 else 4
 
 
 def cold_call_us(f, stream, dev, reps=4, rounds=5):

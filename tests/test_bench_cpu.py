@@ -131,3 +131,10 @@ def test_bf16_calls_carry_their_same_bytes_copy():
     assert abs(c["fwd1"]["frac_of_same_bytes_copy"] - 6.0 / 60.0) < 1e-4
     # calls without a copy measurement carry no such keys
     assert "same_bytes_copy" not in c["dgrad1"]
+
+
+def test_short_calls_get_more_cold_copies():
+    # the cold time is a difference of two graph timings divided by the copy
+    # count: short calls are given more copies
+    assert bench.cold_reps(10.0) == 16 and bench.cold_reps(29.9) == 16
+    assert bench.cold_reps(30.0) == 4 and bench.cold_reps(500.0) == 4
